@@ -1,0 +1,156 @@
+"""CPU oracle for the DSA forward path (test infrastructure only).
+
+Thin ctypes wrapper over ``dsa_oracle.c`` (plain single-threaded C, double
+precision) plus row-level drivers that regenerate a workload's inputs on the
+host with ``dsa_inputs`` and run indexer -> top-k -> sparse attention for the
+requested query rows.  Only the tests, the smoke check and the bench's
+CPU-baseline leg use this package; the GPU library never does.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+_u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no fast-math, so double arithmetic is IEEE)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-fno-fast-math", _SRC, "-o", tmp, "-lm"],
+                   check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_e4m3_to_double.restype = ctypes.c_double
+        lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_indexer_row.restype = None
+        lib.oracle_indexer_row.argtypes = [_u8p, _f32p, _u8p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           _f64p]
+        lib.oracle_topk_row.restype = ctypes.c_int32
+        lib.oracle_topk_row.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int32, _i32p]
+        lib.oracle_sparse_mla_row.restype = None
+        lib.oracle_sparse_mla_row.argtypes = [_u16p, _u16p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_double, _f64p, _f64p]
+        lib.oracle_dense_mla_row.restype = None
+        lib.oracle_dense_mla_row.argtypes = [_u16p, _u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_double, _f64p, _f64p]
+        _lib = lib
+    return _lib
+
+
+# ------------------------------------------------------------------ primitives
+def e4m3_to_f64(b: int) -> float:
+    return _load().oracle_e4m3_to_double(int(b))
+
+
+def bf16_to_f64(u: int) -> float:
+    return _load().oracle_bf16_to_double(int(u))
+
+
+def indexer_row(q_row: np.ndarray, w_row: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Index scores of one query over key rows ``k`` [n, d] (token s = row s)."""
+    q_row = np.ascontiguousarray(q_row, dtype=np.uint8)
+    w_row = np.ascontiguousarray(w_row, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.uint8)
+    H_I, d = q_row.shape
+    n = k.shape[0]
+    assert k.shape[1] == d and w_row.shape == (H_I,)
+    out = np.empty(n, dtype=np.float64)
+    _load().oracle_indexer_row(q_row, w_row, k, n, H_I, d, out)
+    return out
+
+
+def topk_row(scores: np.ndarray, k: int) -> np.ndarray:
+    """Top-k of one score row: ascending token indices, -1 padded to k."""
+    scores = np.ascontiguousarray(scores, dtype=np.float64)
+    out = np.empty(k, dtype=np.int32)
+    _load().oracle_topk_row(scores, scores.shape[0], k, out)
+    return out
+
+
+def sparse_mla_row(q: np.ndarray, kv_rows: np.ndarray, scale: float, D_v: int):
+    """MQA attention of q [H, D_qk] over gathered latent rows [m, D_qk]."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kv_rows = np.ascontiguousarray(kv_rows, dtype=np.uint16).reshape(-1, q.shape[1])
+    H, D_qk = q.shape
+    out = np.empty((H, D_v), dtype=np.float64)
+    lse = np.empty(H, dtype=np.float64)
+    _load().oracle_sparse_mla_row(q, kv_rows, kv_rows.shape[0], H, D_qk, D_v, float(scale), out, lse)
+    return out, lse
+
+
+def dense_mla_row(q: np.ndarray, kv: np.ndarray, n: int, scale: float, D_v: int):
+    """Dense causal attention of q [H, D_qk] over kv [N, D_qk], first n rows visible."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    H, D_qk = q.shape
+    out = np.empty((H, D_v), dtype=np.float64)
+    lse = np.empty(H, dtype=np.float64)
+    _load().oracle_dense_mla_row(q, kv, kv.shape[0], n, H, D_qk, D_v, float(scale), out, lse)
+    return out, lse
+
+
+# ------------------------------------------------------------------ row drivers
+def gather_kv(wl, seq: int, idx: np.ndarray) -> np.ndarray:
+    """Latent rows of the selected tokens (entries < 0 are padding, dropped)."""
+    from dsa_inputs import configs
+    sel = idx[idx >= 0]
+    return configs.kv_bf16(wl, seq, sel)
+
+
+def prefill_row(wl, t: int, k_all: np.ndarray, k: int | None = None):
+    """Oracle chain for prefill query row t (position t, candidates 0..t).
+
+    ``k_all`` holds the key rows of the sequence (at least t+1 of them).
+    Returns dict(scores, idx, out, lse).
+    """
+    from dsa_inputs import configs
+    k = wl.k if k is None else k
+    q_i = configs.q_idx_bytes(wl, [t])[0]
+    w = configs.w_f32(wl, [t])[0]
+    scores = indexer_row(q_i, w, k_all[: t + 1])
+    idx = topk_row(scores, k)
+    q = configs.q_bf16(wl, [t])[0]
+    out, lse = sparse_mla_row(q, gather_kv(wl, 0, idx), wl.scale, wl.D_v)
+    return dict(scores=scores, idx=idx, out=out, lse=lse)
+
+
+def decode_row(wl, b: int, k: int | None = None):
+    """Oracle chain for the decode query of sequence b (position ctx_b - 1).
+
+    Keys and latent rows are regenerated by logical token position; paged
+    layouts therefore do not enter the oracle at all.
+    """
+    from dsa_inputs import configs
+    k = wl.k if k is None else k
+    n = int(configs.ctx_lens(wl)[b])
+    q_i = configs.q_idx_bytes(wl, [b])[0]
+    w = configs.w_f32(wl, [b])[0]
+    keys = configs.k_idx_bytes(wl, b, np.arange(n))
+    scores = indexer_row(q_i, w, keys)
+    idx = topk_row(scores, k)
+    q = configs.q_bf16(wl, [b])[0]
+    out, lse = sparse_mla_row(q, gather_kv(wl, b, idx), wl.scale, wl.D_v)
+    return dict(scores=scores, idx=idx, out=out, lse=lse)

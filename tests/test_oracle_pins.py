@@ -1,0 +1,276 @@
+"""Pins for the CPU oracle: each check is fixed by hand arithmetic, a closed
+form, an independent library routine or a brute-force algorithm, so that a
+dropped term, a wrong sign or index, or a transposed operand in the oracle
+fails at least one of them.  CPU only."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_inputs import configs, gen
+
+
+# --------------------------------------------------------------- storage formats
+def test_e4m3_hand_values():
+    assert oracle.e4m3_to_f64(0x38) == 1.0
+    assert oracle.e4m3_to_f64(0xB8) == -1.0
+    assert oracle.e4m3_to_f64(0x7E) == 448.0
+    assert oracle.e4m3_to_f64(0x01) == 2.0 ** -9
+    assert oracle.e4m3_to_f64(0x08) == 2.0 ** -6
+    assert oracle.e4m3_to_f64(0x44) == 3.0
+    assert math.isnan(oracle.e4m3_to_f64(0x7F))
+
+
+def test_e4m3_all_codes_match_torch():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+def test_bf16_codes_match_torch():
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 1 << 16, size=4000).astype(np.uint16)
+    codes = codes[((codes >> 7) & 0xFF) != 0xFF]  # finite only
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    mine = np.array([oracle.bf16_to_f64(c) for c in codes])
+    assert np.array_equal(mine, ref)
+
+
+# --------------------------------------------------------------- indexer
+def _e4m3(vals):
+    return gen.f32_to_e4m3_bits(np.asarray(vals, dtype=np.float32))
+
+
+def test_indexer_hand_case():
+    # H_I = 2 heads, d_I = 2; scores worked out by hand:
+    #   head dot products q_j . k_s, ReLU, then weighted by w_j and summed.
+    q = _e4m3([[1, 2], [-1, 3]])
+    k = _e4m3([[1, 1], [2, 1], [-1, -1], [0.5, -0.25]])
+    w = np.array([0.5, 2.0], dtype=np.float32)
+    # s0: dots (3, 2)    -> 0.5*3 + 2*2 = 5.5
+    # s1: dots (4, 1)    -> 0.5*4 + 2*1 = 4.0
+    # s2: dots (-3, -2)  -> 0
+    # s3: dots (0, -1.25)-> 0
+    assert np.array_equal(oracle.indexer_row(q, w, k), [5.5, 4.0, 0.0, 0.0])
+
+
+def test_indexer_relu_comes_before_weight():
+    # a negative weight must scale the rectified dot product (not be rectified)
+    q = _e4m3([[1, 2], [-1, 3]])
+    k = _e4m3([[1, 1], [2, 1]])
+    w = np.array([0.5, -2.0], dtype=np.float32)
+    # s0: 0.5*3 + (-2)*2 = -2.5 ; s1: 0.5*4 + (-2)*1 = 0
+    assert np.array_equal(oracle.indexer_row(q, w, k), [-2.5, 0.0])
+
+
+def test_indexer_onehot_zero_and_scaling():
+    rng = np.random.default_rng(1)
+    H_I, d, n = 4, 128, 37
+    q = _e4m3(rng.integers(-4, 5, size=(H_I, d)))
+    k = _e4m3(rng.integers(-4, 5, size=(n, d)))
+    base = oracle.indexer_row(q, np.ones(H_I, np.float32), k)
+    # zero weights -> zero scores
+    assert np.all(oracle.indexer_row(q, np.zeros(H_I, np.float32), k) == 0.0)
+    # power-of-two scaling of all weights scales the scores exactly
+    assert np.array_equal(oracle.indexer_row(q, np.full(H_I, 4.0, np.float32), k), 4.0 * base)
+    # one-hot weights isolate one head; summing them recovers the all-ones score
+    parts = []
+    for j in range(H_I):
+        wj = np.zeros(H_I, np.float32)
+        wj[j] = 1.0
+        parts.append(oracle.indexer_row(q, wj, k))
+    assert np.array_equal(np.sum(parts, axis=0), base)
+    # a head alone is the rectified integer dot product (inputs are small integers)
+    qv = np.array([[oracle.e4m3_to_f64(b) for b in row] for row in q])
+    kv = np.array([[oracle.e4m3_to_f64(b) for b in row] for row in k])
+    dots = kv @ qv[0]
+    assert np.array_equal(parts[0], np.maximum(dots, 0.0))
+    # permuting heads together with their weights changes nothing
+    perm = [2, 0, 3, 1]
+    w = np.array([0.25, 0.5, 1.0, 2.0], np.float32)
+    assert np.array_equal(oracle.indexer_row(q[perm], w[perm], k), oracle.indexer_row(q, w, k))
+
+
+def test_indexer_tiny_workload_scores_are_exact_quarters():
+    wl = configs.WORKLOADS["tiny_prefill_L256"]
+    keys = configs.k_idx_bytes(wl, 0, np.arange(wl.N))
+    for t in (0, 1, 100, 255):
+        s = oracle.indexer_row(configs.q_idx_bytes(wl, [t])[0], configs.w_f32(wl, [t])[0], keys[: t + 1])
+        assert s.shape == (t + 1,)
+        assert np.all(s >= 0.0)
+        assert np.array_equal(s * 4.0, np.round(s * 4.0))
+
+
+# --------------------------------------------------------------- top-k
+def _brute_topk(scores, k):
+    """Rank counting: s is selected iff fewer than k candidates beat it
+    (a larger score, or an equal score at a lower index)."""
+    n = len(scores)
+    sel = []
+    for s in range(n):
+        beats = sum(1 for u in range(n) if scores[u] > scores[s] or (scores[u] == scores[s] and u < s))
+        if beats < k:
+            sel.append(s)
+    return np.array(sel + [-1] * (k - len(sel)), dtype=np.int32)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_matches_rank_counting_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 60))
+    k = int(rng.integers(1, 40))
+    scores = rng.integers(0, 6, size=n).astype(np.float64) * 0.5  # many ties
+    assert np.array_equal(oracle.topk_row(scores, k), _brute_topk(scores, k))
+
+
+def test_topk_special_rows():
+    n, k = 50, 8
+    assert np.array_equal(oracle.topk_row(np.zeros(n), k), np.arange(k))          # all equal
+    assert np.array_equal(oracle.topk_row(np.arange(n, dtype=float), k), np.arange(n - k, n))  # increasing
+    assert np.array_equal(oracle.topk_row(np.arange(n, dtype=float)[::-1].copy(), k), np.arange(k))
+    r = oracle.topk_row(np.ones(5), 8)                                              # fewer candidates
+    assert np.array_equal(r, [0, 1, 2, 3, 4, -1, -1, -1])
+    assert np.array_equal(oracle.topk_row(np.array([-0.0, 0.0, -0.0]), 2), [0, 1])  # -0 == +0
+    assert np.array_equal(oracle.topk_row(np.array([1.0, 3.0, 2.0, 3.0]), 1), [1])  # k = 1, tie to lower
+
+
+def test_topk_random_rows_invariants():
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        n = int(rng.integers(1, 3000))
+        k = int(rng.integers(1, 300))
+        s = rng.standard_normal(n)
+        r = oracle.topk_row(s, k)
+        m = min(n, k)
+        sel = r[:m]
+        assert np.all(r[m:] == -1)
+        assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < n
+        if n > k:
+            thr = np.sort(s)[::-1][k - 1]
+            assert np.all(s[sel] >= thr)
+            assert np.sum(s > thr) <= k
+
+
+# --------------------------------------------------------------- attention
+def test_attention_hand_case():
+    # one head, D_qk = 2, D_v = 1, scale 1: logits (0, 1) -> softmax (1, e)/(1+e)
+    q = gen.f32_to_bf16_bits(np.array([[1.0, 0.0]], np.float32))
+    kv = gen.f32_to_bf16_bits(np.array([[0.0, 2.0], [1.0, 4.0]], np.float32))
+    out, lse = oracle.sparse_mla_row(q, kv, 1.0, 1)
+    e = math.e
+    assert out[0, 0] == pytest.approx(e / (1 + e), rel=1e-15)
+    assert lse[0] == pytest.approx(math.log(1 + e), rel=1e-15)
+
+
+def _rand_bf16(rng, shape, sd=1.0):
+    return gen.f32_to_bf16_bits((rng.standard_normal(shape) * sd).astype(np.float32))
+
+
+def _bf16_to_np(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_dense_matches_torch_sdpa():
+    rng = np.random.default_rng(3)
+    H, D_qk, D_v, N = 3, 24, 16, 11
+    q = _rand_bf16(rng, (H, D_qk))
+    kv = _rand_bf16(rng, (N, D_qk))
+    scale = 0.3
+    qt = torch.from_numpy(_bf16_to_np(q))[None, :, None, :]          # [1, H, 1, D]
+    kt = torch.from_numpy(_bf16_to_np(kv))[None, None].expand(1, H, N, D_qk)
+    vt = torch.from_numpy(_bf16_to_np(kv)[:, :D_v])[None, None].expand(1, H, N, D_v)
+    for n in (1, 5, N):
+        mask = torch.zeros(1, 1, 1, N, dtype=torch.bool)
+        mask[..., :n] = True
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+        out, lse = oracle.dense_mla_row(q, kv, n, scale, D_v)
+        np.testing.assert_allclose(out, ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-13)
+        logits = (qt[0, :, 0] @ kt[0, 0, :n].T) * scale
+        np.testing.assert_allclose(lse, torch.logsumexp(logits, dim=-1).numpy(), rtol=1e-13)
+
+
+def test_sparse_with_all_candidates_equals_dense():
+    wl = configs.WORKLOADS["tiny_prefill_L256"]
+    kv = configs.kv_bf16(wl, 0, np.arange(wl.N))
+    for t in (0, 7, 130, 255):
+        q = configs.q_bf16(wl, [t])[0]
+        o_s, l_s = oracle.sparse_mla_row(q, kv[: t + 1], wl.scale, wl.D_v)
+        o_d, l_d = oracle.dense_mla_row(q, kv, t + 1, wl.scale, wl.D_v)
+        np.testing.assert_allclose(o_s, o_d, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(l_s, l_d, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(5)
+    H, D_qk, D_v, m = 4, 576, 512, 9
+    q = _rand_bf16(rng, (H, D_qk))
+    kv = _rand_bf16(rng, (m, D_qk))
+    kvd = _bf16_to_np(kv)
+    # one selected row: the output is that row's value part, lse its logit
+    out, lse = oracle.sparse_mla_row(q, kv[:1], 0.1, D_v)
+    assert np.array_equal(out, np.broadcast_to(kvd[0, :D_v], (H, D_v)))
+    np.testing.assert_allclose(lse, 0.1 * (_bf16_to_np(q) @ kvd[0]), rtol=1e-13)
+    # zero query: uniform weights -> mean of the values, lse = ln m
+    out, lse = oracle.sparse_mla_row(np.zeros((H, D_qk), np.uint16), kv, 0.1, D_v)
+    np.testing.assert_allclose(out, np.broadcast_to(kvd[:, :D_v].mean(0), (H, D_v)), rtol=1e-13, atol=1e-15)
+    assert np.all(lse == math.log(m))
+    # empty selection
+    out, lse = oracle.sparse_mla_row(q, kv[:0], 0.1, D_v)
+    assert np.all(out == 0.0) and np.all(np.isneginf(lse))
+    # values are the first D_v latent dims only: with the query's trailing
+    # (rope) dims at zero, the rows' trailing dims cannot change the output,
+    # while the logits do use every one of the D_qk dims
+    q0 = q.copy()
+    q0[:, D_v:] = 0
+    kv2 = kv.copy()
+    kv2[:, D_v:] = gen.f32_to_bf16_bits(np.full((m, D_qk - D_v), 3.0, np.float32))
+    o_a, l_a = oracle.sparse_mla_row(q0, kv, 0.1, D_v)
+    o_b, l_b = oracle.sparse_mla_row(q0, kv2, 0.1, D_v)
+    assert np.array_equal(o_a, o_b) and np.array_equal(l_a, l_b)
+    _, l_c = oracle.sparse_mla_row(q, kv2, 0.1, D_v)
+    _, l_d = oracle.sparse_mla_row(q, kv, 0.1, D_v)
+    assert not np.allclose(l_c, l_d)
+
+
+def test_attention_heads_are_independent_and_share_kv():
+    rng = np.random.default_rng(6)
+    H, D_qk, D_v, m = 5, 64, 32, 13
+    q = _rand_bf16(rng, (H, D_qk))
+    kv = _rand_bf16(rng, (m, D_qk))
+    out, lse = oracle.sparse_mla_row(q, kv, 0.2, D_v)
+    for h in range(H):
+        o1, l1 = oracle.sparse_mla_row(q[h:h + 1], kv, 0.2, D_v)
+        assert np.array_equal(o1[0], out[h]) and l1[0] == lse[h]
+    # selection order does not matter
+    perm = rng.permutation(m)
+    o2, l2 = oracle.sparse_mla_row(q, kv[perm], 0.2, D_v)
+    np.testing.assert_allclose(o2, out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l2, lse, rtol=1e-13)
+
+
+# --------------------------------------------------------------- chain
+def test_tiny_chain_invariants_and_k_covering_all():
+    wl = configs.WORKLOADS["tiny_prefill_L256"]
+    keys = configs.k_idx_bytes(wl, 0, np.arange(wl.N))
+    kv = configs.kv_bf16(wl, 0, np.arange(wl.N))
+    for t in (0, 31, 32, 200, 255):
+        r = oracle.prefill_row(wl, t, keys)
+        m = min(t + 1, wl.k)
+        sel = r["idx"][:m]
+        assert np.all(r["idx"][m:] == -1)
+        assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] <= t
+        # k = 256 >= every candidate count: sparse attention is dense causal attention
+        r2 = oracle.prefill_row(wl, t, keys, k=256)
+        assert np.array_equal(r2["idx"][: t + 1], np.arange(t + 1))
+        o_d, l_d = oracle.dense_mla_row(configs.q_bf16(wl, [t])[0], kv, t + 1, wl.scale, wl.D_v)
+        np.testing.assert_allclose(r2["out"], o_d, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(r2["lse"], l_d, rtol=1e-12, atol=1e-12)
+    # row 0 closed form: the only candidate is token 0
+    r0 = oracle.prefill_row(wl, 0, keys)
+    kvd = _bf16_to_np(kv[0])
+    assert np.array_equal(r0["out"], np.broadcast_to(kvd[: wl.D_v], (wl.H, wl.D_v)))
