@@ -1,0 +1,193 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek Sparse Attention forward path.
+ *
+ * The method (sources cited by page title, then section/equation):
+ *  [P1] "DeepSeek-V3.2" release thread with a technical-report walk-through
+ *       (freezhihu.org question 1978819912970555965)
+ *       §2.1.1 Lightning Indexer: index score
+ *              I_{t,s} = sum_j w^I_{t,j} ReLU(q^I_{t,j} . k^I_s), few heads, FP8;
+ *       §2.1.2 Fine-grained token selection: keep the top-k scored KV entries
+ *              per query token and attend over them only (O(L^2) -> O(Lk));
+ *       §2.2   DSA instantiated in MLA, MQA mode: every latent KV entry is
+ *              shared by all query heads of the token;
+ *       §2.3.2 k = 2048 selected KV tokens per query token.
+ *  [P2] "DeepSeek v3.2" analysis article (2048ai.net) §1.2: the indexer key is
+ *       one 128-dim vector per token, evaluated in FP8, ReLU for throughput.
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *    and allocates every buffer; the library never allocates device memory
+ *    and keeps no per-call state.  `stream` is a hipStream_t (NULL = default).
+ *  - Calls are asynchronous and ordered on `stream`.  Inputs are read only;
+ *    outputs are fully overwritten (including -1 / -inf padding).
+ *  - Arguments are validated on the host before any launch.  On failure the
+ *    call returns a status != DSA_OK, launches nothing and touches no output;
+ *    dsa_last_error_message() then describes the problem (thread-local).
+ *  - Launch failures map to DSA_ERR_HIP.  Faults inside kernels surface at
+ *    the caller's next synchronisation.
+ *  - Element types: FP8 = OCP E4M3FN bytes (unit scale); bf16 = raw 16-bit
+ *    patterns in uint16_t; scores, weights, outputs are IEEE fp32.
+ *  - Supported shapes: d_I = 128, 1 <= H_I <= 64, 1 <= H <= 128,
+ *    D_qk = 576, D_v = 512, 1 <= k <= 4096, page_size = 64.  Every pointer
+ *    must be 16-byte aligned.
+ *  - Positions: query row t of a prefill call sits at position q_pos0 + t and
+ *    its candidates are the keys s <= q_pos0 + t (itself included), capped at
+ *    N.  A decode query of sequence b sits at position ctx_len[b] - 1 and its
+ *    candidates are s = 0 .. ctx_len[b] - 1 (its own key is already cached).
+ *  - Selected indices are token positions (logical positions in paged
+ *    layouts), ascending, padded with -1 when fewer than k candidates exist.
+ *    Equal scores are broken toward the lower position.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,         /* null pointer, bad shape, misalignment */
+  DSA_ERR_UNSUPPORTED = 2,         /* valid but outside the supported shapes */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below the *_workspace_bytes query */
+  DSA_ERR_HIP = 4                  /* a HIP runtime call or launch failed */
+} dsa_status;
+
+typedef void* dsa_stream_t; /* hipStream_t */
+
+/* Version of this ABI (bumped on any signature change). */
+int32_t dsa_abi_version(void);
+/* Static description of a status code. */
+const char* dsa_status_string(dsa_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* dsa_last_error_message(void);
+
+/* ---------------------------------------------------------------------------
+ * Lightning-indexer scores, [P1] §2.1.1 (index-score equation).
+ *   q_idx  [T, H_I, d_I] FP8   query-side indexer vectors q^I_{t,j}
+ *   w      [T, H_I]      fp32  per-head weights w^I_{t,j} (any sign)
+ *   k_idx  [N, d_I]      FP8   indexer key of each token s
+ *   scores [T, ld]       fp32  out: scores[t*ld + s] = I_{t,s} for candidate s
+ *                              (s <= q_pos0 + t, s < N); -inf for 0 <= s < N
+ *                              that are not candidates.  ld >= N.
+ * Products are exact; sums are fp32 (relative error ~1e-6).
+ */
+dsa_status dsa_indexer_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T,
+                              int64_t N, int32_t H_I, int32_t d_I, int64_t q_pos0, float* scores, int64_t ld,
+                              dsa_stream_t stream);
+
+/* Indexer scores of B decode queries over paged indexer keys (same equation).
+ *   q_idx [B, H_I, d_I], w [B, H_I]
+ *   k_pool     [n_pages, page_size, d_I] FP8 pool of indexer keys
+ *   page_table [B, max_pages] int32: physical page of logical page p of seq b
+ *   ctx_len    [B] int32 (device), 1 <= ctx_len[b] <= max_ctx <= max_pages*page_size
+ *   scores     [B, ld] fp32 out, ld >= max_ctx: scores[b*ld + s] for s < ctx_len[b],
+ *              -inf for ctx_len[b] <= s < max_ctx.
+ * Token s of sequence b is row page_table[b][s / page_size]*page_size + s % page_size
+ * of the pool; a page id outside [0, n_pages) reads as a non-candidate (-inf).
+ */
+dsa_status dsa_indexer_scores_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool,
+                                    int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                                    const int32_t* ctx_len, int32_t page_size, int64_t B, int32_t H_I,
+                                    int32_t d_I, int64_t max_ctx, float* scores, int64_t ld,
+                                    dsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Per-row top-k selection, [P1] §2.1.2.
+ *   scores [T, ld] fp32 (finite values and -inf; NaN is undefined)
+ *   n_valid: NULL -> row t has candidates s < min(q_pos0 + t + 1, N);
+ *            else device int32 [T]: row t has candidates s < min(n_valid[t], N).
+ *   idx [T, k] int32 out: the min(k, n_t) positions with the largest scores,
+ *            ties to the lower position, ascending, then -1.  -0 equals +0.
+ * Deterministic: the output is a function of the score values only.
+ */
+dsa_status dsa_topk(const float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0,
+                    const int32_t* n_valid, int32_t k, int32_t* idx, dsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Sparse MLA attention in MQA mode, [P1] §2.1.2 (attention over the selected
+ * entries) with §2.2 (one latent KV row shared by all heads).
+ *   q   [T, H, D_qk] bf16  per-head query in the latent space (512 + 64 rope)
+ *   kv  [N, D_qk]    bf16  latent KV rows; keys use all D_qk dims, values
+ *                          the first D_v dims
+ *   idx [T, k] int32       selected rows per query; entries < 0 or >= N skip
+ *   out [T, H, D_v] fp32   out = sum_s softmax_s(scale * q.kv_s) kv_s[:D_v]
+ *   lse [T, H] fp32        natural-log log-sum-exp of the scaled logits
+ * A row with no valid entry yields out = 0 and lse = -inf.  Products are
+ * bf16 x bf16 with fp32 accumulation; probabilities enter the value product
+ * as bf16 (relative error ~2e-3).
+ * ws: scratch for split-key partials when T is small; size from
+ * dsa_sparse_mla_fwd_workspace_bytes (0 is valid when that returns 0).
+ */
+size_t dsa_sparse_mla_fwd_workspace_bytes(int64_t T, int32_t H, int32_t D_v, int32_t k);
+dsa_status dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int64_t T,
+                              int64_t N, int32_t H, int32_t D_qk, int32_t D_v, int32_t k, float scale,
+                              float* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+/* Same attention for B decode queries over a paged latent pool
+ *   q [B, H, D_qk]; kv_pool [n_pages, page_size, D_qk]; page_table/ctx_len as above;
+ *   idx [B, k] logical positions; entries < 0 or >= ctx_len[b] skip.
+ */
+size_t dsa_sparse_mla_fwd_paged_workspace_bytes(int64_t B, int32_t H, int32_t D_v, int32_t k);
+dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, int64_t n_pages,
+                                    const int32_t* page_table, int32_t max_pages, const int32_t* ctx_len,
+                                    int32_t page_size, const int32_t* idx, int64_t B, int32_t H,
+                                    int32_t D_qk, int32_t D_v, int32_t k, float scale, float* out,
+                                    float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused prefill of one sequence: indexer -> top-k -> sparse attention for the
+ * T queries at positions q_pos0 .. q_pos0+T-1 over keys 0 .. N-1 (N >= q_pos0+T
+ * is not required; candidates are capped at N).  The L x L score matrix is
+ * never formed: scores live in a row-tiled part of the workspace.
+ *   idx may be NULL (then kept in the workspace); otherwise [T, k] out.
+ */
+size_t dsa_forward_prefill_workspace_bytes(int64_t T, int64_t N, int32_t H, int32_t D_v, int32_t k);
+dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                               const uint16_t* kv, int64_t T, int64_t N, int32_t H_I, int32_t d_I, int32_t H,
+                               int32_t D_qk, int32_t D_v, int32_t k, int64_t q_pos0, float scale,
+                               int32_t* idx, float* out, float* lse, void* ws, size_t ws_bytes,
+                               dsa_stream_t stream);
+
+/* Row-tile plan of dsa_forward_prefill: the fused call runs the indexer and
+ * top-k over consecutive row tiles of *tile_rows rows, using a score scratch of
+ * row stride *score_ld (fp32) at the start of ws, then one sparse-attention
+ * launch over all T rows.  Lets a caller replay the fused call stage by stage
+ * with dsa_indexer_scores / dsa_topk / dsa_sparse_mla_fwd (e.g. to time each
+ * kernel).  Host pointers; returns DSA_ERR_INVALID_ARG for T < 1 or N < 1. */
+dsa_status dsa_forward_prefill_plan(int64_t T, int64_t N, int64_t* tile_rows, int64_t* score_ld);
+
+/* Fused decode of B sequences with contiguous caches, one query each:
+ *   k_idx [B, N, d_I], kv [B, N, D_qk]; ctx_len [B] (device) with
+ *   1 <= ctx_len[b] <= N.  Other arguments as in the calls above.
+ */
+size_t dsa_forward_decode_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t D_v, int32_t k);
+dsa_status dsa_forward_decode(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                              const uint16_t* kv, const int32_t* ctx_len, int64_t B, int64_t N, int32_t H_I,
+                              int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v, int32_t k, float scale,
+                              int32_t* idx, float* out, float* lse, void* ws, size_t ws_bytes,
+                              dsa_stream_t stream);
+
+/* Fused decode of B sequences over paged caches (64-token pages):
+ *   k_pool [n_pages, page_size, d_I], kv_pool [n_pages, page_size, D_qk],
+ *   page_table [B, max_pages], ctx_len [B] with ctx_len[b] <= max_ctx <=
+ *   max_pages * page_size.  Returned indices are logical positions.
+ */
+size_t dsa_forward_decode_paged_workspace_bytes(int64_t B, int64_t max_ctx, int32_t H, int32_t D_v,
+                                                int32_t k);
+dsa_status dsa_forward_decode_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool,
+                                    const uint16_t* q, const uint16_t* kv_pool, int64_t n_pages,
+                                    const int32_t* page_table, int32_t max_pages, const int32_t* ctx_len,
+                                    int32_t page_size, int64_t B, int64_t max_ctx, int32_t H_I, int32_t d_I,
+                                    int32_t H, int32_t D_qk, int32_t D_v, int32_t k, float scale,
+                                    int32_t* idx, float* out, float* lse, void* ws, size_t ws_bytes,
+                                    dsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,63 @@
+"""Parallel oracle row jobs (test infrastructure).
+
+The oracle itself stays single-threaded; independent query rows run in
+separate spawned processes, each regenerating the workload's inputs on the
+host (keys are generated once per process and cached).
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ProcessPoolExecutor
+import multiprocessing as mp
+
+import numpy as np
+
+_keys_cache: dict = {}
+
+
+def _workload(name: str, k: int | None):
+    from dsa_inputs import configs
+    wl = configs.WORKLOADS[name]
+    return wl if k is None else wl.with_k(k)
+
+
+def _prefill_keys(wl, n: int) -> np.ndarray:
+    from dsa_inputs import configs
+    key = (wl.name, 0)
+    have = _keys_cache.get(key)
+    if have is None or have.shape[0] < n:
+        _keys_cache.clear()
+        have = configs.k_idx_bytes(wl, 0, np.arange(wl.N))
+        _keys_cache[key] = have
+    return have
+
+
+def prefill_job(args):
+    """args = (workload name, row t, k or None) -> oracle chain dict."""
+    import oracle
+    name, t, k = args
+    wl = _workload(name, k)
+    keys = _prefill_keys(wl, t + 1)
+    return oracle.prefill_row(wl, int(t), keys)
+
+
+def decode_job(args):
+    """args = (workload name, sequence b, k or None) -> oracle chain dict."""
+    import oracle
+    name, b, k = args
+    wl = _workload(name, k)
+    return oracle.decode_row(wl, int(b))
+
+
+def default_procs() -> int:
+    n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def run(fn, jobs, procs: int | None = None):
+    procs = procs or default_procs()
+    if procs == 1 or len(jobs) == 1:
+        return [fn(j) for j in jobs]
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=min(procs, len(jobs)), mp_context=ctx) as ex:
+        return list(ex.map(fn, jobs, chunksize=max(1, len(jobs) // (4 * procs))))

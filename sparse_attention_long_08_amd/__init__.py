@@ -1,0 +1,173 @@
+"""Python binding of libdsa.so, the gfx950 DeepSeek Sparse Attention forward
+library.
+
+Argument marshalling only: each function has the name of the C-ABI entry
+point it calls (see include/dsa.h), takes torch CUDA tensors for device
+buffers and raises ``DsaError`` on a non-OK status.  Every step of the path
+runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+_lib = None
+
+_c_i32, _c_i64, _c_f32, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+# argument type lists of every exported entry point (mirrors include/dsa.h)
+SIGNATURES = {
+    "dsa_abi_version": (_c_i32, []),
+    "dsa_status_string": (ctypes.c_char_p, [_c_i32]),
+    "dsa_last_error_message": (ctypes.c_char_p, []),
+    "dsa_indexer_scores": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64, _c_p, _c_i64, _c_p]),
+    "dsa_indexer_scores_paged": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32, _c_i64, _c_i32,
+                                          _c_i32, _c_i64, _c_p, _c_i64, _c_p]),
+    "dsa_topk": (_c_i32, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_i32, _c_p, _c_p]),
+    "dsa_sparse_mla_fwd_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
+    "dsa_sparse_mla_fwd": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p,
+                                    _c_p, _c_p, _c_sz, _c_p]),
+    "dsa_sparse_mla_fwd_paged_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
+    "dsa_sparse_mla_fwd_paged": (_c_i32, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i64, _c_i32,
+                                          _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "dsa_forward_prefill_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32]),
+    "dsa_forward_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                     _c_i32, _c_i32, _c_i64, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "dsa_forward_prefill_plan": (_c_i32, [_c_i64, _c_i64, _c_p, _c_p]),
+    "dsa_forward_decode_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32]),
+    "dsa_forward_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                    _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "dsa_forward_decode_paged_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32]),
+    "dsa_forward_decode_paged": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32,
+                                          _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                                          _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+}
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+def build() -> str:
+    from . import _builder
+    return _builder.build()
+
+
+def load():
+    """Load libdsa.so (building it first only when no built library exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _call(name: str, *args) -> None:
+    lib = load()
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        raise DsaError(name, st, lib.dsa_last_error_message().decode())
+
+
+def dsa_abi_version() -> int:
+    return load().dsa_abi_version()
+
+
+def dsa_indexer_scores(q_idx, w, k_idx, T, N, H_I, d_I, q_pos0, scores, ld, stream=None):
+    _call("dsa_indexer_scores", _ptr(q_idx), _ptr(w), _ptr(k_idx), T, N, H_I, d_I, q_pos0, _ptr(scores), ld,
+          _stream(stream))
+
+
+def dsa_indexer_scores_paged(q_idx, w, k_pool, n_pages, page_table, max_pages, ctx_len, page_size, B, H_I, d_I,
+                             max_ctx, scores, ld, stream=None):
+    _call("dsa_indexer_scores_paged", _ptr(q_idx), _ptr(w), _ptr(k_pool), n_pages, _ptr(page_table), max_pages,
+          _ptr(ctx_len), page_size, B, H_I, d_I, max_ctx, _ptr(scores), ld, _stream(stream))
+
+
+def dsa_topk(scores, ld, T, N, q_pos0, n_valid, k, idx, stream=None):
+    _call("dsa_topk", _ptr(scores), ld, T, N, q_pos0, _ptr(n_valid), k, _ptr(idx), _stream(stream))
+
+
+def dsa_sparse_mla_fwd_workspace_bytes(T, H, D_v, k) -> int:
+    return load().dsa_sparse_mla_fwd_workspace_bytes(T, H, D_v, k)
+
+
+def dsa_sparse_mla_fwd(q, kv, idx, T, N, H, D_qk, D_v, k, scale, out, lse, ws, ws_bytes, stream=None):
+    _call("dsa_sparse_mla_fwd", _ptr(q), _ptr(kv), _ptr(idx), T, N, H, D_qk, D_v, k, scale, _ptr(out), _ptr(lse),
+          _ptr(ws), ws_bytes, _stream(stream))
+
+
+def dsa_sparse_mla_fwd_paged_workspace_bytes(B, H, D_v, k) -> int:
+    return load().dsa_sparse_mla_fwd_paged_workspace_bytes(B, H, D_v, k)
+
+
+def dsa_sparse_mla_fwd_paged(q, kv_pool, n_pages, page_table, max_pages, ctx_len, page_size, idx, B, H, D_qk, D_v,
+                             k, scale, out, lse, ws, ws_bytes, stream=None):
+    _call("dsa_sparse_mla_fwd_paged", _ptr(q), _ptr(kv_pool), n_pages, _ptr(page_table), max_pages, _ptr(ctx_len),
+          page_size, _ptr(idx), B, H, D_qk, D_v, k, scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+          _stream(stream))
+
+
+def dsa_forward_prefill_workspace_bytes(T, N, H, D_v, k) -> int:
+    return load().dsa_forward_prefill_workspace_bytes(T, N, H, D_v, k)
+
+
+def dsa_forward_prefill(q_idx, w, k_idx, q, kv, T, N, H_I, d_I, H, D_qk, D_v, k, q_pos0, scale, idx, out, lse, ws,
+                        ws_bytes, stream=None):
+    _call("dsa_forward_prefill", _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(q), _ptr(kv), T, N, H_I, d_I, H, D_qk,
+          D_v, k, q_pos0, scale, _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def dsa_forward_prefill_plan(T, N):
+    """Returns (tile_rows, score_ld) of the fused prefill's row tiling."""
+    tr, ld = ctypes.c_int64(0), ctypes.c_int64(0)
+    _call("dsa_forward_prefill_plan", T, N, ctypes.byref(tr), ctypes.byref(ld))
+    return tr.value, ld.value
+
+
+def dsa_forward_decode_workspace_bytes(B, N, H, D_v, k) -> int:
+    return load().dsa_forward_decode_workspace_bytes(B, N, H, D_v, k)
+
+
+def dsa_forward_decode(q_idx, w, k_idx, q, kv, ctx_len, B, N, H_I, d_I, H, D_qk, D_v, k, scale, idx, out, lse, ws,
+                       ws_bytes, stream=None):
+    _call("dsa_forward_decode", _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(q), _ptr(kv), _ptr(ctx_len), B, N, H_I,
+          d_I, H, D_qk, D_v, k, scale, _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def dsa_forward_decode_paged_workspace_bytes(B, max_ctx, H, D_v, k) -> int:
+    return load().dsa_forward_decode_paged_workspace_bytes(B, max_ctx, H, D_v, k)
+
+
+def dsa_forward_decode_paged(q_idx, w, k_pool, q, kv_pool, n_pages, page_table, max_pages, ctx_len, page_size, B,
+                             max_ctx, H_I, d_I, H, D_qk, D_v, k, scale, idx, out, lse, ws, ws_bytes, stream=None):
+    _call("dsa_forward_decode_paged", _ptr(q_idx), _ptr(w), _ptr(k_pool), _ptr(q), _ptr(kv_pool), n_pages,
+          _ptr(page_table), max_pages, _ptr(ctx_len), page_size, B, max_ctx, H_I, d_I, H, D_qk, D_v, k, scale,
+          _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))

@@ -1,0 +1,377 @@
+// C ABI of the DSA forward library: host-side validation, workspace sizing
+// and kernel dispatch.  Every check runs before any launch, so a rejected
+// call touches no output.  See include/dsa.h for the contract of each call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dsa_status ok() {
+  g_err[0] = '\0';
+  return DSA_OK;
+}
+
+dsa_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxCtx = 262144;  // longest row the top-k bitmaps cover
+constexpr int32_t kMaxK = 4096;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p) REQUIRE((p) != nullptr, DSA_ERR_INVALID_ARG, "%s is NULL", #p)
+#define REQUIRE_AL(p) REQUIRE(aligned16(p), DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p)
+
+dsa_status check_indexer_shape(int32_t H_I, int32_t d_I) {
+  REQUIRE(d_I == 128, DSA_ERR_UNSUPPORTED, "d_I must be 128 (got %d)", d_I);
+  REQUIRE(H_I >= 1 && H_I <= 64, DSA_ERR_UNSUPPORTED, "H_I must be in [1, 64] (got %d)", H_I);
+  return DSA_OK;
+}
+
+dsa_status check_mla_shape(int32_t H, int32_t D_qk, int32_t D_v, int32_t k) {
+  REQUIRE(D_qk == 576, DSA_ERR_UNSUPPORTED, "D_qk must be 576 (got %d)", D_qk);
+  REQUIRE(D_v == 512, DSA_ERR_UNSUPPORTED, "D_v must be 512 (got %d)", D_v);
+  REQUIRE(H >= 1 && H <= 128, DSA_ERR_UNSUPPORTED, "H must be in [1, 128] (got %d)", H);
+  REQUIRE(k >= 1 && k <= kMaxK, DSA_ERR_UNSUPPORTED, "k must be in [1, %d] (got %d)", kMaxK, k);
+  return DSA_OK;
+}
+
+dsa_status check_paged(const void* pool, int64_t n_pages, const int32_t* page_table, int32_t max_pages,
+                       const int32_t* ctx_len, int32_t page_size, int64_t max_ctx) {
+  REQUIRE_PTR(pool);
+  REQUIRE_PTR(page_table);
+  REQUIRE_PTR(ctx_len);
+  REQUIRE_AL(pool);
+  REQUIRE(page_size == 64, DSA_ERR_UNSUPPORTED, "page_size must be 64 (got %d)", page_size);
+  REQUIRE(n_pages >= 1 && max_pages >= 1, DSA_ERR_INVALID_ARG, "n_pages and max_pages must be >= 1");
+  REQUIRE(max_ctx >= 1 && max_ctx <= (int64_t)max_pages * page_size, DSA_ERR_INVALID_ARG,
+          "max_ctx (%lld) must be in [1, max_pages*page_size]", (long long)max_ctx);
+  return DSA_OK;
+}
+
+// workspace pieces
+size_t mla_ws(int64_t T, int32_t H, int32_t k) {
+  const int32_t s = dsa::sparse_mla_splits(T, H, k);
+  if (s <= 1) return 0;
+  return round_up(sizeof(float) * (size_t)T * s * H * 512) + round_up(sizeof(float) * (size_t)T * s * H);
+}
+
+int64_t prefill_tile_rows(int64_t T, int64_t N) {
+  // score scratch of about 1 GiB (enough rows to fill the GPU, bounded memory)
+  int64_t rows = (int64_t)(((int64_t)1 << 28) / std::max<int64_t>(N, 1));
+  rows = std::max<int64_t>(rows, 256);
+  rows = (rows + 7) / 8 * 8;
+  return std::min<int64_t>(rows, std::max<int64_t>(T, 1));
+}
+
+int64_t score_ld(int64_t N) { return (N + 63) / 64 * 64; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return 1; }
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* dsa_last_error_message(void) { return g_err; }
+
+dsa_status dsa_indexer_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
+                              int32_t H_I, int32_t d_I, int64_t q_pos0, float* scores, int64_t ld,
+                              dsa_stream_t stream) {
+  REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "T must be >= 0 and N >= 1");
+  REQUIRE(q_pos0 >= 0, DSA_ERR_INVALID_ARG, "q_pos0 must be >= 0");
+  REQUIRE(ld >= N, DSA_ERR_INVALID_ARG, "ld (%lld) must be >= N (%lld)", (long long)ld, (long long)N);
+  if (dsa_status s = check_indexer_shape(H_I, d_I)) return s;
+  if (T == 0) return ok();
+  REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(k_idx); REQUIRE_PTR(scores);
+  REQUIRE_AL(q_idx); REQUIRE_AL(k_idx); REQUIRE_AL(w); REQUIRE_AL(scores);
+  return hip_check(dsa::launch_indexer_prefill(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, true,
+                                               (hipStream_t)stream),
+                   "indexer launch");
+}
+
+dsa_status dsa_indexer_scores_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool, int64_t n_pages,
+                                    const int32_t* page_table, int32_t max_pages, const int32_t* ctx_len,
+                                    int32_t page_size, int64_t B, int32_t H_I, int32_t d_I, int64_t max_ctx,
+                                    float* scores, int64_t ld, dsa_stream_t stream) {
+  REQUIRE(B >= 0, DSA_ERR_INVALID_ARG, "B must be >= 0");
+  if (dsa_status s = check_indexer_shape(H_I, d_I)) return s;
+  if (dsa_status s = check_paged(k_pool, n_pages, page_table, max_pages, ctx_len, page_size, max_ctx)) return s;
+  REQUIRE(ld >= max_ctx, DSA_ERR_INVALID_ARG, "ld must be >= max_ctx");
+  if (B == 0) return ok();
+  REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(scores);
+  REQUIRE_AL(q_idx); REQUIRE_AL(w); REQUIRE_AL(scores);
+  dsa::PagedArgs pa{page_table, max_pages, page_size, n_pages};
+  return hip_check(dsa::launch_indexer_decode(q_idx, w, k_pool, 0, &pa, ctx_len, B, max_ctx, H_I, scores, ld,
+                                              (hipStream_t)stream),
+                   "paged indexer launch");
+}
+
+dsa_status dsa_topk(const float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0, const int32_t* n_valid,
+                    int32_t k, int32_t* idx, dsa_stream_t stream) {
+  REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "T must be >= 0 and N >= 1");
+  REQUIRE(N <= kMaxCtx, DSA_ERR_UNSUPPORTED, "N must be <= %lld", (long long)kMaxCtx);
+  REQUIRE(ld >= N, DSA_ERR_INVALID_ARG, "ld must be >= N");
+  REQUIRE(q_pos0 >= 0, DSA_ERR_INVALID_ARG, "q_pos0 must be >= 0");
+  REQUIRE(k >= 1 && k <= kMaxK, DSA_ERR_UNSUPPORTED, "k must be in [1, %d]", kMaxK);
+  if (T == 0) return ok();
+  REQUIRE_PTR(scores); REQUIRE_PTR(idx);
+  REQUIRE_AL(scores); REQUIRE_AL(idx);
+  return hip_check(dsa::launch_topk(scores, ld, T, N, q_pos0, n_valid, k, idx, (hipStream_t)stream),
+                   "top-k launch");
+}
+
+size_t dsa_sparse_mla_fwd_workspace_bytes(int64_t T, int32_t H, int32_t /*D_v*/, int32_t k) {
+  return mla_ws(T, H, k);
+}
+
+static dsa_status run_mla(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int64_t T, int32_t H,
+                          int32_t k, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                          bool seq_per_query, int64_t stride, int64_t seq_len, const int32_t* ctx_len,
+                          const dsa::PagedArgs* paged, hipStream_t st) {
+  const size_t need = mla_ws(T, H, k);
+  REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  REQUIRE(need == 0 || ws != nullptr, DSA_ERR_INVALID_ARG, "ws is NULL");
+  dsa::MlaArgs a{};
+  a.q = q;
+  a.kv = kv;
+  a.idx = idx;
+  a.T = T;
+  a.H = H;
+  a.k = k;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  a.seq_per_query = seq_per_query;
+  a.stride = stride;
+  a.seq_len = seq_len;
+  a.ctx_len = ctx_len;
+  a.paged = paged;
+  a.n_split = dsa::sparse_mla_splits(T, H, k);
+  if (a.n_split > 1) {
+    a.part_o = (float*)ws;
+    a.part_lse = (float*)((char*)ws + round_up(sizeof(float) * (size_t)T * a.n_split * H * 512));
+  }
+  return hip_check(dsa::launch_sparse_mla(a, st), "sparse attention launch");
+}
+
+dsa_status dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int64_t T, int64_t N,
+                              int32_t H, int32_t D_qk, int32_t D_v, int32_t k, float scale, float* out,
+                              float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "T must be >= 0 and N >= 1");
+  if (dsa_status s = check_mla_shape(H, D_qk, D_v, k)) return s;
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (T == 0) return ok();
+  REQUIRE_PTR(q); REQUIRE_PTR(kv); REQUIRE_PTR(idx); REQUIRE_PTR(out); REQUIRE_PTR(lse);
+  REQUIRE_AL(q); REQUIRE_AL(kv); REQUIRE_AL(idx); REQUIRE_AL(out); REQUIRE_AL(lse);
+  return run_mla(q, kv, idx, T, H, k, scale, out, lse, ws, ws_bytes, false, N, N, nullptr, nullptr,
+                 (hipStream_t)stream);
+}
+
+size_t dsa_sparse_mla_fwd_paged_workspace_bytes(int64_t B, int32_t H, int32_t /*D_v*/, int32_t k) {
+  return mla_ws(B, H, k);
+}
+
+dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, int64_t n_pages,
+                                    const int32_t* page_table, int32_t max_pages, const int32_t* ctx_len,
+                                    int32_t page_size, const int32_t* idx, int64_t B, int32_t H, int32_t D_qk,
+                                    int32_t D_v, int32_t k, float scale, float* out, float* lse, void* ws,
+                                    size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(B >= 0, DSA_ERR_INVALID_ARG, "B must be >= 0");
+  if (dsa_status s = check_mla_shape(H, D_qk, D_v, k)) return s;
+  const int64_t cap = (int64_t)max_pages * page_size;
+  if (dsa_status s = check_paged(kv_pool, n_pages, page_table, max_pages, ctx_len, page_size,
+                                 cap > 0 ? cap : 1))
+    return s;
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (B == 0) return ok();
+  REQUIRE_PTR(q); REQUIRE_PTR(idx); REQUIRE_PTR(out); REQUIRE_PTR(lse);
+  REQUIRE_AL(q); REQUIRE_AL(idx); REQUIRE_AL(out); REQUIRE_AL(lse);
+  dsa::PagedArgs pa{page_table, max_pages, page_size, n_pages};
+  return run_mla(q, kv_pool, idx, B, H, k, scale, out, lse, ws, ws_bytes, true, 0, cap, ctx_len, &pa,
+                 (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------ fused prefill
+size_t dsa_forward_prefill_workspace_bytes(int64_t T, int64_t N, int32_t H, int32_t /*D_v*/, int32_t k) {
+  if (T <= 0 || N <= 0 || k <= 0) return 0;
+  const int64_t rows = prefill_tile_rows(T, N);
+  return round_up(sizeof(float) * (size_t)rows * score_ld(N)) + round_up(sizeof(int32_t) * (size_t)T * k) +
+         mla_ws(T, H, k);
+}
+
+dsa_status dsa_forward_prefill_plan(int64_t T, int64_t N, int64_t* tile_rows, int64_t* score_ld_out) {
+  REQUIRE(T >= 1 && N >= 1, DSA_ERR_INVALID_ARG, "T and N must be >= 1");
+  REQUIRE_PTR(tile_rows);
+  REQUIRE_PTR(score_ld_out);
+  *tile_rows = prefill_tile_rows(T, N);
+  *score_ld_out = score_ld(N);
+  return ok();
+}
+
+dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                               const uint16_t* kv, int64_t T, int64_t N, int32_t H_I, int32_t d_I, int32_t H,
+                               int32_t D_qk, int32_t D_v, int32_t k, int64_t q_pos0, float scale, int32_t* idx,
+                               float* out, float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "T must be >= 0 and N >= 1");
+  REQUIRE(N <= kMaxCtx, DSA_ERR_UNSUPPORTED, "N must be <= %lld", (long long)kMaxCtx);
+  REQUIRE(q_pos0 >= 0, DSA_ERR_INVALID_ARG, "q_pos0 must be >= 0");
+  if (dsa_status s = check_indexer_shape(H_I, d_I)) return s;
+  if (dsa_status s = check_mla_shape(H, D_qk, D_v, k)) return s;
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (T == 0) return ok();
+  REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(k_idx); REQUIRE_PTR(q); REQUIRE_PTR(kv);
+  REQUIRE_PTR(out); REQUIRE_PTR(lse);
+  REQUIRE_AL(q_idx); REQUIRE_AL(w); REQUIRE_AL(k_idx); REQUIRE_AL(q); REQUIRE_AL(kv); REQUIRE_AL(out);
+  REQUIRE_AL(lse);
+  if (idx) REQUIRE_AL(idx);
+  const size_t need = dsa_forward_prefill_workspace_bytes(T, N, H, D_v, k);
+  REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  REQUIRE(ws != nullptr, DSA_ERR_INVALID_ARG, "ws is NULL");
+  REQUIRE_AL(ws);
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t rows = prefill_tile_rows(T, N);
+  const int64_t ld = score_ld(N);
+  char* p = (char*)ws;
+  float* scores = (float*)p;
+  p += round_up(sizeof(float) * (size_t)rows * ld);
+  int32_t* idx_ws = (int32_t*)p;
+  p += round_up(sizeof(int32_t) * (size_t)T * k);
+  int32_t* sel = idx ? idx : idx_ws;
+  for (int64_t r0 = 0; r0 < T; r0 += rows) {
+    const int64_t tr = std::min(rows, T - r0);
+    if (dsa_status s = hip_check(dsa::launch_indexer_prefill(q_idx + r0 * H_I * 128, w + r0 * H_I, k_idx, tr, N,
+                                                              H_I, q_pos0 + r0, scores, ld, false, st),
+                                 "indexer launch"))
+      return s;
+    if (dsa_status s = hip_check(dsa::launch_topk(scores, ld, tr, N, q_pos0 + r0, nullptr, k, sel + r0 * k, st),
+                                 "top-k launch"))
+      return s;
+  }
+  return run_mla(q, kv, sel, T, H, k, scale, out, lse, p, ws_bytes - (size_t)(p - (char*)ws), false, N, N,
+                 nullptr, nullptr, st);
+}
+
+// ------------------------------------------------------------------ fused decode
+static size_t decode_ws(int64_t B, int64_t max_ctx, int32_t H, int32_t k) {
+  if (B <= 0 || max_ctx <= 0 || k <= 0) return 0;
+  return round_up(sizeof(float) * (size_t)B * score_ld(max_ctx)) + round_up(sizeof(int32_t) * (size_t)B * k) +
+         mla_ws(B, H, k);
+}
+
+size_t dsa_forward_decode_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t /*D_v*/, int32_t k) {
+  return decode_ws(B, N, H, k);
+}
+
+size_t dsa_forward_decode_paged_workspace_bytes(int64_t B, int64_t max_ctx, int32_t H, int32_t /*D_v*/,
+                                                int32_t k) {
+  return decode_ws(B, max_ctx, H, k);
+}
+
+static dsa_status run_decode(const uint8_t* q_idx, const float* w, const uint8_t* keys, const uint16_t* q,
+                             const uint16_t* kv, const int32_t* ctx_len, int64_t B, int64_t max_ctx, int32_t H_I,
+                             int32_t H, int32_t k, float scale, int32_t* idx, float* out, float* lse, void* ws,
+                             size_t ws_bytes, int64_t stride, const dsa::PagedArgs* paged, hipStream_t st) {
+  const size_t need = decode_ws(B, max_ctx, H, k);
+  REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  REQUIRE(ws != nullptr, DSA_ERR_INVALID_ARG, "ws is NULL");
+  REQUIRE_AL(ws);
+  const int64_t ld = score_ld(max_ctx);
+  char* p = (char*)ws;
+  float* scores = (float*)p;
+  p += round_up(sizeof(float) * (size_t)B * ld);
+  int32_t* idx_ws = (int32_t*)p;
+  p += round_up(sizeof(int32_t) * (size_t)B * k);
+  int32_t* sel = idx ? idx : idx_ws;
+  if (dsa_status s = hip_check(dsa::launch_indexer_decode(q_idx, w, keys, stride, paged, ctx_len, B, max_ctx, H_I,
+                                                          scores, ld, st),
+                               "decode indexer launch"))
+    return s;
+  if (dsa_status s = hip_check(dsa::launch_topk(scores, ld, B, max_ctx, 0, ctx_len, k, sel, st), "top-k launch"))
+    return s;
+  const int64_t seq_len = paged ? (int64_t)paged->max_pages * paged->page_size : stride;
+  return run_mla(q, kv, sel, B, H, k, scale, out, lse, p, ws_bytes - (size_t)(p - (char*)ws), true, stride,
+                 seq_len, ctx_len, paged, st);
+}
+
+dsa_status dsa_forward_decode(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                              const uint16_t* kv, const int32_t* ctx_len, int64_t B, int64_t N, int32_t H_I,
+                              int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v, int32_t k, float scale,
+                              int32_t* idx, float* out, float* lse, void* ws, size_t ws_bytes,
+                              dsa_stream_t stream) {
+  REQUIRE(B >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "B must be >= 0 and N >= 1");
+  REQUIRE(N <= kMaxCtx, DSA_ERR_UNSUPPORTED, "N must be <= %lld", (long long)kMaxCtx);
+  if (dsa_status s = check_indexer_shape(H_I, d_I)) return s;
+  if (dsa_status s = check_mla_shape(H, D_qk, D_v, k)) return s;
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (B == 0) return ok();
+  REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(k_idx); REQUIRE_PTR(q); REQUIRE_PTR(kv);
+  REQUIRE_PTR(ctx_len); REQUIRE_PTR(out); REQUIRE_PTR(lse);
+  REQUIRE_AL(q_idx); REQUIRE_AL(w); REQUIRE_AL(k_idx); REQUIRE_AL(q); REQUIRE_AL(kv); REQUIRE_AL(out);
+  REQUIRE_AL(lse);
+  if (idx) REQUIRE_AL(idx);
+  return run_decode(q_idx, w, k_idx, q, kv, ctx_len, B, N, H_I, H, k, scale, idx, out, lse, ws, ws_bytes, N,
+                    nullptr, (hipStream_t)stream);
+}
+
+dsa_status dsa_forward_decode_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool, const uint16_t* q,
+                                    const uint16_t* kv_pool, int64_t n_pages, const int32_t* page_table,
+                                    int32_t max_pages, const int32_t* ctx_len, int32_t page_size, int64_t B,
+                                    int64_t max_ctx, int32_t H_I, int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v,
+                                    int32_t k, float scale, int32_t* idx, float* out, float* lse, void* ws,
+                                    size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(B >= 0, DSA_ERR_INVALID_ARG, "B must be >= 0");
+  REQUIRE(max_ctx <= kMaxCtx, DSA_ERR_UNSUPPORTED, "max_ctx must be <= %lld", (long long)kMaxCtx);
+  if (dsa_status s = check_indexer_shape(H_I, d_I)) return s;
+  if (dsa_status s = check_mla_shape(H, D_qk, D_v, k)) return s;
+  if (dsa_status s = check_paged(k_pool, n_pages, page_table, max_pages, ctx_len, page_size, max_ctx)) return s;
+  REQUIRE_PTR(kv_pool);
+  REQUIRE_AL(kv_pool);
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (B == 0) return ok();
+  REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(q); REQUIRE_PTR(out); REQUIRE_PTR(lse);
+  REQUIRE_AL(q_idx); REQUIRE_AL(w); REQUIRE_AL(q); REQUIRE_AL(out); REQUIRE_AL(lse);
+  if (idx) REQUIRE_AL(idx);
+  dsa::PagedArgs pa{page_table, max_pages, page_size, n_pages};
+  return run_decode(q_idx, w, k_pool, q, kv_pool, ctx_len, B, max_ctx, H_I, H, k, scale, idx, out, lse, ws,
+                    ws_bytes, 0, &pa, (hipStream_t)stream);
+}
+
+}  // extern "C"

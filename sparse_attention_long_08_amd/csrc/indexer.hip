@@ -1,0 +1,285 @@
+// Lightning indexer on gfx950 FP8 matrix cores.
+//
+// Computes the index score of DeepSeek-V3.2's lightning indexer ("DeepSeek-
+// V3.2" report walk-through, §2.1.1, index-score equation):
+//   I[t, s] = sum_j w[t, j] * ReLU(q_I[t, j, :] . k_I[s, :])
+// with FP8 E4M3 inputs (few heads, 128-dim keys: analysis article §1.2).
+//
+// Mapping: the head-by-key dot products of one query are a 16x128 by 128x16
+// FP8 MFMA per (16-head tile, 16-key block); heads sit on the MFMA rows so a
+// lane holds 4 heads of one key and the head sum is mostly in-lane.  ReLU and
+// the w-weighting are fused into the accumulator epilogue (fp32), and the
+// remaining sum over the four lane groups is a 4x4 transposing reduction that
+// leaves each lane with one finished score of a 64-key group, so stores are
+// fully coalesced.  Keys are streamed (never the L x L matrix): the prefill
+// kernel stages 64-key groups in LDS and shares them across the workgroup's
+// query rows; the decode kernel streams each key once from HBM.
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+
+constexpr int kIdxD = 128;      // indexer head dim
+constexpr int kKeyStride = 144;  // LDS row stride of a staged key (bytes), padded against bank conflicts
+
+// On entry lane (g, c) = (lane/16, lane%16) holds its partial for key
+// 16*b + c of a 64-key group in p[b]; returns the sum over all four lane
+// groups for key 16*g + c.
+__device__ __forceinline__ float group_transpose_reduce(float p0, float p1, float p2, float p3, int g) {
+  const bool hi = (g & 2) != 0;
+  float y0 = shfl_xor_f(hi ? p0 : p2, 32);
+  float y1 = shfl_xor_f(hi ? p1 : p3, 32);
+  float a0 = (hi ? p2 : p0) + y0;
+  float a1 = (hi ? p3 : p1) + y1;
+  const bool odd = (g & 1) != 0;
+  float z = shfl_xor_f(odd ? a0 : a1, 16);
+  return (odd ? a1 : a0) + z;
+}
+
+template <int NT>
+__device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
+                                           int64_t r, bool valid, int32_t H_I, int col, int grp, v8i (&a)[NT],
+                                           float (&wr)[NT][4]) {
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) {
+    const int head = 16 * tl + col;
+    if (valid && head < H_I) {
+      const v4i* p = (const v4i*)(q_idx + ((r * H_I + head) * kIdxD + 32 * grp));
+      v4i lo = p[0], hi = p[1];
+      a[tl] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    } else {
+      a[tl] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hw = 16 * tl + 4 * grp + i;
+      wr[tl][i] = (valid && hw < H_I) ? w[r * H_I + hw] : 0.f;
+    }
+  }
+}
+
+// Weighted, rectified head sum of one query against one 16-key block.
+template <int NT>
+__device__ __forceinline__ float head_sum(const v8i (&a)[NT], const float (&wr)[NT][4], v8i b) {
+  float s = 0.f;
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) {
+    v4f c = mfma_f8_16x16x128(a[tl], b, (v4f){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = fmaf(fmaxf(c[i], 0.f), wr[tl][i], s);
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------- prefill
+// Workgroup = 4 waves x QW query rows, one key chunk of `key_chunk` keys.
+// grid.x: query blocks of 4*QW rows; grid.y: key chunks.
+template <int QW, int NT>
+__global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    int64_t T, int64_t N, int32_t H_I, int64_t q_pos0, float* __restrict__ scores, int64_t ld,
+    int32_t key_chunk, int32_t fill_masked) {
+  constexpr int QB = 4 * QW;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][64 * kKeyStride];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.x * QB;
+  if (r0 >= T) return;
+  const int64_t r_last = min(r0 + QB, T) - 1;
+  const int64_t n_comp_all = min(q_pos0 + r_last + 1, N);  // keys past this are masked for every row
+  const int64_t c0 = (int64_t)blockIdx.y * key_chunk;
+  const int64_t c_end = min(c0 + key_chunk, fill_masked ? N : n_comp_all);
+  if (c0 >= c_end) return;
+  const int64_t n_comp = min(c_end, n_comp_all);
+
+  v8i a[QW][NT];
+  float wr[QW][NT][4];
+  int64_t nq[QW];
+#pragma unroll
+  for (int q = 0; q < QW; ++q) {
+    const int64_t r = r0 + wave * QW + q;
+    const bool valid = r < T;
+    nq[q] = valid ? min(q_pos0 + r + 1, N) : 0;
+    load_query<NT>(q_idx, w, r, valid, H_I, col, grp, a[q], wr[q]);
+  }
+
+  // staging: thread tid moves bytes [32*(tid&3), +32) of key (tid>>2) of a group
+  const int st_key = tid >> 2, st_off = 32 * (tid & 3);
+  auto stage_load = [&](int64_t kg, v4i& s0, v4i& s1) {
+    const int64_t s = kg + st_key;
+    if (s < n_comp) {
+      const v4i* p = (const v4i*)(k_idx + s * kIdxD + st_off);
+      s0 = p[0];
+      s1 = p[1];
+    } else {
+      s0 = (v4i){0, 0, 0, 0};
+      s1 = s0;
+    }
+  };
+
+  v4i s0, s1;
+  stage_load(c0, s0, s1);
+  int buf = 0;
+  for (int64_t kg = c0; kg < c_end; kg += 64) {
+    if (kg < n_comp) {
+      v4i* dst = (v4i*)(&kbuf[buf][st_key * kKeyStride + st_off]);
+      dst[0] = s0;
+      dst[1] = s1;
+    }
+    __syncthreads();
+    if (kg + 64 < n_comp) stage_load(kg + 64, s0, s1);
+    const int64_t s = kg + lane;
+    if (kg < n_comp) {
+      float part[QW][4];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const v4i* src = (const v4i*)(&kbuf[buf][(16 * blk + col) * kKeyStride + 32 * grp]);
+        v4i lo = src[0], hi = src[1];
+        v8i b = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int q = 0; q < QW; ++q) part[q][blk] = head_sum<NT>(a[q], wr[q], b);
+      }
+#pragma unroll
+      for (int q = 0; q < QW; ++q) {
+        const float v = group_transpose_reduce(part[q][0], part[q][1], part[q][2], part[q][3], grp);
+        const int64_t r = r0 + wave * QW + q;
+        if (r < T && s < c_end) {
+          if (s < nq[q])
+            scores[r * ld + s] = v;
+          else if (fill_masked)
+            scores[r * ld + s] = -INFINITY;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < QW; ++q) {
+        const int64_t r = r0 + wave * QW + q;
+        if (r < T && s < c_end) scores[r * ld + s] = -INFINITY;
+      }
+    }
+    buf ^= 1;
+  }
+}
+
+// ---------------------------------------------------------------- decode
+// Workgroup = one query (sequence b = grid.y) and one chunk of `key_chunk`
+// keys; the 4 waves take interleaved 64-key groups, loading each key once.
+template <int NT, class Addr>
+__global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __restrict__ q_idx,
+                                                             const float* __restrict__ w,
+                                                             const uint8_t* __restrict__ keys, Addr addr,
+                                                             const int32_t* __restrict__ ctx_len,
+                                                             int64_t max_ctx, int32_t H_I,
+                                                             float* __restrict__ scores, int64_t ld,
+                                                             int32_t key_chunk) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t b = blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * key_chunk;
+  const int64_t c_end = min(c0 + key_chunk, max_ctx);
+  if (c0 >= c_end) return;
+  int64_t n = ctx_len[b];
+  n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
+
+  v8i a[NT];
+  float wr[NT][4];
+  load_query<NT>(q_idx, w, b, true, H_I, col, grp, a, wr);
+
+  for (int64_t kg = c0 + 64 * wave; kg < c_end; kg += 256) {
+    const int64_t s = kg + lane;
+    if (kg >= n) {
+      if (s < c_end) scores[b * ld + s] = -INFINITY;
+      continue;
+    }
+    v8i bf[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int64_t sk = kg + 16 * blk + col;
+      const int64_t row = sk < n ? addr.row(b, sk) : -1;
+      if (row >= 0) {
+        const v4i* p = (const v4i*)(keys + row * kIdxD + 32 * grp);
+        v4i lo = p[0], hi = p[1];
+        bf[blk] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      } else {
+        bf[blk] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+    float part[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) part[blk] = head_sum<NT>(a, wr, bf[blk]);
+    const float v = group_transpose_reduce(part[0], part[1], part[2], part[3], grp);
+    if (s < c_end) {
+      const bool cand = s < n && addr.row(b, s) >= 0;
+      scores[b * ld + s] = cand ? v : -INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+namespace {
+constexpr int kPrefillQW = 2;
+constexpr int kPrefillChunk = 4096;
+constexpr int kDecodeChunk = 1024;
+
+template <int NT>
+hipError_t prefill_nt(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
+                      int32_t H_I, int64_t q_pos0, float* scores, int64_t ld, bool fill, hipStream_t st) {
+  constexpr int QB = 4 * kPrefillQW;
+  const int64_t n_all = fill ? N : std::min<int64_t>(q_pos0 + T, N);
+  dim3 grid((unsigned)((T + QB - 1) / QB), (unsigned)((n_all + kPrefillChunk - 1) / kPrefillChunk));
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((indexer_prefill_kernel<kPrefillQW, NT>), grid, dim3(256), 0, st, q_idx, w, k_idx, T, N,
+                     H_I, q_pos0, scores, ld, kPrefillChunk, fill ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int NT, class Addr>
+hipError_t decode_nt(const uint8_t* q_idx, const float* w, const uint8_t* keys, Addr addr,
+                     const int32_t* ctx_len, int64_t B, int64_t max_ctx, int32_t H_I, float* scores, int64_t ld,
+                     hipStream_t st) {
+  dim3 grid((unsigned)((max_ctx + kDecodeChunk - 1) / kDecodeChunk), (unsigned)B);
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((indexer_decode_kernel<NT, Addr>), grid, dim3(256), 0, st, q_idx, w, keys, addr, ctx_len,
+                     max_ctx, H_I, scores, ld, kDecodeChunk);
+  return hipGetLastError();
+}
+
+template <class Addr>
+hipError_t decode_dispatch(const uint8_t* q_idx, const float* w, const uint8_t* keys, Addr addr,
+                           const int32_t* ctx_len, int64_t B, int64_t max_ctx, int32_t H_I, float* scores,
+                           int64_t ld, hipStream_t st) {
+  const int nt = (H_I + 15) / 16;
+  switch (nt) {
+    case 1: return decode_nt<1>(q_idx, w, keys, addr, ctx_len, B, max_ctx, H_I, scores, ld, st);
+    case 2: return decode_nt<2>(q_idx, w, keys, addr, ctx_len, B, max_ctx, H_I, scores, ld, st);
+    case 3: return decode_nt<3>(q_idx, w, keys, addr, ctx_len, B, max_ctx, H_I, scores, ld, st);
+    default: return decode_nt<4>(q_idx, w, keys, addr, ctx_len, B, max_ctx, H_I, scores, ld, st);
+  }
+}
+}  // namespace
+
+hipError_t launch_indexer_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T,
+                                  int64_t N, int32_t H_I, int64_t q_pos0, float* scores, int64_t ld,
+                                  bool fill_masked, hipStream_t st) {
+  const int nt = (H_I + 15) / 16;
+  switch (nt) {
+    case 1: return prefill_nt<1>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
+    case 2: return prefill_nt<2>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
+    case 3: return prefill_nt<3>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
+    default: return prefill_nt<4>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
+  }
+}
+
+hipError_t launch_indexer_decode(const uint8_t* q_idx, const float* w, const uint8_t* keys, int64_t stride,
+                                 const PagedArgs* paged, const int32_t* ctx_len, int64_t B, int64_t max_ctx,
+                                 int32_t H_I, float* scores, int64_t ld, hipStream_t st) {
+  if (paged) {
+    AddrPaged ad{paged->page_table, paged->max_pages, __builtin_ctz((unsigned)paged->page_size),
+                 paged->n_pages};
+    return decode_dispatch(q_idx, w, keys, ad, ctx_len, B, max_ctx, H_I, scores, ld, st);
+  }
+  AddrBatched ad{stride};
+  return decode_dispatch(q_idx, w, keys, ad, ctx_len, B, max_ctx, H_I, scores, ld, st);
+}
+
+}  // namespace dsa

@@ -1,0 +1,65 @@
+// Internal kernel launchers (host side).  Shapes are validated by the C-ABI
+// layer before any of these is called; each returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct PagedArgs {
+  const int32_t* page_table;
+  int32_t max_pages;
+  int32_t page_size;
+  int64_t n_pages;
+};
+
+// Lightning-indexer scores for T query rows of one sequence (rows at
+// positions q_pos0 + t) over keys 0..N-1.  fill_masked: also write -inf to
+// the non-candidate keys s < N; otherwise only candidates are written.
+hipError_t launch_indexer_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T,
+                                  int64_t N, int32_t H_I, int64_t q_pos0, float* scores, int64_t ld,
+                                  bool fill_masked, hipStream_t st);
+
+// Indexer scores for B decode queries; keys of sequence b are either rows
+// b*stride + s of k_idx (paged == nullptr) or pool rows via the page table.
+// Writes scores[b*ld + s] for s < max_ctx (-inf past ctx_len[b]).
+hipError_t launch_indexer_decode(const uint8_t* q_idx, const float* w, const uint8_t* keys, int64_t stride,
+                                 const PagedArgs* paged, const int32_t* ctx_len, int64_t B, int64_t max_ctx,
+                                 int32_t H_I, float* scores, int64_t ld, hipStream_t st);
+
+// Top-k per row: n_t = min(n_valid ? n_valid[t] : q_pos0 + t + 1, N).
+hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0,
+                       const int32_t* n_valid, int32_t k, int32_t* idx, hipStream_t st);
+
+// Sparse MLA-MQA attention.  Query t reads latent rows of sequence
+// (seq_per_query ? t : 0) through the given addressing: contiguous rows
+// (kv + row*D_qk with row = b*stride + s, s < seq_len) or paged.
+// n_split > 1 splits each query's k entries over n_split workgroups and
+// merges the partials (part_o [T, n_split, H, D_v], part_lse [T, n_split, H]).
+struct MlaArgs {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const int32_t* idx;
+  int64_t T;
+  int32_t H;
+  int32_t k;
+  float scale;
+  float* out;
+  float* lse;
+  // addressing
+  bool seq_per_query;
+  int64_t stride;            // contiguous: row = b*stride + s
+  int64_t seq_len;           // contiguous: valid s < seq_len
+  const int32_t* ctx_len;    // optional per-sequence valid length (decode)
+  const PagedArgs* paged;    // non-null: paged addressing
+  // split-key partials
+  int32_t n_split;
+  float* part_o;
+  float* part_lse;
+};
+hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
+
+// Number of key splits used for T queries of H heads with k entries each.
+int32_t sparse_mla_splits(int64_t T, int32_t H, int32_t k);
+
+}  // namespace dsa

@@ -1,0 +1,275 @@
+// Per-row top-k selection (fine-grained token selection of DeepSeek Sparse
+// Attention, "DeepSeek-V3.2" report walk-through §2.1.2): for each query row
+// keep the k candidates with the largest index scores, ties to the lower
+// position, emitted in ascending position order and padded with -1.
+//
+// One workgroup per row.  Scores become order-preserving uint32 keys and the
+// k-th largest key (theta) is found by radix refinement: a 12-bit histogram
+// over the whole row (global pass 1), then the keys of the threshold bin
+// (~1% of a row) are gathered into LDS (global pass 2) and refined there
+// (12 + 8 more bits) without touching HBM again.  Rows whose threshold bin
+// overflows the LDS list (heavy ties) refine with further global passes.
+// Selection is recorded in two LDS bitmaps over the row: "key > theta" and
+// "key == theta"; one block scan over the bitmaps then gives each selected
+// position its output slot (the lowest-position ties are the first r
+// "== theta" bits), so the output is ascending with no sort.
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kTopkCap = 4096;  // LDS candidate list capacity
+
+struct TopkShared {
+  uint32_t hist[4096];
+  uint32_t list_key[kTopkCap];
+  int32_t list_idx[kTopkCap];
+  uint32_t wave_a[kTopkWaves];
+  uint32_t wave_b[kTopkWaves];
+  uint32_t sel_bin;
+  uint32_t sel_above;
+  uint32_t list_n;
+  uint32_t pad;
+};
+
+// Inclusive block scan of two counters (1024 threads).  Returns inclusive
+// prefixes in *a, *b and the block totals in *ta, *tb.
+__device__ __forceinline__ void block_scan2(TopkShared& sh, uint32_t* a, uint32_t* b, uint32_t* ta,
+                                            uint32_t* tb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = *a, y = *b;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t xs = __shfl_up(x, d, 64), ys = __shfl_up(y, d, 64);
+    if (lane >= d) {
+      x += xs;
+      y += ys;
+    }
+  }
+  if (lane == 63) {
+    sh.wave_a[wave] = x;
+    sh.wave_b[wave] = y;
+  }
+  __syncthreads();
+  uint32_t pa = 0, pb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t wa = sh.wave_a[w], wb = sh.wave_b[w];
+    if (w < wave) {
+      pa += wa;
+      pb += wb;
+    }
+    sa += wa;
+    sb += wb;
+  }
+  __syncthreads();
+  *a = x + pa;
+  *b = y + pb;
+  *ta = sa;
+  *tb = sb;
+}
+
+// Given histogram counts over `nbins` bins (bins are ordered by key), the
+// number `above` of keys greater than every bin and the rank k, find the
+// bin holding the k-th largest key.  Publishes sh.sel_bin and sh.sel_above
+// (= keys greater than that bin).
+__device__ __forceinline__ void find_bin(TopkShared& sh, int nbins, uint32_t above, uint32_t k) {
+  const int tid = threadIdx.x;
+  // thread tid owns bins nbins-1-4*tid .. nbins-4-4*tid (top-down order)
+  uint32_t c = 0;
+  const int top = nbins - 1 - 4 * tid;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (top - i >= 0) c += sh.hist[top - i];
+  uint32_t inc = c, dummy = 0, tot, tot2;
+  block_scan2(sh, &inc, &dummy, &tot, &tot2);
+  uint32_t run = above + inc - c;  // keys in bins above this thread's bins
+  if (top >= 0 && run < k && run + c >= k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bin = top - i;
+      const uint32_t h = sh.hist[bin];
+      if (run < k && run + h >= k) {
+        sh.sel_bin = (uint32_t)bin;
+        sh.sel_above = run;
+        break;
+      }
+      run += h;
+    }
+  }
+  __syncthreads();
+}
+
+// Radix levels: 0 -> key bits 31..20, 1 -> bits 19..8, 2 -> bits 7..0.
+__device__ __forceinline__ int level_shift(int level) { return level == 0 ? 20 : (level == 1 ? 8 : 0); }
+__device__ __forceinline__ int level_bits(int level) { return level == 2 ? 8 : 12; }
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t ld,
+                                                             int64_t T, int64_t N, int64_t q_pos0,
+                                                             const int32_t* __restrict__ n_valid, int32_t k,
+                                                             int32_t* __restrict__ idx, int32_t n_words) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
+  uint32_t* gt_bits = reinterpret_cast<uint32_t*>(smem + sizeof(TopkShared));
+  uint32_t* eq_bits = gt_bits + n_words;
+
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  int64_t n = n_valid ? (int64_t)n_valid[t] : q_pos0 + t + 1;
+  n = n < 0 ? 0 : (n > N ? N : n);
+  int32_t* out = idx + t * (int64_t)k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* row = scores + t * ld;
+
+  // ------------------------------------------------------------ global refinement
+  // Current candidate key range [lo, hi]; `above` keys are > hi.
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu, above = 0u, in_range = (uint32_t)n;
+  int level = 0;  // 0: bits 31..20, 1: bits 19..8, 2: bits 7..0
+  for (; level < 3; ++level) {
+    if (level > 0 && in_range <= (uint32_t)kTopkCap) break;
+    const int sh_ = level_shift(level), nb = 1 << level_bits(level);
+    for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int64_t s = tid; s < n; s += kTopkThreads) {
+      const uint32_t key = order_key(row[s]);
+      if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key >> sh_) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_bin(sh, nb, above, (uint32_t)k);
+    const uint32_t bin = sh.sel_bin;
+    above = sh.sel_above;
+    in_range = sh.hist[bin];
+    const uint32_t span = (sh_ == 0) ? 0u : ((1u << sh_) - 1u);
+    lo = (lo & ~(((uint32_t)(nb - 1)) << sh_)) | (bin << sh_);
+    hi = lo | span;
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------ collect pass
+  for (int i = tid; i < 2 * n_words; i += kTopkThreads) gt_bits[i] = 0;  // gt and eq maps are adjacent
+  if (tid == 0) sh.list_n = 0;
+  __syncthreads();
+  const bool exact = (lo == hi);
+  for (int64_t s = tid; s < n; s += kTopkThreads) {
+    const uint32_t key = order_key(row[s]);
+    if (key > hi) {
+      atomicOr(&gt_bits[s >> 5], 1u << (s & 31));
+    } else if (key >= lo) {
+      if (exact) {
+        atomicOr(&eq_bits[s >> 5], 1u << (s & 31));
+      } else {
+        const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+        sh.list_key[slot] = key;
+        sh.list_idx[slot] = (int32_t)s;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ------------------------------------------------------------ LDS refinement
+  if (!exact) {
+    const int nl = (int)sh.list_n;
+    for (; level < 3; ++level) {
+      const int sh_ = level_shift(level), nb = 1 << level_bits(level);
+      for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < nl; i += kTopkThreads) {
+        const uint32_t key = sh.list_key[i];
+        if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key >> sh_) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      find_bin(sh, nb, above, (uint32_t)k);
+      const uint32_t bin = sh.sel_bin;
+      above = sh.sel_above;
+      const uint32_t span = (sh_ == 0) ? 0u : ((1u << sh_) - 1u);
+      lo = (lo & ~(((uint32_t)(nb - 1)) << sh_)) | (bin << sh_);
+      hi = lo | span;
+      __syncthreads();
+    }
+    // lo == hi == theta: mark list entries
+    for (int i = tid; i < nl; i += kTopkThreads) {
+      const uint32_t key = sh.list_key[i];
+      const int32_t s = sh.list_idx[i];
+      if (key > hi)
+        atomicOr(&gt_bits[s >> 5], 1u << (s & 31));
+      else if (key == hi)
+        atomicOr(&eq_bits[s >> 5], 1u << (s & 31));
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------ ordered emit
+  // Thread tid owns words [wpt*tid, wpt*tid + wpt) i.e. a contiguous range of positions.
+  const int wpt = (n_words + kTopkThreads - 1) / kTopkThreads;
+  const int w0 = tid * wpt;
+  uint32_t cg = 0, ce = 0;
+  for (int i = 0; i < wpt; ++i) {
+    const int wi = w0 + i;
+    if (wi < n_words) {
+      cg += __popc(gt_bits[wi]);
+      ce += __popc(eq_bits[wi]);
+    }
+  }
+  uint32_t ig = cg, ie = ce, tg, te;
+  block_scan2(sh, &ig, &ie, &tg, &te);
+  const uint32_t r = (uint32_t)k - tg;  // ties to take, lowest positions first
+  uint32_t eq_before = ie - ce;
+  uint32_t sel_words[8];
+  uint32_t cs = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int wi = w0 + i;
+    uint32_t g = 0, e = 0;
+    if (i < wpt && wi < n_words) {
+      g = gt_bits[wi];
+      e = eq_bits[wi];
+    }
+    uint32_t keep = 0;
+    while (e && eq_before < r) {
+      const uint32_t lowbit = e & (~e + 1u);
+      keep |= lowbit;
+      e &= e - 1u;
+      ++eq_before;
+    }
+    sel_words[i] = g | keep;
+    cs += __popc(sel_words[i]);
+  }
+  uint32_t is = cs, dummy = 0, ts, td;
+  block_scan2(sh, &is, &dummy, &ts, &td);
+  uint32_t pos = is - cs;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t m = sel_words[i];
+    const int base = (w0 + i) * 32;
+    while (m) {
+      const int b = __ffs(m) - 1;
+      out[pos++] = base + b;
+      m &= m - 1u;
+    }
+  }
+}
+
+hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0,
+                       const int32_t* n_valid, int32_t k, int32_t* idx, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  const int32_t n_words = (int32_t)((N + 31) / 32);
+  const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words;
+  static bool attr_set = false;
+  if (!attr_set) {
+    // rows up to 262144 keys: 48 KiB of fixed state + 64 KiB of bitmaps
+    hipError_t e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, T, N, q_pos0,
+                     n_valid, k, idx, n_words);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

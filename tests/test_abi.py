@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every entry point include/dsa.h declares,
+and rejects bad arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_long_08_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    declared = _declared()
+    assert declared, "no declarations parsed"
+    assert sorted(dsa.SIGNATURES) == declared
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dsa.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = dsa.load()
+    assert lib.dsa_abi_version() == 1
+    for s in range(5):
+        assert lib.dsa_status_string(s)
+    assert lib.dsa_status_string(99) == b"unknown status"
+
+
+FAKE = 0x100000  # an aligned non-null address; validation fails before any use
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    # d_I must be 128
+    ((FAKE, FAKE, FAKE, 4, 8, 4, 64, 0, FAKE, 8, 0), 2, "d_I"),
+    # H_I range
+    ((FAKE, FAKE, FAKE, 4, 8, 65, 128, 0, FAKE, 8, 0), 2, "H_I"),
+    # ld < N
+    ((FAKE, FAKE, FAKE, 4, 8, 4, 128, 0, FAKE, 7, 0), 1, "ld"),
+    # null pointer
+    ((0, FAKE, FAKE, 4, 8, 4, 128, 0, FAKE, 8, 0), 1, "q_idx"),
+    # misaligned pointer
+    ((FAKE + 4, FAKE, FAKE, 4, 8, 4, 128, 0, FAKE, 8, 0), 1, "aligned"),
+])
+def test_indexer_validation(args, status, needle):
+    lib = dsa.load()
+    st = lib.dsa_indexer_scores(*args)
+    assert st == status
+    assert needle in lib.dsa_last_error_message().decode()
+
+
+def test_topk_and_attention_validation():
+    lib = dsa.load()
+    assert lib.dsa_topk(FAKE, 8, 2, 8, 0, 0, 0, FAKE, 0) == 2          # k = 0
+    assert lib.dsa_topk(FAKE, 8, 2, 8, 0, 0, 5000, FAKE, 0) == 2       # k too large
+    assert lib.dsa_topk(FAKE, 300000, 2, 300000, 0, 0, 8, FAKE, 0) == 2  # row longer than supported
+    assert lib.dsa_topk(FAKE, 8, 0, 8, 0, 0, 4, FAKE, 0) == 0          # empty call is a no-op
+    # attention: D_qk / D_v / H / scale / workspace
+    assert lib.dsa_sparse_mla_fwd(FAKE, FAKE, FAKE, 4, 8, 8, 512, 512, 4, 0.1, FAKE, FAKE, 0, 0, 0) == 2
+    assert lib.dsa_sparse_mla_fwd(FAKE, FAKE, FAKE, 4, 8, 8, 576, 256, 4, 0.1, FAKE, FAKE, 0, 0, 0) == 2
+    assert lib.dsa_sparse_mla_fwd(FAKE, FAKE, FAKE, 4, 8, 200, 576, 512, 4, 0.1, FAKE, FAKE, 0, 0, 0) == 2
+    assert lib.dsa_sparse_mla_fwd(FAKE, FAKE, FAKE, 4, 8, 8, 576, 512, 4, -1.0, FAKE, FAKE, 0, 0, 0) == 1
+    need = lib.dsa_sparse_mla_fwd_workspace_bytes(4, 128, 512, 2048)
+    assert need > 0  # few queries: split partials need scratch
+    assert lib.dsa_sparse_mla_fwd(FAKE, FAKE, FAKE, 4, 8, 128, 576, 512, 2048, 0.1, FAKE, FAKE, FAKE, need - 1,
+                                  0) == 3
+    assert lib.dsa_sparse_mla_fwd_workspace_bytes(100000, 128, 512, 2048) == 0
+
+
+def test_fused_validation():
+    lib = dsa.load()
+    need = lib.dsa_forward_prefill_workspace_bytes(1024, 1024, 128, 512, 64)
+    assert need >= 1024 * 1024 * 4
+    st = lib.dsa_forward_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, 1024, 1024, 64, 128, 128, 576, 512, 64, 0, 0.07, 0,
+                                 FAKE, FAKE, FAKE, need - 1, 0)
+    assert st == 3 and "workspace" in lib.dsa_last_error_message().decode()
+    # paged decode: page size and context bound
+    st = lib.dsa_forward_decode_paged(FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 4, FAKE, 32, 2, 100, 64, 128, 128, 576,
+                                      512, 64, 0.07, 0, FAKE, FAKE, FAKE, 1 << 30, 0)
+    assert st == 2 and "page_size" in lib.dsa_last_error_message().decode()
+    st = lib.dsa_forward_decode_paged(FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 4, FAKE, 64, 2, 300, 64, 128, 128, 576,
+                                      512, 64, 0.07, 0, FAKE, FAKE, FAKE, 1 << 30, 0)
+    assert st == 1 and "max_ctx" in lib.dsa_last_error_message().decode()
+
+
+def test_binding_raises():
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.dsa_indexer_scores(FAKE, FAKE, FAKE, 4, 8, 4, 64, 0, FAKE, 8, stream=0)
+    assert e.value.status == 2

@@ -1,0 +1,107 @@
+"""End-to-end GPU parity of the fused calls on the five workloads: tiny exact
+prefill (both k), 64 x 32K contiguous decode, 32K and 128K causal prefill
+(sampled rows) and 32-sequence paged decode with 4K..128K contexts."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import jobs
+from dsa_inputs import configs, device
+from dsa_run import check_attention, check_selection, decode, paged_decode, prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("k", [32, 256])
+def test_tiny_prefill_exact(dsa, k):
+    wl = configs.WORKLOADS["tiny_prefill_L256"].with_k(k)
+    _case(f"forward_prefill tiny L=256 k={k}")
+    inp = device.make_prefill_inputs(wl)
+    idx, out, lse = prefill(wl, inp)
+    g_idx, g_out, g_lse = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    keys = configs.k_idx_bytes(wl, 0, np.arange(wl.N))
+    kv_all = configs.kv_bf16(wl, 0, np.arange(wl.N))
+    for t in range(wl.T):
+        r = oracle.prefill_row(wl, t, keys)
+        check_selection(g_idx[t], r["idx"], r["scores"], k, exact=True)
+        check_attention(g_out[t], g_lse[t], r["out"], r["lse"])
+        if k >= wl.N:  # every candidate selected: equals dense causal attention
+            o_d, l_d = oracle.dense_mla_row(configs.q_bf16(wl, [t])[0], kv_all, t + 1, wl.scale, wl.D_v)
+            check_attention(g_out[t], g_lse[t], o_d, l_d)
+
+
+def _check_rows(name, rows, results, g_idx, g_out, g_lse, k):
+    swapped = 0
+    for i, r in enumerate(results):
+        d = check_selection(g_idx[i], r["idx"], r["scores"], k, exact=False)
+        swapped += d > 0
+        # rows whose selection differs only by near-ties: the outputs still
+        # obey the absolute rules; the relative-RMS rule is for equal sets
+        check_attention(g_out[i], g_lse[i], r["out"], r["lse"], rel_rms=None if d else 1e-2)
+    print(f"[{name}] {len(rows)} rows checked, {swapped} with near-tie swaps", flush=True)
+    assert swapped <= max(2, len(rows) // 20)
+
+
+def test_decode_b64_ctx32k(dsa):
+    wl = configs.WORKLOADS["decode_b64_ctx32k"]
+    _case("forward_decode B=64 N=32768")
+    inp = device.make_decode_inputs(wl)
+    idx, out, lse = decode(wl, inp)
+    g_idx, g_out, g_lse = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    del inp, idx, out, lse
+    _free()
+    rows = list(range(wl.B))
+    results = jobs.run(jobs.decode_job, [(wl.name, b, None) for b in rows])
+    _check_rows(wl.name, rows, results, g_idx, g_out, g_lse, wl.k)
+
+
+def test_paged_decode_b32(dsa):
+    wl = configs.WORKLOADS["paged_decode_b32_ctx4k_128k"]
+    _case("forward_decode_paged B=32 ctx 4K..128K")
+    inp = device.make_paged_inputs(wl)
+    idx, out, lse = paged_decode(wl, inp)
+    g_idx, g_out, g_lse = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    del inp, idx, out, lse
+    _free()
+    rows = list(range(wl.B))
+    results = jobs.run(jobs.decode_job, [(wl.name, b, None) for b in rows])
+    _check_rows(wl.name, rows, results, g_idx, g_out, g_lse, wl.k)
+
+
+def _prefill_sampled(name, rows):
+    wl = configs.WORKLOADS[name]
+    _case(f"forward_prefill {name} T={wl.T}")
+    inp = device.make_prefill_inputs(wl)
+    idx, out, lse = prefill(wl, inp)
+    ridx = torch.from_numpy(np.asarray(rows)).cuda()
+    g_idx = idx[ridx].cpu().numpy()
+    g_out = out[ridx].cpu().numpy()
+    g_lse = lse[ridx].cpu().numpy()
+    del inp, idx, out, lse
+    _free()
+    results = jobs.run(jobs.prefill_job, [(wl.name, int(t), None) for t in rows])
+    _check_rows(name, rows, results, g_idx, g_out, g_lse, wl.k)
+
+
+def test_prefill_32k_sampled(dsa):
+    wl = configs.WORKLOADS["prefill_L32k"]
+    rows = np.unique(np.concatenate([configs.sample_rows(wl, wl.oracle_rows), np.arange(64),
+                                     np.arange(wl.T - 64, wl.T), [2046, 2047, 2048, 2049]]))
+    _prefill_sampled(wl.name, rows)
+
+
+def test_prefill_128k_sampled(dsa):
+    wl = configs.WORKLOADS["prefill_L128k"]
+    rows = np.unique(np.concatenate([configs.sample_rows(wl, wl.oracle_rows), np.arange(8), [2047, 2048],
+                                     [wl.T - 1]]))
+    _prefill_sampled(wl.name, rows)

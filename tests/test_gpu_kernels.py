@@ -1,0 +1,278 @@
+"""Stage-level GPU parity: each C-ABI call against the CPU oracle on seeded
+inputs, covering several tiles, ragged tails and edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_inputs import configs, device, gen
+from dsa_run import check_attention, check_scores, ws_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ generator
+def test_device_generator_matches_host(dsa):
+    for name in ("tiny_prefill_L256", "prefill_L32k"):
+        wl = configs.WORKLOADS[name]
+        _case(f"generator {name}")
+        rows = 40
+        inp = {}
+        q_idx = torch.empty((rows, wl.H_I, wl.d_I), dtype=torch.uint8, device="cuda")
+        w = torch.empty((rows, wl.H_I), dtype=torch.float32, device="cuda")
+        k_idx = torch.empty((rows, wl.d_I), dtype=torch.uint8, device="cuda")
+        q = torch.empty((rows, wl.H, wl.D_qk), dtype=torch.uint16, device="cuda")
+        kv = torch.empty((rows, wl.D_qk), dtype=torch.uint16, device="cuda")
+        device._fill_common(wl, q_idx, w, k_idx, q, kv, rows, rows)
+        torch.cuda.synchronize()
+        r = np.arange(rows)
+        assert np.array_equal(q_idx.cpu().numpy(), configs.q_idx_bytes(wl, r))
+        assert np.array_equal(w.cpu().numpy(), configs.w_f32(wl, r))
+        assert np.array_equal(k_idx.cpu().numpy(), configs.k_idx_bytes(wl, 0, r))
+        assert np.array_equal(q.cpu().numpy().view(np.uint16), configs.q_bf16(wl, r))
+        assert np.array_equal(kv.cpu().numpy().view(np.uint16), configs.kv_bf16(wl, 0, r))
+    # paged pools through a row map
+    wl = configs.WORKLOADS["paged_decode_b32_ctx4k_128k"]
+    _case("generator paged rowmap")
+    rowmap = np.array([5 * wl.S + 7, 3, 2 * wl.S + 70000, 0], dtype=np.int64)
+    kv = torch.empty((4, wl.D_qk), dtype=torch.uint16, device="cuda")
+    device.fill(kv, 4, wl.D_qk, device.BF16_NORMAL, wl.seed, gen.STREAM_KV, div=wl.kv_div,
+                rowmap=torch.from_numpy(rowmap).cuda())
+    torch.cuda.synchronize()
+    ref = np.stack([configs.kv_bf16(wl, int(r // wl.S), [int(r % wl.S)])[0] for r in rowmap])
+    assert np.array_equal(kv.cpu().numpy().view(np.uint16), ref)
+
+
+# ------------------------------------------------------------------ indexer
+def test_indexer_tiny_exact(dsa):
+    wl = configs.WORKLOADS["tiny_prefill_L256"]
+    _case("indexer tiny L=256 exact")
+    inp = device.make_prefill_inputs(wl)
+    T, N = wl.T, wl.N
+    ld = N + 4
+    scores = torch.full((T, ld), 7.0, dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores(inp["q_idx"], inp["w"], inp["k_idx"], T, N, wl.H_I, wl.d_I, 0, scores, ld)
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()
+    keys = configs.k_idx_bytes(wl, 0, np.arange(N))
+    for t in range(T):
+        o = oracle.indexer_row(configs.q_idx_bytes(wl, [t])[0], configs.w_f32(wl, [t])[0], keys[: t + 1])
+        assert np.array_equal(s[t, : t + 1].astype(np.float64), o), f"row {t}"
+        assert np.all(np.isneginf(s[t, t + 1: N])), f"row {t} mask"
+        assert np.all(s[t, N:] == 7.0), "wrote past N"
+
+
+@pytest.mark.parametrize("H_I", [64, 20, 4])
+def test_indexer_offset_rows_multi_chunk(dsa, H_I):
+    base = configs.WORKLOADS["prefill_L32k"]
+    wl = configs.Workload("idx_probe", "prefill", 3, B=1, N=9100, H_I=H_I, H=128, k=2048)
+    wl = configs.Workload(**{**wl.__dict__, "cfg_no": base.cfg_no})
+    q_pos0, T, N = 9000, 37, 9100  # ragged query block, 3 key chunks, causal cap at N
+    _case(f"indexer offset rows H_I={H_I} q_pos0={q_pos0} T={T} N={N}")
+    q_idx = torch.empty((q_pos0 + T, H_I, 128), dtype=torch.uint8, device="cuda")
+    w = torch.empty((q_pos0 + T, H_I), dtype=torch.float32, device="cuda")
+    k_idx = torch.empty((N, 128), dtype=torch.uint8, device="cuda")
+    device.fill(q_idx, q_pos0 + T, H_I * 128, device.E4M3_NORMAL, wl.seed, gen.STREAM_Q_IDX)
+    device.fill(w, q_pos0 + T, H_I, device.F32_UNIFORM, wl.seed, gen.STREAM_W)
+    device.fill(k_idx, N, 128, device.E4M3_NORMAL, wl.seed, gen.STREAM_K_IDX)
+    ld = 9152
+    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores(q_idx[q_pos0:], w[q_pos0:], k_idx, T, N, H_I, 128, q_pos0, scores, ld)
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()
+    keys = configs.k_idx_bytes(wl, 0, np.arange(N))
+    for t in range(T):
+        pos = q_pos0 + t
+        n = min(pos + 1, N)
+        o = oracle.indexer_row(configs.q_idx_bytes(wl, [pos])[0], configs.w_f32(wl, [pos])[0], keys[:n])
+        check_scores(s[t, :n], o)
+        assert np.all(np.isneginf(s[t, n:N]))
+
+
+def test_indexer_paged(dsa):
+    wl = configs.WORKLOADS["paged_decode_b32_ctx4k_128k"]
+    ctx = np.array([1, 63, 64, 65, 3000, 200], dtype=np.int32)
+    B = len(ctx)
+    _case(f"indexer paged ctx={ctx.tolist()}")
+    npg = (ctx + 63) // 64
+    P = int(npg.sum()) + 3  # a few spare pages never referenced
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(P)
+    max_pages = int(npg.max()) + 2
+    pt = np.full((B, max_pages), -1, dtype=np.int32)
+    rowmap = np.zeros(P * 64, dtype=np.int64)
+    f = 0
+    for b in range(B):
+        for lp in range(npg[b]):
+            p = int(perm[f]); f += 1
+            pt[b, lp] = p
+            rowmap[p * 64:(p + 1) * 64] = b * wl.S + lp * 64 + np.arange(64)
+    k_pool = torch.empty((P, 64, 128), dtype=torch.uint8, device="cuda")
+    device.fill(k_pool, P * 64, 128, device.E4M3_NORMAL, wl.seed, gen.STREAM_K_IDX,
+                rowmap=torch.from_numpy(rowmap).cuda())
+    q_idx = torch.empty((B, 64, 128), dtype=torch.uint8, device="cuda")
+    w = torch.empty((B, 64), dtype=torch.float32, device="cuda")
+    device.fill(q_idx, B, 64 * 128, device.E4M3_NORMAL, wl.seed, gen.STREAM_Q_IDX)
+    device.fill(w, B, 64, device.F32_UNIFORM, wl.seed, gen.STREAM_W)
+    max_ctx = 3050
+    ld = 3072
+    scores = torch.empty((B, ld), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores_paged(q_idx, w, k_pool, P, torch.from_numpy(pt).cuda(), max_pages,
+                                 torch.from_numpy(ctx).cuda(), 64, B, 64, 128, max_ctx, scores, ld)
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()
+    for b in range(B):
+        keys = configs.k_idx_bytes(wl, b, np.arange(ctx[b]))
+        o = oracle.indexer_row(configs.q_idx_bytes(wl, [b])[0], configs.w_f32(wl, [b])[0], keys)
+        check_scores(s[b, : ctx[b]], o)
+        assert np.all(np.isneginf(s[b, ctx[b]: max_ctx]))
+
+
+# ------------------------------------------------------------------ top-k
+def _topk_rows():
+    rng = np.random.default_rng(5)
+    rows = []
+    rows.append(("normal", rng.standard_normal(5000)))
+    rows.append(("normal_long", rng.standard_normal(131072) * 30 + 150))
+    rows.append(("int_ties", rng.integers(0, 10, 40000).astype(np.float64)))
+    rows.append(("all_equal", np.full(20000, 3.5)))
+    rows.append(("increasing", np.arange(9000, dtype=np.float64)))
+    rows.append(("decreasing", np.arange(9000, dtype=np.float64)[::-1].copy()))
+    z = rng.integers(0, 2, 6000).astype(np.float64) * 0.0
+    z[rng.random(6000) < 0.5] = -0.0
+    z[rng.random(6000) < 0.01] = 1.0
+    rows.append(("signed_zeros", z))
+    x = rng.standard_normal(7000)
+    x[rng.random(7000) < 0.3] = -np.inf
+    rows.append(("with_neg_inf", x))
+    rows.append(("short", rng.standard_normal(100)))
+    rows.append(("one", np.array([2.0])))
+    rows.append(("quantised_ties", np.round(rng.standard_normal(65536) * 4) / 4))
+    return rows
+
+
+@pytest.mark.parametrize("k", [1, 97, 2048])
+def test_topk_host_rows(dsa, k):
+    rows = _topk_rows()
+    T = len(rows)
+    N = max(len(r) for _, r in rows)
+    ld = (N + 3) // 4 * 4
+    host = np.full((T, ld), np.nan, dtype=np.float32)
+    n_valid = np.zeros(T, dtype=np.int32)
+    for i, (_, r) in enumerate(rows):
+        host[i, : len(r)] = r.astype(np.float32)
+        n_valid[i] = len(r)
+    _case(f"topk host rows k={k} T={T} N={N}")
+    scores = torch.from_numpy(host).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(scores, ld, T, N, 0, torch.from_numpy(n_valid).cuda(), k, idx)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    for i, (name, r) in enumerate(rows):
+        o = oracle.topk_row(r.astype(np.float32).astype(np.float64), k)
+        assert np.array_equal(g[i], o), f"row {name}"
+
+
+def test_topk_causal_rule(dsa):
+    # n_valid = NULL: row t has min(q_pos0 + t + 1, N) candidates
+    rng = np.random.default_rng(8)
+    T, N, k, q_pos0 = 40, 3000, 64, 2980
+    host = rng.standard_normal((T, N)).astype(np.float32)
+    _case("topk causal rule")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(torch.from_numpy(host).cuda(), N, T, N, q_pos0, None, k, idx)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    for t in range(T):
+        n = min(q_pos0 + t + 1, N)
+        assert np.array_equal(g[t], oracle.topk_row(host[t, :n].astype(np.float64), k))
+    # rows with fewer candidates than k
+    idx2 = torch.empty((3, k), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(torch.from_numpy(host[:3]).cuda(), N, 3, N, 0, None, k, idx2)
+    torch.cuda.synchronize()
+    for t in range(3):
+        assert np.array_equal(idx2.cpu().numpy()[t], list(range(t + 1)) + [-1] * (k - t - 1))
+
+
+# ------------------------------------------------------------------ attention
+def _rand_idx(rng, T, k, n):
+    idx = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        m = int(rng.integers(0, min(k, n) + 1)) if t % 5 else min(k, n)
+        idx[t, :m] = np.sort(rng.choice(n, size=m, replace=False))
+    idx[0, :] = -1  # an empty row
+    return idx
+
+
+@pytest.mark.parametrize("T,k,H", [(3, 2048, 128), (40, 300, 128), (300, 64, 128), (17, 100, 8), (9, 70, 40)])
+def test_sparse_mla_against_oracle(dsa, T, k, H):
+    name = "tiny_prefill_L256" if H == 8 else "prefill_L32k"
+    wl0 = configs.WORKLOADS[name]
+    N = 4096
+    wl = configs.Workload(**{**wl0.__dict__, "H": H, "N": N})
+    _case(f"sparse_mla T={T} k={k} H={H} N={N}")
+    rng = np.random.default_rng(T * 1000 + k)
+    q = torch.empty((T, H, 576), dtype=torch.uint16, device="cuda")
+    kv = torch.empty((N, 576), dtype=torch.uint16, device="cuda")
+    device.fill(q, T, H * 576, device.BF16_NORMAL, wl.seed, gen.STREAM_Q)
+    device.fill(kv, N, 576, device.BF16_NORMAL, wl.seed, gen.STREAM_KV, div=wl.kv_div)
+    idx = _rand_idx(rng, T, k, N)
+    idx[1, 0] = N + 5  # out-of-range entries are skipped
+    out = torch.empty((T, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    nb = dsa.dsa_sparse_mla_fwd_workspace_bytes(T, H, 512, k)
+    ws = ws_tensor(nb)
+    dsa.dsa_sparse_mla_fwd(q, kv, torch.from_numpy(idx).cuda(), T, N, H, 576, 512, k, wl.scale, out, lse, ws, nb)
+    torch.cuda.synchronize()
+    g_out, g_lse = out.cpu().numpy(), lse.cpu().numpy()
+    qh = configs.q_bf16(wl, np.arange(T))
+    for t in range(T):
+        sel = idx[t][(idx[t] >= 0) & (idx[t] < N)]
+        o_out, o_lse = oracle.sparse_mla_row(qh[t], configs.kv_bf16(wl, 0, sel), wl.scale, 512)
+        check_attention(g_out[t], g_lse[t], o_out, o_lse)
+
+
+def test_sparse_mla_paged(dsa):
+    wl = configs.WORKLOADS["paged_decode_b32_ctx4k_128k"]
+    ctx = np.array([5, 700, 4096, 2000], dtype=np.int32)
+    B, k, H = len(ctx), 512, 128
+    _case("sparse_mla paged")
+    npg = (ctx + 63) // 64
+    P = int(npg.sum())
+    rng = np.random.default_rng(12)
+    perm = rng.permutation(P)
+    max_pages = int(npg.max())
+    pt = np.full((B, max_pages), -1, dtype=np.int32)
+    rowmap = np.zeros(P * 64, dtype=np.int64)
+    f = 0
+    for b in range(B):
+        for lp in range(npg[b]):
+            p = int(perm[f]); f += 1
+            pt[b, lp] = p
+            rowmap[p * 64:(p + 1) * 64] = b * wl.S + lp * 64 + np.arange(64)
+    kv_pool = torch.empty((P, 64, 576), dtype=torch.uint16, device="cuda")
+    device.fill(kv_pool, P * 64, 576, device.BF16_NORMAL, wl.seed, gen.STREAM_KV, div=wl.kv_div,
+                rowmap=torch.from_numpy(rowmap).cuda())
+    q = torch.empty((B, H, 576), dtype=torch.uint16, device="cuda")
+    device.fill(q, B, H * 576, device.BF16_NORMAL, wl.seed, gen.STREAM_Q)
+    idx = np.full((B, k), -1, dtype=np.int32)
+    for b in range(B):
+        m = min(k, int(ctx[b]))
+        idx[b, :m] = np.sort(rng.choice(int(ctx[b]), size=m, replace=False))
+    idx[1, 3] = int(ctx[1]) + 10  # beyond the context: skipped
+    out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    nb = dsa.dsa_sparse_mla_fwd_paged_workspace_bytes(B, H, 512, k)
+    ws = ws_tensor(nb)
+    dsa.dsa_sparse_mla_fwd_paged(q, kv_pool, P, torch.from_numpy(pt).cuda(), max_pages, torch.from_numpy(ctx).cuda(),
+                                 64, torch.from_numpy(idx).cuda(), B, H, 576, 512, k, wl.scale, out, lse, ws, nb)
+    torch.cuda.synchronize()
+    qh = configs.q_bf16(wl, np.arange(B))
+    for b in range(B):
+        sel = idx[b][(idx[b] >= 0) & (idx[b] < ctx[b])]
+        o_out, o_lse = oracle.sparse_mla_row(qh[b], configs.kv_bf16(wl, b, sel), wl.scale, 512)
+        check_attention(out.cpu().numpy()[b], lse.cpu().numpy()[b], o_out, o_lse)
