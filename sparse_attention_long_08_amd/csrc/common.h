@@ -24,6 +24,25 @@ __device__ __forceinline__ v4f mfma_f8_16x16x128(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// D = A(16x32 bf16) * B(32x16 bf16) + C.  Lane l supplies A row (l % 16) /
+// B column (l % 16), k values 8*(l/16) .. +7.  C/D: lane l holds column
+// l % 16, rows 4*(l/16) + i.  Products are exact and the accumulation is
+// fp32-accurate.
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Widens 8 FP8 E4M3 values (two dwords) to bf16.  Every E4M3 value is
+// exactly representable in bf16, so this is exact.
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v8bf e4m3x8_to_bf16(int lo, int hi) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return (v8bf){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // D = A(32x16 bf16) * B(16x32 bf16) + C.  Lane l supplies A row (l % 32) and
 // B column (l % 32), k values 8*(l/32) .. +7.  C/D: lane l holds column
 // l % 32, rows 8*(r/4) + 4*(l/32) + (r%4) for r = 0..15.

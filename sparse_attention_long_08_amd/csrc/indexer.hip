@@ -1,26 +1,33 @@
-// Lightning indexer on gfx950 FP8 matrix cores.
+// Lightning indexer on gfx950 matrix cores.
 //
 // Computes the index score of DeepSeek-V3.2's lightning indexer ("DeepSeek-
 // V3.2" report walk-through, §2.1.1, index-score equation):
 //   I[t, s] = sum_j w[t, j] * ReLU(q_I[t, j, :] . k_I[s, :])
 // with FP8 E4M3 inputs (few heads, 128-dim keys: analysis article §1.2).
 //
-// Mapping: the head-by-key dot products of one query are a 16x128 by 128x16
-// FP8 MFMA per (16-head tile, 16-key block); heads sit on the MFMA rows so a
-// lane holds 4 heads of one key and the head sum is mostly in-lane.  ReLU and
-// the w-weighting are fused into the accumulator epilogue (fp32), and the
-// remaining sum over the four lane groups is a 4x4 transposing reduction that
-// leaves each lane with one finished score of a 64-key group, so stores are
-// fully coalesced.  Keys are streamed (never the L x L matrix): the prefill
-// kernel stages 64-key groups in LDS and shares them across the workgroup's
-// query rows; the decode kernel streams each key once from HBM.
+// Precision: gfx950's FP8 MFMA keeps only ~14 bits when it sums products
+// (measured: errors up to 1e-4 of sum|products| per instruction), which is
+// far from fp32.  The FP8 operands are therefore widened to bf16 in
+// registers (exact: every E4M3 value is a bf16 value) and contracted on the
+// bf16 MFMA, whose products are exact and whose sums are fp32-accurate.
+//
+// Mapping: the head-by-key dot products of one query are 16x32 by 32x16 bf16
+// MFMAs per (16-head tile, 16-key block), four k-steps for d = 128; heads sit
+// on the MFMA rows so a lane holds 4 heads of one key and the head sum is
+// mostly in-lane.  ReLU and the w-weighting are fused into the accumulator
+// epilogue (fp32), and the remaining sum over the four lane groups is a 4x4
+// transposing reduction that leaves each lane with one finished score of a
+// 64-key group, so stores are fully coalesced.  Keys are streamed (never the
+// L x L matrix): the prefill kernel stages 64-key groups in LDS (widened to
+// bf16 once per workgroup) and shares them across the workgroup's query
+// rows; the decode kernel streams each key once from HBM.
 #include "common.h"
 #include "launch.h"
 
 namespace dsa {
 
-constexpr int kIdxD = 128;      // indexer head dim
-constexpr int kKeyStride = 144;  // LDS row stride of a staged key (bytes), padded against bank conflicts
+constexpr int kIdxD = 128;       // indexer head dim
+constexpr int kKeyStride = 272;  // LDS row stride of a staged bf16 key (bytes), padded against bank conflicts
 
 // On entry lane (g, c) = (lane/16, lane%16) holds its partial for key
 // 16*b + c of a 64-key group in p[b]; returns the sum over all four lane
@@ -36,19 +43,36 @@ __device__ __forceinline__ float group_transpose_reduce(float p0, float p1, floa
   return (odd ? a1 : a0) + z;
 }
 
+// A lane's 32 FP8 values (dims 32*g .. 32*g+31 of one vector) as the four
+// bf16 k-steps of the MFMA: step s covers dims 32*g + 8*s .. +7.  A and B
+// use the same dim <-> (lane group, step, slot) map, so the contraction
+// covers all 128 dims.
+struct Frag {
+  v8bf s[4];
+};
+
+__device__ __forceinline__ Frag widen32(v4i lo, v4i hi) {
+  Frag f;
+  f.s[0] = e4m3x8_to_bf16(lo.x, lo.y);
+  f.s[1] = e4m3x8_to_bf16(lo.z, lo.w);
+  f.s[2] = e4m3x8_to_bf16(hi.x, hi.y);
+  f.s[3] = e4m3x8_to_bf16(hi.z, hi.w);
+  return f;
+}
+
 template <int NT>
 __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
-                                           int64_t r, bool valid, int32_t H_I, int col, int grp, v8i (&a)[NT],
+                                           int64_t r, bool valid, int32_t H_I, int col, int grp, Frag (&a)[NT],
                                            float (&wr)[NT][4]) {
 #pragma unroll
   for (int tl = 0; tl < NT; ++tl) {
     const int head = 16 * tl + col;
     if (valid && head < H_I) {
       const v4i* p = (const v4i*)(q_idx + ((r * H_I + head) * kIdxD + 32 * grp));
-      v4i lo = p[0], hi = p[1];
-      a[tl] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      a[tl] = widen32(p[0], p[1]);
     } else {
-      a[tl] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) a[tl].s[st] = (v8bf){};
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -60,11 +84,13 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx, co
 
 // Weighted, rectified head sum of one query against one 16-key block.
 template <int NT>
-__device__ __forceinline__ float head_sum(const v8i (&a)[NT], const float (&wr)[NT][4], v8i b) {
+__device__ __forceinline__ float head_sum(const Frag (&a)[NT], const float (&wr)[NT][4], const Frag& b) {
   float s = 0.f;
 #pragma unroll
   for (int tl = 0; tl < NT; ++tl) {
-    v4f c = mfma_f8_16x16x128(a[tl], b, (v4f){0.f, 0.f, 0.f, 0.f});
+    v4f c = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) c = mfma_bf16_16x16x32(a[tl].s[st], b.s[st], c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s = fmaf(fmaxf(c[i], 0.f), wr[tl][i], s);
   }
@@ -72,14 +98,16 @@ __device__ __forceinline__ float head_sum(const v8i (&a)[NT], const float (&wr)[
 }
 
 // ---------------------------------------------------------------- prefill
-// Workgroup = 4 waves x QW query rows, one key chunk of `key_chunk` keys.
-// grid.x: query blocks of 4*QW rows; grid.y: key chunks.
-template <int QW, int NT>
-__global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
+// Workgroup = NW waves x QW query rows, one key chunk of `key_chunk` keys.
+// grid.x: query blocks of NW*QW rows; grid.y: key chunks.
+template <int NW, int QW, int NT>
+__global__ __launch_bounds__(64 * NW, 1) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     int64_t T, int64_t N, int32_t H_I, int64_t q_pos0, float* __restrict__ scores, int64_t ld,
     int32_t key_chunk, int32_t fill_masked) {
-  constexpr int QB = 4 * QW;
+  constexpr int QB = NW * QW;
+  constexpr int kStageBytes = 64 * kIdxD / (64 * NW);  // FP8 bytes each thread stages per group
+  static_assert(kStageBytes == 16 || kStageBytes == 32, "staging covers a 64-key group");
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][64 * kKeyStride];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -92,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   if (c0 >= c_end) return;
   const int64_t n_comp = min(c_end, n_comp_all);
 
-  v8i a[QW][NT];
+  Frag a[QW][NT];
   float wr[QW][NT][4];
   int64_t nq[QW];
 #pragma unroll
@@ -103,17 +131,27 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     load_query<NT>(q_idx, w, r, valid, H_I, col, grp, a[q], wr[q]);
   }
 
-  // staging: thread tid moves bytes [32*(tid&3), +32) of key (tid>>2) of a group
-  const int st_key = tid >> 2, st_off = 32 * (tid & 3);
+  // staging: thread tid moves FP8 bytes [kStageBytes*(tid%per_key), +kStageBytes)
+  // of key tid/per_key of a 64-key group and stores them widened to bf16
+  constexpr int per_key = kIdxD / kStageBytes;
+  const int st_key = tid / per_key, st_off = kStageBytes * (tid % per_key);
   auto stage_load = [&](int64_t kg, v4i& s0, v4i& s1) {
     const int64_t s = kg + st_key;
+    s0 = (v4i){0, 0, 0, 0};
+    s1 = s0;
     if (s < n_comp) {
       const v4i* p = (const v4i*)(k_idx + s * kIdxD + st_off);
       s0 = p[0];
-      s1 = p[1];
-    } else {
-      s0 = (v4i){0, 0, 0, 0};
-      s1 = s0;
+      if (kStageBytes == 32) s1 = p[1];
+    }
+  };
+  auto stage_store = [&](int bufi, v4i s0, v4i s1) {
+    v8bf* dst = (v8bf*)(&kbuf[bufi][st_key * kKeyStride + 2 * st_off]);
+    dst[0] = e4m3x8_to_bf16(s0.x, s0.y);
+    dst[1] = e4m3x8_to_bf16(s0.z, s0.w);
+    if (kStageBytes == 32) {
+      dst[2] = e4m3x8_to_bf16(s1.x, s1.y);
+      dst[3] = e4m3x8_to_bf16(s1.z, s1.w);
     }
   };
 
@@ -121,11 +159,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   stage_load(c0, s0, s1);
   int buf = 0;
   for (int64_t kg = c0; kg < c_end; kg += 64) {
-    if (kg < n_comp) {
-      v4i* dst = (v4i*)(&kbuf[buf][st_key * kKeyStride + st_off]);
-      dst[0] = s0;
-      dst[1] = s1;
-    }
+    if (kg < n_comp) stage_store(buf, s0, s1);
     __syncthreads();
     if (kg + 64 < n_comp) stage_load(kg + 64, s0, s1);
     const int64_t s = kg + lane;
@@ -133,9 +167,10 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
       float part[QW][4];
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const v4i* src = (const v4i*)(&kbuf[buf][(16 * blk + col) * kKeyStride + 32 * grp]);
-        v4i lo = src[0], hi = src[1];
-        v8i b = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const v8bf* src = (const v8bf*)(&kbuf[buf][(16 * blk + col) * kKeyStride + 64 * grp]);
+        Frag b;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) b.s[st] = src[st];
 #pragma unroll
         for (int q = 0; q < QW; ++q) part[q][blk] = head_sum<NT>(a[q], wr[q], b);
       }
@@ -181,7 +216,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
   int64_t n = ctx_len[b];
   n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
 
-  v8i a[NT];
+  Frag a[NT];
   float wr[NT][4];
   load_query<NT>(q_idx, w, b, true, H_I, col, grp, a, wr);
 
@@ -191,22 +226,23 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
       if (s < c_end) scores[b * ld + s] = -INFINITY;
       continue;
     }
-    v8i bf[4];
+    v4i raw[4][2];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const int64_t sk = kg + 16 * blk + col;
       const int64_t row = sk < n ? addr.row(b, sk) : -1;
       if (row >= 0) {
         const v4i* p = (const v4i*)(keys + row * kIdxD + 32 * grp);
-        v4i lo = p[0], hi = p[1];
-        bf[blk] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        raw[blk][0] = p[0];
+        raw[blk][1] = p[1];
       } else {
-        bf[blk] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+        raw[blk][0] = (v4i){0, 0, 0, 0};
+        raw[blk][1] = raw[blk][0];
       }
     }
     float part[4];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) part[blk] = head_sum<NT>(a, wr, bf[blk]);
+    for (int blk = 0; blk < 4; ++blk) part[blk] = head_sum<NT>(a, wr, widen32(raw[blk][0], raw[blk][1]));
     const float v = group_transpose_reduce(part[0], part[1], part[2], part[3], grp);
     if (s < c_end) {
       const bool cand = s < n && addr.row(b, s) >= 0;
@@ -217,18 +253,19 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
 
 // ---------------------------------------------------------------- launchers
 namespace {
-constexpr int kPrefillQW = 2;
+constexpr int kPrefillNW = 8;
+constexpr int kPrefillQW = 1;
 constexpr int kPrefillChunk = 4096;
 constexpr int kDecodeChunk = 1024;
 
 template <int NT>
 hipError_t prefill_nt(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
                       int32_t H_I, int64_t q_pos0, float* scores, int64_t ld, bool fill, hipStream_t st) {
-  constexpr int QB = 4 * kPrefillQW;
+  constexpr int QB = kPrefillNW * kPrefillQW;
   const int64_t n_all = fill ? N : std::min<int64_t>(q_pos0 + T, N);
   dim3 grid((unsigned)((T + QB - 1) / QB), (unsigned)((n_all + kPrefillChunk - 1) / kPrefillChunk));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((indexer_prefill_kernel<kPrefillQW, NT>), grid, dim3(256), 0, st, q_idx, w, k_idx, T, N,
+  hipLaunchKernelGGL((indexer_prefill_kernel<kPrefillNW, kPrefillQW, NT>), grid, dim3(64 * kPrefillNW), 0, st, q_idx, w, k_idx, T, N,
                      H_I, q_pos0, scores, ld, kPrefillChunk, fill ? 1 : 0);
   return hipGetLastError();
 }

@@ -8,22 +8,24 @@
 //   out[t,h] = sum_s softmax(z)_s * kv[s,:512],  lse[t,h] = ln sum_s exp(z_s)
 //
 // Mapping: one workgroup (4 waves) owns one query and all its heads; wave w
-// owns heads 32w..32w+31 and keeps their query rows in VGPRs (as the MFMA B
-// operand) and their fp32 output accumulators (512 x 32 per wave) in
-// registers.  Selected latent rows are gathered 32 at a time into LDS (double
-// buffered, next block prefetched into registers while the current one is
-// consumed) in two layouts: row-major (swizzled 16-byte chunks) for the
-// logits S^T = K Q^T, and transposed for the value product O^T = V^T P^T.
-// Writing the logits transposed (keys on MFMA rows, heads on columns) makes
-// each lane own a single head: the softmax statistics are per-lane scalars,
-// the fp32 probabilities feed the value MFMA's B operand straight from the
-// logit accumulator layout (only a key permutation, mirrored in the V^T
-// reads), and the output rescale is one multiply per accumulator.  The
-// running max is only moved when it grows by more than 2^8 (exact: the
-// final normalisation uses the same max), so rescales are rare.
+// owns heads 32w..32w+31, keeps their query rows in VGPRs (the MFMA B operand
+// of the logit product) and their fp32 output accumulators (512 x 32) in
+// accumulation registers.  Selected latent rows are gathered 32 at a time
+// straight from HBM into LDS with the gfx950 global->LDS DMA (16 bytes per
+// lane, no staging registers), double buffered so the next block streams in
+// while the current one is consumed.  The LDS copy is row-major in 16-byte
+// chunks with an XOR swizzle; the logits S^T = K Q^T read it as rows, and
+// the value product O^T = V^T P^T reads the same bytes transposed with
+// ds_read_b64_tr_b16, so one copy serves both.  Putting keys on the MFMA
+// rows makes each lane own a single head: softmax statistics are per-lane
+// scalars, the probabilities feed the value MFMA's B operand directly from
+// the logit accumulator layout (a key permutation mirrored in the transposed
+// V reads), and a rescale is one multiply per accumulator.  The running max
+// only moves when it grows by more than 2^8 (exact: the final normalisation
+// uses the same max), so rescales are rare.
 // Small batches (decode) split each query's k entries over several
-// workgroups; partial (out, lse) pairs are merged exactly by
-// combine_kernel: lse = ln sum_i e^{lse_i}, out = sum_i e^{lse_i - lse} out_i.
+// workgroups; partial (out, lse) pairs are merged exactly by combine_kernel:
+// lse = ln sum_i e^{lse_i}, out = sum_i e^{lse_i - lse} out_i.
 #include "common.h"
 #include "launch.h"
 
@@ -31,21 +33,26 @@ namespace dsa {
 
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
-constexpr int kBlk = 32;                  // selected rows per block
-constexpr int kChunks = kDqk / 8;         // 16-byte chunks per latent row (72)
-constexpr int kVtStride = 36;             // V^T row stride in bf16 (32 keys + 4 pad)
-constexpr int kKBytes = kBlk * kDqk * 2;  // 36864
-constexpr int kVtBytes = kDv * kVtStride * 2;  // 36864
-constexpr int kBufBytes = kKBytes + kVtBytes + 128;
-constexpr int kMlaLds = kBufBytes;
-constexpr int kUnits = kChunks * (kBlk / 4);  // (chunk, row-quad) staging units per block: 576
+constexpr int kBlk = 32;                     // selected rows per block
+constexpr int kChunks = kDqk / 8;            // 16-byte chunks per latent row (72)
+constexpr int kBufBytes = kBlk * kDqk * 2;   // 36864 bytes per buffer
+constexpr int kHeadsPerWave = 16;               // 8 waves x 16 heads
 
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v8f __attribute__((ext_vector_type(8)));
+typedef short v8s_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) uint8_t* lds_u8_ptr;
 
-// 16-byte chunk slot of (row r, chunk c) in the K layout; XOR swizzle keeps
-// both the row-quad staging writes and the MFMA operand reads conflict-free.
+// 16-byte chunk slot of (row r, chunk c); the XOR swizzle spreads the eight
+// rows read together by an MFMA operand load over all LDS banks.
 __device__ __forceinline__ int kslot(int r, int c) { return r * kChunks + (c ^ ((r ^ (r >> 2)) & 7)); }
+__device__ __forceinline__ void kslot_inv(int slot, int& r, int& c) {
+  r = slot / kChunks;
+  c = (slot - r * kChunks) ^ ((r ^ (r >> 2)) & 7);
+}
 
 struct MlaParams {
   const uint16_t* q;
@@ -67,10 +74,11 @@ struct MlaParams {
 };
 
 template <class Addr>
-__global__ __launch_bounds__(256, 1) void sparse_mla_kernel(MlaParams p, Addr addr) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+__global__ __launch_bounds__(512, 1) void sparse_mla_kernel(MlaParams p, Addr addr) {
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kBufBytes];
+  __shared__ v8bf qtail[4 * 8 * 64];  // 32 KiB: query steps 14..17 of all waves
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, hl = lane & 31;
+  const int g4 = lane >> 4, hl = lane & 15;
   const int64_t t = blockIdx.x / p.n_split;
   const int sp = blockIdx.x % p.n_split;
   const int j0 = sp * p.per_split;
@@ -78,113 +86,146 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(MlaParams p, Addr ad
   const int64_t b = p.seq_per_query ? t : 0;
   int64_t n_b = p.ctx_len ? (int64_t)p.ctx_len[b] : p.seq_len;
   if (n_b > p.seq_len) n_b = p.seq_len;
-  const int head = 32 * wave + hl;
-  const bool active = 32 * wave < p.H;
+  const int head = kHeadsPerWave * wave + hl;
+  const bool active = kHeadsPerWave * wave < p.H;
   const int32_t* idx_row = p.idx + t * (int64_t)p.k;
 
-  // ---- query rows of this wave's heads (MFMA B operand of the logit product)
-  v8bf qf[36];
+  // ---- query rows of this wave's 16 heads: B operand of the logit MFMA,
+  // step st covers dims 32*st + 8*g4 .. +7.  Steps 0..13 stay in VGPRs; steps
+  // 14..17 (dims 448..575) are parked in LDS in the same lane order and read
+  // back per block.  Lanes past the last head read head H-1 and zero it.
+  constexpr int kQReg = 14;
+  v8bf qf[kQReg];
+  {
+    const bool hv = head < p.H;
+    const uint16_t* qrow = p.q + (t * p.H + (hv ? head : p.H - 1)) * (int64_t)kDqk + 8 * g4;
 #pragma unroll
-  for (int st = 0; st < 36; ++st) {
-    if (head < p.H) {
-      qf[st] = *(const v8bf*)(p.q + ((t * p.H + head) * (int64_t)kDqk + 16 * st + 8 * g));
-    } else {
-      qf[st] = (v8bf){};
+    for (int st = 0; st < kQReg; ++st) {
+      const v8bf v = *(const v8bf*)(qrow + 32 * st);
+      qf[st] = hv ? v : (v8bf){};
+    }
+#pragma unroll
+    for (int st = kQReg; st < 18; ++st) {
+      const v8bf v = *(const v8bf*)(qrow + 32 * st);
+      qtail[((st - kQReg) * 8 + wave) * 64 + lane] = hv ? v : (v8bf){};
     }
   }
 
-  // ---- staging: unit u = c*8 + qd moves chunk c of rows 4qd..4qd+3
-  v4i stg[3][4];
-  int32_t stg_ok[3];
-  auto stage_load = [&](int jb) {
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int u = tid + 256 * i;
-      stg_ok[i] = 0;
-      if (u < kUnits) {
-        const int c = u >> 3, qd = u & 7;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int j = jb + 4 * qd + rr;
-          int64_t row = -1;
-          if (j < j1) {
-            const int32_t s = idx_row[j];
-            if (s >= 0 && s < n_b) row = addr.row(b, s);
-          }
-          if (row >= 0) {
-            stg[i][rr] = *(const v4i*)(p.kv + row * kDqk + 8 * c);
-            stg_ok[i] |= 1 << rr;
-          } else {
-            stg[i][rr] = (v4i){0, 0, 0, 0};
-          }
-        }
-      }
+  // Row of entry j of this query (-1: skipped).  Lanes 0..31 of every wave
+  // resolve the 32 entries of a block; the DMA lanes pick them up by shuffle.
+  auto resolve = [&](int jb) -> int32_t {
+    const int j = jb + (lane & 31);
+    int32_t row = -1;
+    if (j < j1) {
+      const int32_t s = idx_row[j];
+      if (s >= 0 && s < n_b) row = (int32_t)addr.row(b, s);
     }
+    return row;
   };
-  auto stage_store = [&](int buf) {
-    uint8_t* base = smem + buf * kBufBytes;
-    uint16_t* vt = (uint16_t*)(base + kKBytes);
-    int32_t* valid = (int32_t*)(base + kKBytes + kVtBytes);
+  // Gather the 32 rows of a block into LDS buffer `bi`: 36 DMA instructions
+  // of 64 x 16 bytes, spread over the 8 waves.  Skipped entries read row 0
+  // (their logits are masked, so the bytes only have to be finite).
+  auto gather = [&](int bi, int32_t my_row) {
+    uint8_t* base = kbuf[bi];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int u = tid + 256 * i;
-      if (u < kUnits) {
-        const int c = u >> 3, qd = u & 7;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) ((v4i*)base)[kslot(4 * qd + rr, c)] = stg[i][rr];
-        if (c < kDv / 8) {
-          // transpose 4 rows x 8 columns: column e -> 4 keys at V^T[8c + e][4qd .. 4qd+3]
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            // dword e2 of each row holds columns 2*e2 (low half) and 2*e2+1 (high half)
-            const uint32_t r0 = (uint32_t)stg[i][0][e2], r1 = (uint32_t)stg[i][1][e2];
-            const uint32_t r2 = (uint32_t)stg[i][2][e2], r3 = (uint32_t)stg[i][3][e2];
-            v2i lo, hi;
-            lo.x = (int)__builtin_amdgcn_perm(r1, r0, 0x05040100u);  // (r0.lo, r1.lo)
-            lo.y = (int)__builtin_amdgcn_perm(r3, r2, 0x05040100u);
-            hi.x = (int)__builtin_amdgcn_perm(r1, r0, 0x07060302u);  // (r0.hi, r1.hi)
-            hi.y = (int)__builtin_amdgcn_perm(r3, r2, 0x07060302u);
-            *(v2i*)(vt + (8 * c + 2 * e2) * kVtStride + 4 * qd) = lo;
-            *(v2i*)(vt + (8 * c + 2 * e2 + 1) * kVtStride + 4 * qd) = hi;
-          }
-        }
-        if (c == 0) {
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) valid[4 * qd + rr] = (stg_ok[i] >> rr) & 1;
-        }
+    for (int i = 0; i < 5; ++i) {
+      const int ins = wave + 8 * i;
+      if (ins < kBlk * kChunks / 64) {
+        const int slot0 = 64 * ins;
+        int r, c;
+        kslot_inv(slot0 + lane, r, c);
+        int32_t row = __shfl(my_row, r, 64);
+        row = row < 0 ? 0 : row;
+        const uint16_t* src = p.kv + ((uint64_t)(uint32_t)row * kDqk + 8 * c);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(base + slot0 * 16), 16, 0, 0);
       }
     }
   };
 
-  v16f o[16];
+  // ---- per-lane LDS byte offsets of the operand reads (everything else is
+  // a compile-time immediate).  Logits: M-tile mt reads key 16*mt + hl, chunk
+  // 4*st + g4 = 8*(st/2) + (4*(st%2) + g4).
+  uint32_t s_addr[2][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = (v16f){};
+  for (int mt = 0; mt < 2; ++mt) {
+    const int r = 16 * mt + hl;
+    const int f = (r ^ (r >> 2)) & 7;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) s_addr[mt][par] = (uint32_t)(r * kChunks + ((4 * par + g4) ^ f)) * 16u;
+  }
+  // Values: for c'-tile ct, lane (g4, 4*rq + qq) supplies columns 16*ct + 4*qq ..
+  // of key rows 4*g4 + rq (k-slots 0..3) and 16 + 4*g4 + rq (k-slots 4..7);
+  // chunk 2*ct + qq/2 = 8*(ct/4) + (2*(ct%4) + qq/2), byte 8*(qq%2) within it.
+  uint32_t v_addr[2][4];
+  {
+    const int rq = hl >> 2, qq = hl & 3;
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+      const int r = 16 * hv + 4 * g4 + rq;
+      const int f = (r ^ (r >> 2)) & 7;
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4)
+        v_addr[hv][m4] = (uint32_t)(r * kChunks + ((2 * m4 + (qq >> 1)) ^ f)) * 16u + 8u * (qq & 1);
+    }
+  }
+
+  v4f o[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) o[i] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // pipeline state: rows of the next block, valid masks of the current and next
+  int32_t row_next = -1;
+  uint64_t valid_cur = 0, valid_next = 0;
+  if (j0 < j1) {
+    const int32_t r0 = resolve(j0);
+    valid_cur = __ballot(r0 >= 0) & 0xFFFFFFFFull;
+    gather(0, r0);
+    if (j0 + kBlk < j1) {
+      row_next = resolve(j0 + kBlk);
+      valid_next = __ballot(row_next >= 0) & 0xFFFFFFFFull;
+    }
+  }
+
+  int buf = 0;
   for (int jb = j0; jb < j1; jb += kBlk) {
-    stage_load(jb);
-    stage_store(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (jb + kBlk < j1) gather(buf ^ 1, row_next);
+    const uint64_t valid = valid_cur;
+    valid_cur = valid_next;
+    if (jb + 2 * kBlk < j1) {
+      row_next = resolve(jb + 2 * kBlk);
+      valid_next = __ballot(row_next >= 0) & 0xFFFFFFFFull;
+    }
     if (active) {
-      const uint8_t* base = smem;
-      const uint16_t* vt = (const uint16_t*)(base + kKBytes);
-      const int32_t* valid = (const int32_t*)(base + kKBytes + kVtBytes);
-      // logits S^T[key, head] over the 576 latent dims
-      v16f sacc = (v16f){};
+      const lds_u8_ptr base = (lds_u8_ptr)kbuf[buf];
+      // logits S^T[key, head]: two 16-key M-tiles x 18 k-steps
+      v4f sacc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int st = 0; st < 36; ++st) {
-        const v8bf a = ((const v8bf*)base)[kslot(hl, 2 * st + g)];
-        sacc = mfma_bf16_32x32x16(a, qf[st], sacc);
+      for (int st = 0; st < 18; ++st) {
+        const v8bf qb = st < kQReg ? qf[st < kQReg ? st : 0] : qtail[((st - kQReg) * 8 + wave) * 64 + lane];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const v8bf a =
+              *(const __attribute__((address_space(3))) v8bf*)(base + s_addr[mt][st & 1] + 128 * (st >> 1));
+          sacc[mt] = mfma_bf16_16x16x32(a, qb, sacc[mt]);
+        }
+        if ((st % 6) == 5) __builtin_amdgcn_sched_barrier(0);
       }
-      // lane: head hl; register i: key 8*(i/4) + 4*g + (i%4) of the block
-      float z[16];
+      // lane: head hl; sacc[mt][i] is key 16*mt + 4*g4 + i of the block;
+      // scaled to log2 units in place, masked keys at -inf
       float mloc = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 8 * (i >> 2) + 4 * g + (i & 3);
-        z[i] = valid[key] ? sacc[i] * p.scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, z[i]);
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * mt + 4 * g4 + i;
+          sacc[mt][i] = ((valid >> key) & 1) ? sacc[mt][i] * p.scale_log2 : -INFINITY;
+          mloc = fmaxf(mloc, sacc[mt][i]);
+        }
       }
+      mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
       mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
       const bool need = mloc > m_run + 8.0f;
       if (__any(need)) {
@@ -193,41 +234,39 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(MlaParams p, Addr ad
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
-        for (int ti = 0; ti < 16; ++ti) o[ti] *= alpha;
+        for (int ct = 0; ct < 32; ++ct) o[ct] *= alpha;
       }
-      v8f pf0, pf1;
+      v8f pf;
       float lsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = (m_run == -INFINITY) ? 0.f : exp2f(z[i] - m_run);
+      for (int i = 0; i < 8; ++i) {
+        const float pv = (m_run == -INFINITY) ? 0.f : exp2f(sacc[i >> 2][i & 3] - m_run);
         lsum += pv;
-        if (i < 8)
-          pf0[i] = pv;
-        else
-          pf1[i - 8] = pv;
+        pf[i] = pv;
       }
       l_run += lsum;
-      const v8bf pb0 = __builtin_convertvector(pf0, v8bf);
-      const v8bf pb1 = __builtin_convertvector(pf1, v8bf);
-      // O^T[c', head] += V^T[c', keys] P^T[keys, head]
+      // B operand of the value MFMA: k-slot 8*g4 + j <-> key 4*g4 + j (j < 4),
+      // 16 + 4*g4 + (j - 4) (j >= 4): exactly this lane's probabilities
+      const v8bf pb = __builtin_convertvector(pf, v8bf);
+      // O^T[c', head] += V^T[c', keys] P^T[keys, head], 32 c'-tiles of 16
 #pragma unroll
-      for (int ti = 0; ti < 16; ++ti) {
-        const uint16_t* vrow = vt + (32 * ti + hl) * kVtStride;
-        const v4bf a0 = *(const v4bf*)(vrow + 4 * g);
-        const v4bf a1 = *(const v4bf*)(vrow + 8 + 4 * g);
-        const v4bf a2 = *(const v4bf*)(vrow + 16 + 4 * g);
-        const v4bf a3 = *(const v4bf*)(vrow + 24 + 4 * g);
-        const v8bf va = (v8bf){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        const v8bf vb = (v8bf){a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
-        o[ti] = mfma_bf16_32x32x16(va, pb0, o[ti]);
-        o[ti] = mfma_bf16_32x32x16(vb, pb1, o[ti]);
+      for (int ct = 0; ct < 32; ++ct) {
+        const v4s lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + v_addr[0][ct & 3] + 128 * (ct >> 2)));
+        const v4s hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + v_addr[1][ct & 3] + 128 * (ct >> 2)));
+        const v8bf va = __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        o[ct] = mfma_bf16_16x16x32(va, pb, o[ct]);
+        // bound how far the scheduler hoists operand reads (register budget)
+        if ((ct & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();
+    buf ^= 1;
   }
 
   if (!active || head >= p.H) return;
-  const float l_tot = l_run + shfl_xor_f(l_run, 32);
+  float l_tot = l_run + shfl_xor_f(l_run, 16);
+  l_tot += shfl_xor_f(l_tot, 32);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   const float lse_v = empty ? -INFINITY : (m_run + log2f(l_tot)) * 0.69314718055994530942f;
@@ -240,15 +279,10 @@ __global__ __launch_bounds__(256, 1) void sparse_mla_kernel(MlaParams p, Addr ad
     orow = p.part_o + ((t * p.n_split + sp) * p.H + head) * (int64_t)kDv;
     lrow = p.part_lse + (t * p.n_split + sp) * p.H + head;
   }
+  // O^T layout: lane (g4, head hl) holds c' = 16*ct + 4*g4 + i
 #pragma unroll
-  for (int ti = 0; ti < 16; ++ti) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      v4f v = {o[ti][4 * q4] * inv, o[ti][4 * q4 + 1] * inv, o[ti][4 * q4 + 2] * inv, o[ti][4 * q4 + 3] * inv};
-      *(v4f*)(orow + 32 * ti + 8 * q4 + 4 * g) = v;
-    }
-  }
-  if (g == 0) *lrow = lse_v;
+  for (int ct = 0; ct < 32; ++ct) *(v4f*)(orow + 16 * ct + 4 * g4) = o[ct] * inv;
+  if (g4 == 0) *lrow = lse_v;
 }
 
 // Exact merge of split partials; one workgroup of 128 threads per (t, head).
@@ -292,15 +326,8 @@ int32_t sparse_mla_splits(int64_t T, int32_t /*H*/, int32_t k) {
 namespace {
 template <class Addr>
 hipError_t launch_mla(const MlaParams& p, Addr addr, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel<Addr>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMlaLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const int64_t blocks = p.T * p.n_split;
-  hipLaunchKernelGGL((sparse_mla_kernel<Addr>), dim3((unsigned)blocks), dim3(256), kMlaLds, st, p, addr);
+  hipLaunchKernelGGL((sparse_mla_kernel<Addr>), dim3((unsigned)blocks), dim3(512), 0, st, p, addr);
   return hipGetLastError();
 }
 }  // namespace
