@@ -77,12 +77,15 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx, co
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hw = 16 * tl + 4 * grp + i;
-      wr[tl][i] = (valid && hw < H_I) ? w[r * H_I + hw] : 0.f;
+      wr[tl][i] = (valid && hw < H_I) ? 0.5f * w[r * H_I + hw] : 0.f;
     }
   }
 }
 
 // Weighted, rectified head sum of one query against one 16-key block.
+// wr holds w/2: w * ReLU(c) = (|c| + c) * (w/2) exactly (the doubling and the
+// halving are exact), which is one add with an abs source modifier plus one
+// FMA -- fmaxf would cost an extra canonicalisation per element.
 template <int NT>
 __device__ __forceinline__ float head_sum(const Frag (&a)[NT], const float (&wr)[NT][4], const Frag& b) {
   float s = 0.f;
@@ -92,7 +95,7 @@ __device__ __forceinline__ float head_sum(const Frag (&a)[NT], const float (&wr)
 #pragma unroll
     for (int st = 0; st < 4; ++st) c = mfma_bf16_16x16x32(a[tl].s[st], b.s[st], c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(fmaxf(c[i], 0.f), wr[tl][i], s);
+    for (int i = 0; i < 4; ++i) s = fmaf(__builtin_fabsf(c[i]) + c[i], wr[tl][i], s);
   }
   return s;
 }

@@ -37,6 +37,9 @@ constexpr int kBlk = 32;                     // selected rows per block
 constexpr int kChunks = kDqk / 8;            // 16-byte chunks per latent row (72)
 constexpr int kBufBytes = kBlk * kDqk * 2;   // 36864 bytes per buffer
 constexpr int kHeadsPerWave = 16;               // 8 waves x 16 heads
+constexpr int kStages = 3;                      // LDS pipeline depth
+constexpr int kDmaPerWave = 5;                  // ceil(36 DMA instructions / 8 waves)
+constexpr int kMaxK = 4096;                     // entries per query the row table holds
 
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -73,10 +76,32 @@ struct MlaParams {
   float* part_lse;
 };
 
+// Drives the 3-stage pipeline over the three LDS stage buffers.  The buffers
+// arrive as restrict-qualified parameters: after inlining, every access
+// through them carries alias-scope metadata, which lets the compiler see that
+// the stage being read is not the stage a DMA is still writing (otherwise it
+// waits for every outstanding DMA before the first LDS read).
+template <class Gather, class Step>
+__device__ __forceinline__ void run_pipeline(uint8_t* __restrict__ kb0, uint8_t* __restrict__ kb1,
+                                             uint8_t* __restrict__ kb2, int nb, Gather& gather, Step& step) {
+  if (nb > 0) gather(kb0, 0);
+  if (nb > 1) gather(kb1, 1);
+  for (int blk = 0; blk < nb; blk += 3) {
+    step(kb0, kb2, blk);
+    if (blk + 1 < nb) step(kb1, kb0, blk + 1);
+    if (blk + 2 < nb) step(kb2, kb1, blk + 2);
+  }
+}
+
 template <class Addr>
 __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(MlaParams p, Addr addr) {
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kBufBytes];
-  __shared__ v8bf qtail[4 * 8 * 64];  // 32 KiB: query steps 14..17 of all waves
+  // three separate stage buffers, so the compiler can tell the stage being
+  // read from the stages the DMA is still writing
+  __shared__ __attribute__((aligned(16))) uint8_t kb0[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kb1[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kb2[kBufBytes];
+  __shared__ v8bf qtail[4 * 8 * 64];   // 32 KiB: query steps 14..17 of all waves
+  __shared__ int32_t rows[kMaxK];      // latent row of every entry of this split (-1: skipped)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, hl = lane & 15;
   const int64_t t = blockIdx.x / p.n_split;
@@ -89,6 +114,19 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(MlaParams p, Addr ad
   const int head = kHeadsPerWave * wave + hl;
   const bool active = kHeadsPerWave * wave < p.H;
   const int32_t* idx_row = p.idx + t * (int64_t)p.k;
+  const int n_ent = j1 > j0 ? j1 - j0 : 0;
+  const int nb = (n_ent + kBlk - 1) / kBlk;
+
+  // ---- resolve every entry to a latent row once (index and page-table
+  // loads happen here only, so the block loop issues no other memory reads)
+  for (int e = tid; e < nb * kBlk; e += 512) {
+    int32_t row = -1;
+    if (e < n_ent) {
+      const int32_t s = idx_row[j0 + e];
+      if (s >= 0 && s < n_b) row = (int32_t)addr.row(b, s);
+    }
+    rows[e] = row;
+  }
 
   // ---- query rows of this wave's 16 heads: B operand of the logit MFMA,
   // step st covers dims 32*st + 8*g4 .. +7.  Steps 0..13 stay in VGPRs; steps
@@ -110,35 +148,28 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(MlaParams p, Addr ad
       qtail[((st - kQReg) * 8 + wave) * 64 + lane] = hv ? v : (v8bf){};
     }
   }
+  __syncthreads();
 
-  // Row of entry j of this query (-1: skipped).  Lanes 0..31 of every wave
-  // resolve the 32 entries of a block; the DMA lanes pick them up by shuffle.
-  auto resolve = [&](int jb) -> int32_t {
-    const int j = jb + (lane & 31);
-    int32_t row = -1;
-    if (j < j1) {
-      const int32_t s = idx_row[j];
-      if (s >= 0 && s < n_b) row = (int32_t)addr.row(b, s);
-    }
-    return row;
-  };
-  // Gather the 32 rows of a block into LDS buffer `bi`: 36 DMA instructions
-  // of 64 x 16 bytes, spread over the 8 waves.  Skipped entries read row 0
-  // (their logits are masked, so the bytes only have to be finite).
-  auto gather = [&](int bi, int32_t my_row) {
-    uint8_t* base = kbuf[bi];
+  // Gather the 32 rows of block `blk` into LDS stage `bi`: 36 DMA
+  // instructions of 64 x 16 bytes; every wave issues exactly kDmaPerWave
+  // (waves 4..7 repeat their first one, an identical rewrite) so the
+  // outstanding-load count is the same on every wave.  Skipped entries read
+  // row 0 (their logits are masked, so the bytes only have to be finite).
+  auto gather = [&](uint8_t* base, int blk) {
+    // slot indices are recomputed per call (cheap) rather than kept live
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int ins = wave + 8 * i;
-      if (ins < kBlk * kChunks / 64) {
-        const int slot0 = 64 * ins;
-        int r, c;
-        kslot_inv(slot0 + lane, r, c);
-        int32_t row = __shfl(my_row, r, 64);
-        row = row < 0 ? 0 : row;
-        const uint16_t* src = p.kv + ((uint64_t)(uint32_t)row * kDqk + 8 * c);
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(base + slot0 * 16), 16, 0, 0);
-      }
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      int ins = wave + 8 * i;
+      if (ins >= kBlk * kChunks / 64) ins = wave;
+      const int slot0 = 64 * ins;
+      int r, c;
+      kslot_inv(slot0 + lane + zero, r, c);
+      int32_t row = rows[blk * kBlk + r];
+      row = row < 0 ? 0 : row;
+      const uint16_t* src = p.kv + ((uint64_t)(uint32_t)row * kDqk + 8 * c);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(base + slot0 * 16), 16, 0, 0);
     }
   };
 
@@ -174,32 +205,22 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(MlaParams p, Addr ad
   for (int i = 0; i < 32; ++i) o[i] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // pipeline state: rows of the next block, valid masks of the current and next
-  int32_t row_next = -1;
-  uint64_t valid_cur = 0, valid_next = 0;
-  if (j0 < j1) {
-    const int32_t r0 = resolve(j0);
-    valid_cur = __ballot(r0 >= 0) & 0xFFFFFFFFull;
-    gather(0, r0);
-    if (j0 + kBlk < j1) {
-      row_next = resolve(j0 + kBlk);
-      valid_next = __ballot(row_next >= 0) & 0xFFFFFFFFull;
-    }
-  }
-
-  int buf = 0;
-  for (int jb = j0; jb < j1; jb += kBlk) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (jb + kBlk < j1) gather(buf ^ 1, row_next);
-    const uint64_t valid = valid_cur;
-    valid_cur = valid_next;
-    if (jb + 2 * kBlk < j1) {
-      row_next = resolve(jb + 2 * kBlk);
-      valid_next = __ballot(row_next >= 0) & 0xFFFFFFFFull;
-    }
+  // 3-stage pipeline: blocks blk+1 and blk+2 stream in while blk is consumed
+  // One pipeline step: wait for this wave's DMA of block blk (block blk+1 may
+  // stay in flight), barrier (every wave's DMA of blk landed and block blk-1
+  // is fully consumed), launch the DMA of blk+2 into the freed stage, then
+  // consume stage `cur`.  s_barrier is used bare: a fenced __syncthreads()
+  // would also wait for the DMA still in flight.
+  auto step = [&](const uint8_t* cur, uint8_t* next2, int blk) {
+    if (blk + 1 < nb)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (blk + 2 < nb) gather(next2, blk + 2);
+    const uint64_t valid = __ballot(rows[blk * kBlk + (lane & 31)] >= 0) & 0xFFFFFFFFull;
     if (active) {
-      const lds_u8_ptr base = (lds_u8_ptr)kbuf[buf];
+      const lds_u8_ptr base = (lds_u8_ptr)cur;
       // logits S^T[key, head]: two 16-key M-tiles x 18 k-steps
       v4f sacc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -213,34 +234,39 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(MlaParams p, Addr ad
         }
         if ((st % 6) == 5) __builtin_amdgcn_sched_barrier(0);
       }
-      // lane: head hl; sacc[mt][i] is key 16*mt + 4*g4 + i of the block;
-      // scaled to log2 units in place, masked keys at -inf
+      // lane: head hl; sacc[mt][i] is key 16*mt + 4*g4 + i of the block (raw
+      // logit; masked keys set to -inf).  The running max m_run is kept in
+      // log2 units: p = 2^(logit * scale*log2e - m_run).
       float mloc = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = 16 * mt + 4 * g4 + i;
-          sacc[mt][i] = ((valid >> key) & 1) ? sacc[mt][i] * p.scale_log2 : -INFINITY;
+          sacc[mt][i] = ((valid >> key) & 1) ? sacc[mt][i] : -INFINITY;
           mloc = fmaxf(mloc, sacc[mt][i]);
         }
       }
       mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
       mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+      mloc *= p.scale_log2;  // scale > 0 keeps the order
       const bool need = mloc > m_run + 8.0f;
       if (__any(need)) {
         const float m_new = need ? mloc : m_run;
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
         for (int ct = 0; ct < 32; ++ct) o[ct] *= alpha;
       }
+      // masked keys: fma(-inf, s, -m) = -inf -> 2^-inf = 0; before the first
+      // valid key m_run is -inf and every logit is -inf, so the bias is 0
+      const float mneg = (m_run == -INFINITY) ? 0.f : -m_run;
       v8f pf;
       float lsum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float pv = (m_run == -INFINITY) ? 0.f : exp2f(sacc[i >> 2][i & 3] - m_run);
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 2][i & 3], p.scale_log2, mneg));
         lsum += pv;
         pf[i] = pv;
       }
@@ -261,8 +287,9 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(MlaParams p, Addr ad
         if ((ct & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }
     }
-    buf ^= 1;
-  }
+  };
+
+  run_pipeline(kb0, kb1, kb2, nb, gather, step);
 
   if (!active || head >= p.H) return;
   float l_tot = l_run + shfl_xor_f(l_run, 16);
