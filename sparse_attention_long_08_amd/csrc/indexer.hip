@@ -86,17 +86,30 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx, co
 // wr holds w/2: w * ReLU(c) = (|c| + c) * (w/2) exactly (the doubling and the
 // halving are exact), which is one add with an abs source modifier plus one
 // FMA -- fmaxf would cost an extra canonicalisation per element.
+// Each 16-head tile keeps its own partial sum (short dependency chains); the
+// tiles are added at the end.
 template <int NT>
 __device__ __forceinline__ float head_sum(const Frag (&a)[NT], const float (&wr)[NT][4], const Frag& b) {
-  float s = 0.f;
+  v4f c[NT];
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) c[tl] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+#pragma unroll
+    for (int tl = 0; tl < NT; ++tl) c[tl] = mfma_bf16_16x16x32(a[tl].s[st], b.s[st], c[tl]);
+  }
+  float part[NT];
 #pragma unroll
   for (int tl = 0; tl < NT; ++tl) {
-    v4f c = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < 4; ++st) c = mfma_bf16_16x16x32(a[tl].s[st], b.s[st], c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(__builtin_fabsf(c[i]) + c[i], wr[tl][i], s);
+    float s0 = (__builtin_fabsf(c[tl][0]) + c[tl][0]) * wr[tl][0];
+    float s1 = (__builtin_fabsf(c[tl][1]) + c[tl][1]) * wr[tl][1];
+    s0 = fmaf(__builtin_fabsf(c[tl][2]) + c[tl][2], wr[tl][2], s0);
+    s1 = fmaf(__builtin_fabsf(c[tl][3]) + c[tl][3], wr[tl][3], s1);
+    part[tl] = s0 + s1;
   }
+  float s = part[0];
+#pragma unroll
+  for (int tl = 1; tl < NT; ++tl) s += part[tl];
   return s;
 }
 

@@ -18,9 +18,9 @@
 
 namespace dsa {
 
-constexpr int kTopkThreads = 1024;
+constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kTopkCap = 4096;  // LDS candidate list capacity
+constexpr int kTopkCap = 3072;  // LDS candidate list capacity (two workgroups fit a CU)
 
 struct TopkShared {
   uint32_t hist[4096];
@@ -34,7 +34,7 @@ struct TopkShared {
   uint32_t pad;
 };
 
-// Inclusive block scan of two counters (1024 threads).  Returns inclusive
+// Inclusive block scan of two counters (one workgroup).  Returns inclusive
 // prefixes in *a, *b and the block totals in *ta, *tb.
 __device__ __forceinline__ void block_scan2(TopkShared& sh, uint32_t* a, uint32_t* b, uint32_t* ta,
                                             uint32_t* tb) {
@@ -76,20 +76,22 @@ __device__ __forceinline__ void block_scan2(TopkShared& sh, uint32_t* a, uint32_
 // bin holding the k-th largest key.  Publishes sh.sel_bin and sh.sel_above
 // (= keys greater than that bin).
 __device__ __forceinline__ void find_bin(TopkShared& sh, int nbins, uint32_t above, uint32_t k) {
+  constexpr int BPT = 4096 / kTopkThreads;  // bins per thread at the widest level
   const int tid = threadIdx.x;
-  // thread tid owns bins nbins-1-4*tid .. nbins-4-4*tid (top-down order)
+  // thread tid owns bins nbins-1-BPT*tid .. nbins-BPT-BPT*tid (top-down order)
   uint32_t c = 0;
-  const int top = nbins - 1 - 4 * tid;
+  const int top = nbins - 1 - BPT * tid;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < BPT; ++i)
     if (top - i >= 0) c += sh.hist[top - i];
   uint32_t inc = c, dummy = 0, tot, tot2;
   block_scan2(sh, &inc, &dummy, &tot, &tot2);
   uint32_t run = above + inc - c;  // keys in bins above this thread's bins
   if (top >= 0 && run < k && run + c >= k) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < BPT; ++i) {
       const int bin = top - i;
+      if (bin < 0) break;
       const uint32_t h = sh.hist[bin];
       if (run < k && run + h >= k) {
         sh.sel_bin = (uint32_t)bin;
@@ -100,6 +102,26 @@ __device__ __forceinline__ void find_bin(TopkShared& sh, int nbins, uint32_t abo
     }
   }
   __syncthreads();
+}
+
+// Calls fn(s, key) for every candidate s < n of the row, four per load when
+// the row is 16-byte aligned (any order: the callers only count or mark).
+template <class Fn>
+__device__ __forceinline__ void scan_row(const float* __restrict__ row, int64_t n, bool vec, Fn&& fn) {
+  const int tid = threadIdx.x;
+  if (vec) {
+    const int64_t n4 = n & ~(int64_t)3;
+    for (int64_t s = 4 * (int64_t)tid; s < n4; s += 4 * kTopkThreads) {
+      const v4f v = *(const v4f*)(row + s);
+      fn(s, order_key(v[0]));
+      fn(s + 1, order_key(v[1]));
+      fn(s + 2, order_key(v[2]));
+      fn(s + 3, order_key(v[3]));
+    }
+    for (int64_t s = n4 + tid; s < n; s += kTopkThreads) fn(s, order_key(row[s]));
+  } else {
+    for (int64_t s = tid; s < n; s += kTopkThreads) fn(s, order_key(row[s]));
+  }
 }
 
 // Radix levels: 0 -> key bits 31..20, 1 -> bits 19..8, 2 -> bits 7..0.
@@ -125,6 +147,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     return;
   }
   const float* row = scores + t * ld;
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
 
   // ------------------------------------------------------------ global refinement
   // Current candidate key range [lo, hi]; `above` keys are > hi.
@@ -135,10 +158,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     const int sh_ = level_shift(level), nb = 1 << level_bits(level);
     for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0;
     __syncthreads();
-    for (int64_t s = tid; s < n; s += kTopkThreads) {
-      const uint32_t key = order_key(row[s]);
+    scan_row(row, n, vec, [&](int64_t, uint32_t key) {
       if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key >> sh_) & (nb - 1)], 1u);
-    }
+    });
     __syncthreads();
     find_bin(sh, nb, above, (uint32_t)k);
     const uint32_t bin = sh.sel_bin;
@@ -155,8 +177,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   if (tid == 0) sh.list_n = 0;
   __syncthreads();
   const bool exact = (lo == hi);
-  for (int64_t s = tid; s < n; s += kTopkThreads) {
-    const uint32_t key = order_key(row[s]);
+  scan_row(row, n, vec, [&](int64_t s, uint32_t key) {
     if (key > hi) {
       atomicOr(&gt_bits[s >> 5], 1u << (s & 31));
     } else if (key >= lo) {
@@ -168,7 +189,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         sh.list_idx[slot] = (int32_t)s;
       }
     }
-  }
+  });
   __syncthreads();
 
   // ------------------------------------------------------------ LDS refinement
@@ -219,10 +240,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   block_scan2(sh, &ig, &ie, &tg, &te);
   const uint32_t r = (uint32_t)k - tg;  // ties to take, lowest positions first
   uint32_t eq_before = ie - ce;
-  uint32_t sel_words[8];
+  uint32_t sel_words[16];
   uint32_t cs = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     const int wi = w0 + i;
     uint32_t g = 0, e = 0;
     if (i < wpt && wi < n_words) {
@@ -243,7 +264,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   block_scan2(sh, &is, &dummy, &ts, &td);
   uint32_t pos = is - cs;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     uint32_t m = sel_words[i];
     const int base = (w0 + i) * 32;
     while (m) {
@@ -261,7 +282,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, in
   const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words;
   static bool attr_set = false;
   if (!attr_set) {
-    // rows up to 262144 keys: 48 KiB of fixed state + 64 KiB of bitmaps
+    // rows up to 262144 keys: fixed state + 64 KiB of bitmaps
     hipError_t e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192));
     if (e != hipSuccess) return e;
