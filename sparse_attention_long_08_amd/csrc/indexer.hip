@@ -269,9 +269,9 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
 
 // ---------------------------------------------------------------- launchers
 namespace {
-constexpr int kPrefillNW = 8;
+constexpr int kPrefillNW = 4;
 constexpr int kPrefillQW = 1;
-constexpr int kPrefillChunk = 4096;
+constexpr int kPrefillChunk = 8192;
 constexpr int kDecodeChunk = 1024;
 
 template <int NT>

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(MlaParams p, Addr ad
               *(const __attribute__((address_space(3))) v8bf*)(base + s_addr[mt][st & 1] + 128 * (st >> 1));
           sacc[mt] = mfma_bf16_16x16x32(a, qb, sacc[mt]);
         }
-        if ((st % 6) == 5) __builtin_amdgcn_sched_barrier(0);
+        if ((st % 2) == 1) __builtin_amdgcn_sched_barrier(0);
       }
       // lane: head hl; sacc[mt][i] is key 16*mt + 4*g4 + i of the block (raw
       // logit; masked keys set to -inf).  The running max m_run is kept in
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(512, 1) void sparse_mla_kernel(MlaParams p, Addr ad
         const v8bf va = __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         o[ct] = mfma_bf16_16x16x32(va, pb, o[ct]);
         // bound how far the scheduler hoists operand reads (register budget)
-        if ((ct & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        if ((ct & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
