@@ -10,6 +10,16 @@ bit-identical to one fused call.
 
 Prints one JSON line: query-tokens/s, the dominant kernel's roofline, and the
 CPU oracle's rate on a bounded sample of the same workload.
+
+Other modes (not the headline line):
+  --workload decode_b64_ctx32k | paged_decode_b32_ctx4k_128k
+      one step = one fused decode call (indexer -> top-k -> split attention ->
+      combine) for the whole batch; per-kernel times come from a staged replay
+      through the paged entry points (the contiguous cache is addressed through
+      an identity page table for it).
+  --copy-calibration
+      copies a 1 GiB buffer three times with a plain device copy, so that HBM
+      byte counters read under a profiler can be scaled against a known size.
 """
 from __future__ import annotations
 
@@ -26,6 +36,34 @@ METRIC = "DSA query-tokens/s at 128K ctx, k=2048 (indexer+topk+sparse MLA); %roo
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+
+# HBM bytes per dispatch read with rocprofv3 (FETCH_SIZE and WRITE_SIZE, one counter per run),
+# scaled by what the same counters read for a plain 1 GiB device copy (bytes read =
+# FETCH_SIZE KiB x 1024 x 2.0, bytes written = WRITE_SIZE KiB x 1024 x 1.0).  Each entry holds
+# the hash of the kernel sources the counters were taken on; once a source changes, the
+# figure no longer describes the kernel and the roofline reports traffic as null.
+COUNTER_TRAFFIC = {
+    ("prefill_L128k", "indexer"): ("405db5745fd97c6b", ("indexer.hip", "common.h", "launch.h"), 1130.24e6),
+    ("prefill_L128k", "topk"): ("37e0d6361a587fae", ("topk.hip", "common.h", "launch.h"), 1117.57e6),
+    ("prefill_L128k", "sparse_mla"): ("17949ff47ce3c62f", ("sparse_mla.hip", "common.h", "launch.h"), 206030.07e6),
+    ("paged_decode_b32_ctx4k_128k", "indexer"): ("405db5745fd97c6b", ("indexer.hip", "common.h", "launch.h"),
+                                                 278.34e6),
+    ("paged_decode_b32_ctx4k_128k", "topk"): ("37e0d6361a587fae", ("topk.hip", "common.h", "launch.h"), 8.64e6),
+}
+
+
+def counter_traffic(workload: str, kernel: str):
+    """Counter-measured HBM bytes per dispatch, or None if absent or taken on other sources."""
+    import hashlib
+    ent = COUNTER_TRAFFIC.get((workload, kernel))
+    if ent is None:
+        return None
+    digest, files, nbytes = ent
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "sparse_attention_long_08_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return nbytes if h.hexdigest()[:16] == digest else None
 
 
 def algorithmic_work(wl, T):
@@ -65,26 +103,56 @@ def cpu_baseline(wl, rows: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 3 prefill, 200 decode)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 1 prefill, 20 decode)")
     ap.add_argument("--workload", default="prefill_L128k")
-    ap.add_argument("--cpu-rows", type=int, default=6)
+    ap.add_argument("--cpu-rows", type=int, default=60, help="query rows the CPU oracle baseline times")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the DSA path here is a single-GPU kernel library).", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        return copy_calibration()
+
+    from dsa_inputs import configs
+
+    wl = configs.WORKLOADS[args.workload]
+    decode = wl.kind != "prefill"
+    if args.steps is None:
+        args.steps = 200 if decode else 3
+    if args.warmup is None:
+        args.warmup = 20 if decode else 1
+    if decode:
+        return bench_decode(args, wl)
+    return bench_prefill(args, wl)
+
+
+def copy_calibration():
+    """Three plain device copies of 1 GiB (reads 1 GiB and writes 1 GiB each)."""
+    import torch
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for i in range(3):
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy {i + 1}/3 of {nbytes} bytes done", file=sys.stderr, flush=True)
+    print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 3}))
+
+
+def bench_prefill(args, wl):
     import numpy as np
     import torch
 
     import sparse_attention_long_08_amd as dsa
-    from dsa_inputs import configs, device
+    from dsa_inputs import device
 
     dsa.load()
-    wl = configs.WORKLOADS[args.workload]
-    assert wl.kind == "prefill"
     T, N, k = wl.T, wl.N, wl.k
     print(f"[bench] generating {wl.name} inputs on the GPU", file=sys.stderr, flush=True)
     inp = device.make_prefill_inputs(wl)
@@ -157,11 +225,14 @@ def main():
     same = bool(torch.equal(f_idx, idx) and torch.equal(f_lse, lse) and torch.equal(f_out, out))
     del f_out
     w = algorithmic_work(wl, T)
-    t_roof = max(w["idx_flops"] / (PEAK_FP8_TFLOPS * 1e12) + w["mla_flops"] / (PEAK_BF16_TFLOPS * 1e12),
-                 (w["idx_bytes"] + w["topk_bytes"] + w["mla_bytes"]) / (PEAK_HBM_GBS * 1e9))
+    hbm_s = (w["idx_bytes"] + w["topk_bytes"] + w["mla_bytes"]) / (PEAK_HBM_GBS * 1e9)
+    # the method's roofline prices the indexer at the FP8 MFMA peak; the kernel here
+    # contracts the (exactly widened) FP8 values on bf16 MFMA, so its own peak is bf16's
+    t_roof = max(w["idx_flops"] / (PEAK_FP8_TFLOPS * 1e12) + w["mla_flops"] / (PEAK_BF16_TFLOPS * 1e12), hbm_s)
+    t_roof_bf16 = max((w["idx_flops"] + w["mla_flops"]) / (PEAK_BF16_TFLOPS * 1e12), hbm_s)
     kernels = {
         "sparse_mla": ("mfma", w["mla_flops"] / (stage_ms["sparse_mla"] * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
-        "indexer": ("mfma", w["idx_flops"] / (stage_ms["indexer"] * 1e-3) / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"),
+        "indexer": ("mfma", w["idx_flops"] / (stage_ms["indexer"] * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
         "topk": ("hbm", w["topk_bytes"] / (stage_ms["topk"] * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"),
     }
     dom = max(stage_ms, key=stage_ms.get)
@@ -178,15 +249,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3(indexer)+bf16(attention), fp32 accumulate",
+        "dtype": "bf16",
         "data": "synthetic (seeded counter-based generator, device-resident)",
         "config": {"workload": wl.name, "L": T, "k": k, "H_I": wl.H_I, "d_I": wl.d_I, "H": wl.H,
                    "D_qk": wl.D_qk, "D_v": wl.D_v, "causal": True, "parallelism": "single GPU"},
         "roofline": {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
-                     "frac": ach / peak, "traffic": None, "launches_per_step": launches,
-                     "avg_launch_ms": stage_ms[dom] / launches},
+                     "frac": ach / peak, "traffic": counter_traffic(wl.name, dom), "launches_per_step": launches,
+                     "avg_launch_ms": stage_ms[dom] / launches,
+                     "frac_vs_fp8_peak": (ach / PEAK_FP8_TFLOPS) if dom == "indexer" else None},
         "stages_ms": stage_ms,
-        "path_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_per_step},
+        "path_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_per_step,
+                          "t_roof_bf16_indexer_ms": t_roof_bf16 * 1e3,
+                          "frac_bf16_indexer": t_roof_bf16 * 1e3 / ms_per_step},
         "fused_call_ms": fused_ms,
         "staged_equals_fused": same,
     }
@@ -195,6 +269,152 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
     else:
         rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+def decode_work(wl, ctx):
+    """Algorithmic bytes of one decode step (every input read once, outputs written once)."""
+    import numpy as np
+    ctx = ctx.astype(np.float64)
+    sel = np.minimum(ctx, wl.k).sum()
+    idx_bytes = wl.B * (wl.H_I * wl.d_I + 4 * wl.H_I) + ctx.sum() * wl.d_I
+    topk_bytes = wl.B * wl.k * 4
+    mla_bytes = wl.B * (wl.H * wl.D_qk * 2 + wl.H * wl.D_v * 4 + wl.H * 4) + sel * wl.D_qk * 2
+    idx_flops = ctx.sum() * 2 * wl.H_I * wl.d_I
+    mla_flops = sel * 2 * wl.H * (wl.D_qk + wl.D_v)
+    return dict(idx_bytes=idx_bytes, topk_bytes=topk_bytes, mla_bytes=mla_bytes, idx_flops=idx_flops,
+                mla_flops=mla_flops, selected=sel, keys=ctx.sum())
+
+
+def bench_decode(args, wl):
+    import numpy as np
+    import torch
+
+    import sparse_attention_long_08_amd as dsa
+    from dsa_inputs import configs, device
+
+    dsa.load()
+    B, k = wl.B, wl.k
+    ctx = configs.ctx_lens(wl)
+    max_ctx = int(ctx.max())
+    print(f"[bench] generating {wl.name} inputs on the GPU", file=sys.stderr, flush=True)
+    if wl.kind == "paged_decode":
+        inp = device.make_paged_inputs(wl)
+        k_pool, kv_pool, page_table, n_pages = inp["k_pool"], inp["kv_pool"], inp["page_table"], inp["n_pages"]
+        max_pages = page_table.shape[1]
+        nb = dsa.dsa_forward_decode_paged_workspace_bytes(B, max_ctx, wl.H, wl.D_v, k)
+    else:
+        inp = device.make_decode_inputs(wl)
+        # the contiguous [B, N, dim] caches seen as pools of 64-token pages with an identity table
+        max_pages = wl.N // wl.page
+        n_pages = B * max_pages
+        k_pool, kv_pool = inp["k_idx"], inp["kv"]
+        page_table = torch.arange(n_pages, dtype=torch.int32, device="cuda").reshape(B, max_pages)
+        nb = dsa.dsa_forward_decode_workspace_bytes(B, wl.N, wl.H, wl.D_v, k)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, wl.H, wl.D_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, wl.H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        if wl.kind == "paged_decode":
+            dsa.dsa_forward_decode_paged(inp["q_idx"], inp["w"], k_pool, inp["q"], kv_pool, n_pages, page_table,
+                                         max_pages, inp["ctx_len"], wl.page, B, max_ctx, wl.H_I, wl.d_I, wl.H,
+                                         wl.D_qk, wl.D_v, k, wl.scale, idx, out, lse, ws, ws.numel())
+        else:
+            dsa.dsa_forward_decode(inp["q_idx"], inp["w"], inp["k_idx"], inp["q"], inp["kv"], inp["ctx_len"], B,
+                                   wl.N, wl.H_I, wl.d_I, wl.H, wl.D_qk, wl.D_v, k, wl.scale, idx, out, lse, ws,
+                                   ws.numel())
+
+    # staged replay through the paged entry points, for per-kernel times
+    ld = (max_ctx + 63) // 64 * 64
+    scores = torch.empty((B, ld), dtype=torch.float32, device="cuda")
+    s_idx = torch.empty_like(idx)
+    s_out = torch.empty_like(out)
+    s_lse = torch.empty_like(lse)
+    mla_nb = dsa.dsa_sparse_mla_fwd_paged_workspace_bytes(B, wl.H, wl.D_v, k)
+    mla_ws = torch.empty(max(mla_nb, 256), dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def staged(record):
+        if record:
+            ev[0].record(stream)
+        dsa.dsa_indexer_scores_paged(inp["q_idx"], inp["w"], k_pool, n_pages, page_table, max_pages, inp["ctx_len"],
+                                     wl.page, B, wl.H_I, wl.d_I, max_ctx, scores, ld)
+        if record:
+            ev[1].record(stream)
+        dsa.dsa_topk(scores, ld, B, max_ctx, 0, inp["ctx_len"], k, s_idx)
+        if record:
+            ev[2].record(stream)
+        dsa.dsa_sparse_mla_fwd_paged(inp["q"], kv_pool, n_pages, page_table, max_pages, inp["ctx_len"], wl.page,
+                                     s_idx, B, wl.H, wl.D_qk, wl.D_v, k, wl.scale, s_out, s_lse, mla_ws, mla_nb)
+        if record:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        fused()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} fused decode steps done", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        staged(False)
+    stage_ms = {"indexer": 0.0, "topk": 0.0, "sparse_mla": 0.0}
+    for _ in range(args.steps):
+        staged(True)
+        torch.cuda.synchronize()
+        stage_ms["indexer"] += ev[0].elapsed_time(ev[1])
+        stage_ms["topk"] += ev[1].elapsed_time(ev[2])
+        stage_ms["sparse_mla"] += ev[2].elapsed_time(ev[3])
+    stage_ms = {kk: v / args.steps for kk, v in stage_ms.items()}
+    same = bool(torch.equal(s_idx, idx) and torch.equal(s_out, out) and torch.equal(s_lse, lse))
+
+    w = decode_work(wl, ctx)
+    total_bytes = w["idx_bytes"] + w["topk_bytes"] + w["mla_bytes"]
+    t_roof = max(total_bytes / (PEAK_HBM_GBS * 1e9),
+                 w["idx_flops"] / (PEAK_FP8_TFLOPS * 1e12) + w["mla_flops"] / (PEAK_BF16_TFLOPS * 1e12))
+    kernels = {
+        "indexer": ("hbm", w["idx_bytes"] / (stage_ms["indexer"] * 1e-3) / 1e9),
+        "topk": ("hbm", w["topk_bytes"] / (stage_ms["topk"] * 1e-3) / 1e9),
+        "sparse_mla": ("hbm", w["mla_bytes"] / (stage_ms["sparse_mla"] * 1e-3) / 1e9),
+    }
+    dom = max(stage_ms, key=stage_ms.get)
+    bound, ach = kernels[dom]
+    rec = {
+        "metric": "DSA decode query-tokens/s (indexer+topk+sparse MLA); %roofline",
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "host_wall_ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator, device-resident)",
+        "config": {"workload": wl.name, "B": B, "max_ctx": max_ctx, "mean_ctx": float(ctx.mean()), "k": k,
+                   "H_I": wl.H_I, "H": wl.H, "paged": wl.kind == "paged_decode"},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM_GBS, "traffic": counter_traffic(wl.name, dom), "launches_per_step": 1,
+                     "avg_launch_ms": stage_ms[dom]},
+        "stages_ms": stage_ms,
+        "path_roofline": {"t_roof_ms": t_roof * 1e3, "algorithmic_bytes": total_bytes,
+                          "frac": t_roof * 1e3 / ms_per_step},
+        "staged_equals_fused": same,
+        "cpu_baseline": None,
+    }
     print(json.dumps(rec))
 
 
