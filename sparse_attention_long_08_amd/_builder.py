@@ -19,16 +19,40 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = ["hipcc", *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-x", "hip", *srcs, "-o", tmp]
+# Per-source extra flags.  The attention kernel keeps its logit accumulators
+# in VGPRs (VGPR-form MFMAs) so that its 256 output accumulators alone fill
+# the accumulation registers.
+SOURCE_FLAGS = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
+        sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libdsa.so")
+    return r
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    import concurrent.futures
+    import tempfile
+    inc = ["-I", os.path.join(ROOT, "include")]
+    with tempfile.TemporaryDirectory(prefix="dsa_build_") as tmpdir:
+        objs, cmds = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src.replace(".", "_") + ".o")
+            objs.append(obj)
+            flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+            cmds.append(["hipcc", *flags, *SOURCE_FLAGS.get(src, []), *extra, *inc, "-x", "hip", "-c",
+                         os.path.join(CSRC, src), "-o", obj])
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            results = list(ex.map(_run, cmds))
+        tmp = LIB + ".tmp"
+        link = ["hipcc", "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp]
+        results.append(_run(link))
     if verbose:
-        sys.stderr.write(r.stderr)
+        for r in results:
+            sys.stderr.write(r.stderr)
     os.replace(tmp, LIB)
     return LIB
 
