@@ -19,10 +19,12 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The attention kernel keeps its logit accumulators
-# in VGPRs (VGPR-form MFMAs) so that its 256 output accumulators alone fill
-# the accumulation registers.
-SOURCE_FLAGS = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags: VGPR-form MFMAs.  The attention kernel keeps its
+# logit accumulators in VGPRs so that its 256 output accumulators alone fill
+# the accumulation registers; the indexer's epilogue reads every accumulator
+# with VALU instructions, which cannot read accumulation registers directly.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCE_FLAGS = {"sparse_mla.hip": _VGPR_FORM, "indexer.hip": _VGPR_FORM}
 
 
 def _run(cmd):

@@ -85,9 +85,8 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx, co
 // Weighted, rectified head sum of one query against one 16-key block.
 // wr holds w/2: w * ReLU(c) = (|c| + c) * (w/2) exactly (the doubling and the
 // halving are exact), which is one add with an abs source modifier plus one
-// FMA -- fmaxf would cost an extra canonicalisation per element.
-// Each 16-head tile keeps its own partial sum (short dependency chains); the
-// tiles are added at the end.
+// FMA per element -- fmaxf would cost an extra canonicalisation.  The 4*NT
+// elements of a lane accumulate in two FMA chains.
 template <int NT>
 __device__ __forceinline__ float head_sum(const Frag (&a)[NT], const float (&wr)[NT][4], const Frag& b) {
   v4f c[NT];
@@ -98,19 +97,15 @@ __device__ __forceinline__ float head_sum(const Frag (&a)[NT], const float (&wr)
 #pragma unroll
     for (int tl = 0; tl < NT; ++tl) c[tl] = mfma_bf16_16x16x32(a[tl].s[st], b.s[st], c[tl]);
   }
-  float part[NT];
+  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
   for (int tl = 0; tl < NT; ++tl) {
-    float s0 = (__builtin_fabsf(c[tl][0]) + c[tl][0]) * wr[tl][0];
-    float s1 = (__builtin_fabsf(c[tl][1]) + c[tl][1]) * wr[tl][1];
+    s0 = fmaf(__builtin_fabsf(c[tl][0]) + c[tl][0], wr[tl][0], s0);
+    s1 = fmaf(__builtin_fabsf(c[tl][1]) + c[tl][1], wr[tl][1], s1);
     s0 = fmaf(__builtin_fabsf(c[tl][2]) + c[tl][2], wr[tl][2], s0);
     s1 = fmaf(__builtin_fabsf(c[tl][3]) + c[tl][3], wr[tl][3], s1);
-    part[tl] = s0 + s1;
   }
-  float s = part[0];
-#pragma unroll
-  for (int tl = 1; tl < NT; ++tl) s += part[tl];
-  return s;
+  return s0 + s1;
 }
 
 // ---------------------------------------------------------------- prefill

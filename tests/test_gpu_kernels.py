@@ -236,6 +236,41 @@ def test_sparse_mla_against_oracle(dsa, T, k, H):
         check_attention(g_out[t], g_lse[t], o_out, o_lse)
 
 
+def _bf16_bits(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_sparse_mla_large_logit_jump(dsa):
+    """A selected row whose logit exceeds every earlier block's by far more
+    than the softmax reference allows (~120 in log2 units): the query must be
+    redone against the true max and still match the oracle.  Query 0 meets
+    the large row in its fourth block, query 1 in its first."""
+    T, H, N, k = 2, 32, 256, 128
+    scale = 1.0 / np.sqrt(192.0)
+    _case("sparse_mla large logit jump")
+    qv = np.ones((T, H, 576), dtype=np.float32) * (1.0 + 0.25 * (np.arange(H) % 4))[None, :, None]
+    kvv = np.full((N, 576), 2.0 ** -7, dtype=np.float32)
+    kvv[200] = 2.0
+    kvv[3, :512] = -(2.0 ** -6)  # a second, distinct small row
+    q_h, kv_h = _bf16_bits(qv), _bf16_bits(kvv)
+    idx = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    idx[0, 100] = 200
+    idx[1, 5] = 200
+    q = torch.from_numpy(q_h.view(np.int16)).cuda().view(torch.uint16)
+    kv = torch.from_numpy(kv_h.view(np.int16)).cuda().view(torch.uint16)
+    out = torch.empty((T, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    nb = dsa.dsa_sparse_mla_fwd_workspace_bytes(T, H, 512, k)
+    ws = ws_tensor(nb)
+    dsa.dsa_sparse_mla_fwd(q, kv, torch.from_numpy(idx).cuda(), T, N, H, 576, 512, k, scale, out, lse, ws, nb)
+    torch.cuda.synchronize()
+    g_out, g_lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(np.isfinite(g_out)) and np.all(np.isfinite(g_lse))
+    for t in range(T):
+        o_out, o_lse = oracle.sparse_mla_row(q_h[t], kv_h[idx[t]], scale, 512)
+        check_attention(g_out[t], g_lse[t], o_out, o_lse)
+
+
 def test_sparse_mla_paged(dsa):
     wl = configs.WORKLOADS["paged_decode_b32_ctx4k_128k"]
     ctx = np.array([5, 700, 4096, 2000], dtype=np.int32)
