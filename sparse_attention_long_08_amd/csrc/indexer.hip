@@ -27,7 +27,12 @@
 namespace dsa {
 
 constexpr int kIdxD = 128;       // indexer head dim
-constexpr int kKeyStride = 272;  // LDS row stride of a staged bf16 key (bytes), padded against bank conflicts
+constexpr int kKeyStride = 256;  // LDS row of a staged bf16 key (bytes): 16 chunks of 16 bytes
+
+// 16-byte chunk slot of chunk c of staged key `key` (a swizzle chosen by
+// measuring LDS bank conflicts on gfx950: the operand reads below -- 16
+// consecutive keys x 4 chunk groups per instruction -- are conflict-free).
+__device__ __forceinline__ int kchunk(int key, int c) { return c ^ (((key & 3) << 2) | ((key >> 2) & 3)); }
 
 // On entry lane (g, c) = (lane/16, lane%16) holds its partial for key
 // 16*b + c of a 64-key group in p[b]; returns the sum over all four lane
@@ -142,10 +147,11 @@ __global__ __launch_bounds__(64 * NW, 1) void indexer_prefill_kernel(
     load_query<NT>(q_idx, w, r, valid, H_I, col, grp, a[q], wr[q]);
   }
 
-  // staging: thread tid moves FP8 bytes [kStageBytes*(tid%per_key), +kStageBytes)
-  // of key tid/per_key of a 64-key group and stores them widened to bf16
-  constexpr int per_key = kIdxD / kStageBytes;
-  const int st_key = tid / per_key, st_off = kStageBytes * (tid % per_key);
+  // staging: lane l of wave w moves FP8 bytes [32*(l/16), +32) of key
+  // 16*w + l%16 of a 64-key group and stores them widened to bf16 (the same
+  // shape as the operand reads, which keeps the LDS writes cheap)
+  static_assert(NW == 4, "staging maps 256 threads onto 64 keys x 4 slices");
+  const int st_key = 16 * wave + (lane & 15), st_off = kStageBytes * (lane >> 4);
   auto stage_load = [&](int64_t kg, v4i& s0, v4i& s1) {
     const int64_t s = kg + st_key;
     s0 = (v4i){0, 0, 0, 0};
@@ -157,13 +163,12 @@ __global__ __launch_bounds__(64 * NW, 1) void indexer_prefill_kernel(
     }
   };
   auto stage_store = [&](int bufi, v4i s0, v4i s1) {
-    v8bf* dst = (v8bf*)(&kbuf[bufi][st_key * kKeyStride + 2 * st_off]);
-    dst[0] = e4m3x8_to_bf16(s0.x, s0.y);
-    dst[1] = e4m3x8_to_bf16(s0.z, s0.w);
-    if (kStageBytes == 32) {
-      dst[2] = e4m3x8_to_bf16(s1.x, s1.y);
-      dst[3] = e4m3x8_to_bf16(s1.z, s1.w);
-    }
+    v8bf* row = (v8bf*)(&kbuf[bufi][st_key * kKeyStride]);
+    const int c0 = st_off / 8;  // bf16 chunk of FP8 byte st_off
+    row[kchunk(st_key, c0 + 0)] = e4m3x8_to_bf16(s0.x, s0.y);
+    row[kchunk(st_key, c0 + 1)] = e4m3x8_to_bf16(s0.z, s0.w);
+    row[kchunk(st_key, c0 + 2)] = e4m3x8_to_bf16(s1.x, s1.y);
+    row[kchunk(st_key, c0 + 3)] = e4m3x8_to_bf16(s1.z, s1.w);
   };
 
   v4i s0, s1;
@@ -178,10 +183,12 @@ __global__ __launch_bounds__(64 * NW, 1) void indexer_prefill_kernel(
       float part[QW][4];
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const v8bf* src = (const v8bf*)(&kbuf[buf][(16 * blk + col) * kKeyStride + 64 * grp]);
+        // key 16*blk + col, chunks 4*grp + st (dims 32*grp + 8*st ..)
+        const int key = 16 * blk + col;
+        const v8bf* row = (const v8bf*)(&kbuf[buf][key * kKeyStride]);
         Frag b;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) b.s[st] = src[st];
+        for (int st = 0; st < 4; ++st) b.s[st] = row[kchunk(key, 4 * grp + st)];
 #pragma unroll
         for (int q = 0; q < QW; ++q) part[q][blk] = head_sum<NT>(a[q], wr[q], b);
       }

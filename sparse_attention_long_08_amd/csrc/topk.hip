@@ -3,15 +3,26 @@
 // keep the k candidates with the largest index scores, ties to the lower
 // position, emitted in ascending position order and padded with -1.
 //
-// One workgroup per row.  Scores become order-preserving uint32 keys and the
-// k-th largest key (theta) is found by radix refinement: a 12-bit histogram
-// over the whole row (global pass 1), then the keys of the threshold bin
-// (~1% of a row) are gathered into LDS (global pass 2) and refined there
-// (12 + 8 more bits) without touching HBM again.  Rows whose threshold bin
-// overflows the LDS list (heavy ties) refine with further global passes.
-// Selection is recorded in two LDS bitmaps over the row: "key > theta" and
-// "key == theta"; one block scan over the bitmaps then gives each selected
-// position its output slot (the lowest-position ties are the first r
+// One workgroup per row; scores become order-preserving uint32 keys.
+//
+// Sampled path (long rows): 1/16 of the row, in 256-byte chunks spread over
+// the whole row, is read into LDS and its exact r-th largest key is found by
+// radix selection, with r chosen so that about 1.37k keys of the full row are
+// expected at or above it.  One pass over the row then gathers every key at
+// or above that estimate into an LDS list; if the list holds at least k and at
+// most its capacity, the exact k-th largest key (theta) and the selection come
+// from the list alone -- about 1.06 row reads in all.  Otherwise the row takes
+// the exact path.
+//
+// Exact path: theta by radix refinement -- a 12-bit histogram over the whole
+// row (one pass), then the keys of the threshold bin (~1% of a row) are
+// gathered into the LDS list (second pass) and refined there (12 + 8 more
+// bits).  Rows whose threshold bin overflows the list (heavy ties) refine
+// with further passes over the row.
+//
+// Either way the selection is recorded in two LDS bitmaps over the row,
+// "key > theta" and "key == theta"; one block scan over the bitmaps gives each
+// selected position its output slot (the lowest-position ties are the first r
 // "== theta" bits), so the output is ascending with no sort.
 #include "common.h"
 #include "launch.h"
@@ -20,7 +31,9 @@ namespace dsa {
 
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kTopkCap = 3072;  // LDS candidate list capacity (two workgroups fit a CU)
+constexpr int kTopkCap = 3584;  // LDS candidate list capacity (two workgroups fit a CU)
+constexpr int kSampleStride = 16;   // the sample reads one 64-key chunk in 16
+constexpr int kSampleMinN = 8192;   // shorter rows take the exact path
 
 struct TopkShared {
   uint32_t hist[4096];
@@ -104,14 +117,32 @@ __device__ __forceinline__ void find_bin(TopkShared& sh, int nbins, uint32_t abo
   __syncthreads();
 }
 
-// Calls fn(s, key) for every candidate s < n of the row, four per load when
-// the row is 16-byte aligned (any order: the callers only count or mark).
+// Calls fn(s, key) for every candidate s < n of the row (any order: the
+// callers only count, mark or gather).  On a 16-byte aligned row each thread
+// issues four 16-byte loads before using any of them, so enough reads are in
+// flight to cover the memory latency.
 template <class Fn>
 __device__ __forceinline__ void scan_row(const float* __restrict__ row, int64_t n, bool vec, Fn&& fn) {
   const int tid = threadIdx.x;
   if (vec) {
+    constexpr int kU = 4;
+    constexpr int64_t kStep = 4 * kTopkThreads;  // keys per unrolled sub-step
+    const int64_t n16 = n / (kU * kStep) * (kU * kStep);
+    for (int64_t s0 = 4 * (int64_t)tid; s0 < n16; s0 += kU * kStep) {
+      v4f v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = *(const v4f*)(row + s0 + u * kStep);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t s = s0 + u * kStep;
+        fn(s, order_key(v[u][0]));
+        fn(s + 1, order_key(v[u][1]));
+        fn(s + 2, order_key(v[u][2]));
+        fn(s + 3, order_key(v[u][3]));
+      }
+    }
     const int64_t n4 = n & ~(int64_t)3;
-    for (int64_t s = 4 * (int64_t)tid; s < n4; s += 4 * kTopkThreads) {
+    for (int64_t s = n16 + 4 * (int64_t)tid; s < n4; s += kStep) {
       const v4f v = *(const v4f*)(row + s);
       fn(s, order_key(v[0]));
       fn(s + 1, order_key(v[1]));
@@ -127,6 +158,157 @@ __device__ __forceinline__ void scan_row(const float* __restrict__ row, int64_t 
 // Radix levels: 0 -> key bits 31..20, 1 -> bits 19..8, 2 -> bits 7..0.
 __device__ __forceinline__ int level_shift(int level) { return level == 0 ? 20 : (level == 1 ? 8 : 0); }
 __device__ __forceinline__ int level_bits(int level) { return level == 2 ? 8 : 12; }
+
+// Ordered emit: positions whose gt bit is set, plus the lowest-position
+// (k - #gt) positions whose eq bit is set, in ascending order.
+__device__ __forceinline__ void emit_selection(TopkShared& sh, const uint32_t* gt_bits, const uint32_t* eq_bits,
+                                               int n_words, uint32_t k, int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  // Thread tid owns words [wpt*tid, wpt*tid + wpt) i.e. a contiguous range of positions.
+  const int wpt = (n_words + kTopkThreads - 1) / kTopkThreads;
+  const int w0 = tid * wpt;
+  uint32_t cg = 0, ce = 0;
+  for (int i = 0; i < wpt; ++i) {
+    const int wi = w0 + i;
+    if (wi < n_words) {
+      cg += __popc(gt_bits[wi]);
+      ce += __popc(eq_bits[wi]);
+    }
+  }
+  uint32_t ig = cg, ie = ce, tg, te;
+  block_scan2(sh, &ig, &ie, &tg, &te);
+  const uint32_t r = k - tg;  // ties to take, lowest positions first
+  uint32_t eq_before = ie - ce;
+  uint32_t sel_words[16];
+  uint32_t cs = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int wi = w0 + i;
+    uint32_t g = 0, e = 0;
+    if (i < wpt && wi < n_words) {
+      g = gt_bits[wi];
+      e = eq_bits[wi];
+    }
+    uint32_t keep = 0;
+    while (e && eq_before < r) {
+      const uint32_t lowbit = e & (~e + 1u);
+      keep |= lowbit;
+      e &= e - 1u;
+      ++eq_before;
+    }
+    sel_words[i] = g | keep;
+    cs += __popc(sel_words[i]);
+  }
+  uint32_t is = cs, dummy = 0, ts, td;
+  block_scan2(sh, &is, &dummy, &ts, &td);
+  uint32_t pos = is - cs;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t m = sel_words[i];
+    const int base = (w0 + i) * 32;
+    while (m) {
+      const int b = __ffs(m) - 1;
+      out[pos++] = base + b;
+      m &= m - 1u;
+    }
+  }
+}
+
+// Exact radix selection of the k-th largest of the `nl` keys in sh.list_key
+// whose value lies in [lo, hi] (`above` list keys are larger than hi), from
+// radix level `level` on; leaves lo == hi == that key.
+__device__ __forceinline__ void refine_list(TopkShared& sh, int nl, uint32_t& lo, uint32_t& hi, uint32_t above,
+                                            int level, uint32_t k, const uint32_t* keys) {
+  const int tid = threadIdx.x;
+  for (; level < 3; ++level) {
+    const int sh_ = level_shift(level), nb = 1 << level_bits(level);
+    for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < nl; i += kTopkThreads) {
+      const uint32_t key = keys[i];
+      if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key >> sh_) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_bin(sh, nb, above, k);
+    const uint32_t bin = sh.sel_bin;
+    above = sh.sel_above;
+    const uint32_t span = (sh_ == 0) ? 0u : ((1u << sh_) - 1u);
+    lo = (lo & ~(((uint32_t)(nb - 1)) << sh_)) | (bin << sh_);
+    hi = lo | span;
+    __syncthreads();
+  }
+}
+
+// Sampled path (see the file comment).  Returns false, having written
+// nothing, when the gathered list misses [k, capacity]; the caller then takes
+// the exact path.  Needs a 16-byte aligned row with n >= kSampleMinN; the
+// bitmap area (n_words * 8 bytes >= n / 4 bytes) doubles as the sample buffer.
+__device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __restrict__ row, int64_t n, int32_t k,
+                                             uint32_t* gt_bits, uint32_t* eq_bits, int n_words,
+                                             int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  uint32_t* sample = gt_bits;
+  // sampled chunk j: keys 64*(16*j + (5*j % 16)) .. +63, whole chunks inside the row
+  const int64_t n_chunks = n / 64;
+  const int m_chunks = (int)((n_chunks + kSampleStride - 1) / kSampleStride);
+  int m = 0;  // sampled keys (a multiple of 64, counted by every thread alike)
+  for (int j = 0; j < m_chunks; ++j)
+    if ((int64_t)kSampleStride * j + (5 * j) % kSampleStride < n_chunks) m += 64;
+  for (int f = tid; f < m_chunks * 16; f += kTopkThreads) {
+    const int j = f >> 4;
+    const int64_t chunk = (int64_t)kSampleStride * j + (5 * j) % kSampleStride;
+    if (chunk < n_chunks) {
+      const v4f v = *(const v4f*)(row + 64 * chunk + 4 * (f & 15));
+      // compact slot: chunks are skipped only at the very end, so j-th kept chunk = j
+      uint32_t* dst = sample + 64 * j + 4 * (f & 15);
+      dst[0] = order_key(v[0]);
+      dst[1] = order_key(v[1]);
+      dst[2] = order_key(v[2]);
+      dst[3] = order_key(v[3]);
+    }
+  }
+  __syncthreads();
+  // rank of the estimate within the sample: about 1.37k of the row lie above it
+  const int64_t target = (int64_t)k + (int64_t)k * 3 / 8;
+  int64_t rs = (target * m + n - 1) / n;
+  if (rs < 1) rs = 1;
+  if (rs > m) rs = m;
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
+  refine_list(sh, m, lo, hi, 0u, 0, (uint32_t)rs, sample);
+  const uint32_t t_est = lo;
+
+  if (tid == 0) sh.list_n = 0;
+  __syncthreads();
+  scan_row(row, n, true, [&](int64_t s, uint32_t key) {
+    if (key >= t_est) {
+      const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+      if (slot < (uint32_t)kTopkCap) {
+        sh.list_key[slot] = key;
+        sh.list_idx[slot] = (int32_t)s;
+      }
+    }
+  });
+  __syncthreads();
+  const uint32_t c = sh.list_n;
+  if (c < (uint32_t)k || c > (uint32_t)kTopkCap) return false;  // uniform across the workgroup
+
+  lo = 0u;
+  hi = 0xFFFFFFFFu;
+  refine_list(sh, (int)c, lo, hi, 0u, 0, (uint32_t)k, sh.list_key);
+  for (int i = tid; i < 2 * n_words; i += kTopkThreads) gt_bits[i] = 0;  // gt and eq maps are adjacent
+  __syncthreads();
+  for (int i = tid; i < (int)c; i += kTopkThreads) {
+    const uint32_t key = sh.list_key[i];
+    const int32_t s = sh.list_idx[i];
+    if (key > hi)
+      atomicOr(&gt_bits[s >> 5], 1u << (s & 31));
+    else if (key == hi)
+      atomicOr(&eq_bits[s >> 5], 1u << (s & 31));
+  }
+  __syncthreads();
+  emit_selection(sh, gt_bits, eq_bits, n_words, (uint32_t)k, out);
+  return true;
+}
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t ld,
                                                              int64_t T, int64_t N, int64_t q_pos0,
@@ -148,6 +330,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
   const float* row = scores + t * ld;
   const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
+  if (vec && n >= kSampleMinN && topk_sampled(sh, row, n, k, gt_bits, eq_bits, n_words, out)) return;
 
   // ------------------------------------------------------------ global refinement
   // Current candidate key range [lo, hi]; `above` keys are > hi.
@@ -195,23 +378,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   // ------------------------------------------------------------ LDS refinement
   if (!exact) {
     const int nl = (int)sh.list_n;
-    for (; level < 3; ++level) {
-      const int sh_ = level_shift(level), nb = 1 << level_bits(level);
-      for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < nl; i += kTopkThreads) {
-        const uint32_t key = sh.list_key[i];
-        if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key >> sh_) & (nb - 1)], 1u);
-      }
-      __syncthreads();
-      find_bin(sh, nb, above, (uint32_t)k);
-      const uint32_t bin = sh.sel_bin;
-      above = sh.sel_above;
-      const uint32_t span = (sh_ == 0) ? 0u : ((1u << sh_) - 1u);
-      lo = (lo & ~(((uint32_t)(nb - 1)) << sh_)) | (bin << sh_);
-      hi = lo | span;
-      __syncthreads();
-    }
+    refine_list(sh, nl, lo, hi, above, level, (uint32_t)k, sh.list_key);
     // lo == hi == theta: mark list entries
     for (int i = tid; i < nl; i += kTopkThreads) {
       const uint32_t key = sh.list_key[i];
@@ -224,67 +391,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     __syncthreads();
   }
 
-  // ------------------------------------------------------------ ordered emit
-  // Thread tid owns words [wpt*tid, wpt*tid + wpt) i.e. a contiguous range of positions.
-  const int wpt = (n_words + kTopkThreads - 1) / kTopkThreads;
-  const int w0 = tid * wpt;
-  uint32_t cg = 0, ce = 0;
-  for (int i = 0; i < wpt; ++i) {
-    const int wi = w0 + i;
-    if (wi < n_words) {
-      cg += __popc(gt_bits[wi]);
-      ce += __popc(eq_bits[wi]);
-    }
-  }
-  uint32_t ig = cg, ie = ce, tg, te;
-  block_scan2(sh, &ig, &ie, &tg, &te);
-  const uint32_t r = (uint32_t)k - tg;  // ties to take, lowest positions first
-  uint32_t eq_before = ie - ce;
-  uint32_t sel_words[16];
-  uint32_t cs = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int wi = w0 + i;
-    uint32_t g = 0, e = 0;
-    if (i < wpt && wi < n_words) {
-      g = gt_bits[wi];
-      e = eq_bits[wi];
-    }
-    uint32_t keep = 0;
-    while (e && eq_before < r) {
-      const uint32_t lowbit = e & (~e + 1u);
-      keep |= lowbit;
-      e &= e - 1u;
-      ++eq_before;
-    }
-    sel_words[i] = g | keep;
-    cs += __popc(sel_words[i]);
-  }
-  uint32_t is = cs, dummy = 0, ts, td;
-  block_scan2(sh, &is, &dummy, &ts, &td);
-  uint32_t pos = is - cs;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t m = sel_words[i];
-    const int base = (w0 + i) * 32;
-    while (m) {
-      const int b = __ffs(m) - 1;
-      out[pos++] = base + b;
-      m &= m - 1u;
-    }
-  }
+  emit_selection(sh, gt_bits, eq_bits, n_words, (uint32_t)k, out);
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0,
                        const int32_t* n_valid, int32_t k, int32_t* idx, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const int32_t n_words = (int32_t)((N + 31) / 32);
-  const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words;
+  // bitmaps (2 x n_words words) + 256 bytes: the sampled path's key sample
+  // (at most n/4 + 240 bytes) reuses the bitmap area
+  const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words + 256;
   static bool attr_set = false;
   if (!attr_set) {
     // rows up to 262144 keys: fixed state + 64 KiB of bitmaps
     hipError_t e = hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192));
+                                       (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192 + 256));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
