@@ -53,15 +53,20 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f c) {
 // ------------------------------------------------------------------ addressing
 // Row index (into a [rows, dim] array) of token s of sequence b, or -1 when
 // the token has no backing row.
+// group_row(b, g): row of token g of a 64-aligned group g .. g+63 whose tokens
+// sit in consecutive rows (true for every layout here, pages being 64 tokens),
+// or -1 when the group has no backing rows.
 struct AddrSingle {  // one contiguous sequence of n rows
   int64_t n;
   __device__ __forceinline__ int64_t row(int64_t /*b*/, int64_t s) const { return (s >= 0 && s < n) ? s : -1; }
+  __device__ __forceinline__ int64_t group_row(int64_t b, int64_t g) const { return row(b, g); }
 };
 struct AddrBatched {  // [B, stride] contiguous sequences
   int64_t stride;
   __device__ __forceinline__ int64_t row(int64_t b, int64_t s) const {
     return (s >= 0 && s < stride) ? b * stride + s : -1;
   }
+  __device__ __forceinline__ int64_t group_row(int64_t b, int64_t g) const { return row(b, g); }
 };
 struct AddrPaged {  // pool of pages addressed through a page table
   const int32_t* page_table;
@@ -76,6 +81,7 @@ struct AddrPaged {  // pool of pages addressed through a page table
     if (p < 0 || p >= n_pages) return -1;
     return ((int64_t)p << page_shift) + (s & ((1 << page_shift) - 1));
   }
+  __device__ __forceinline__ int64_t group_row(int64_t b, int64_t g) const { return row(b, g); }
 };
 
 // ------------------------------------------------------------------ top-k keys

@@ -217,6 +217,10 @@ __global__ __launch_bounds__(64 * NW, 1) void indexer_prefill_kernel(
 // ---------------------------------------------------------------- decode
 // Workgroup = one query (sequence b = grid.y) and one chunk of `key_chunk`
 // keys; the 4 waves take interleaved 64-key groups, loading each key once.
+// The FP8 keys stream straight from HBM into registers, software pipelined:
+// the row of group i+2 is resolved (one page lookup per 64-key group, which
+// always lies in one page) and the keys of group i+1 are loaded while group
+// i is on the matrix cores.
 template <int NT, class Addr>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __restrict__ q_idx,
                                                              const float* __restrict__ w,
@@ -238,19 +242,21 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
   float wr[NT][4];
   load_query<NT>(q_idx, w, b, true, H_I, col, grp, a, wr);
 
-  for (int64_t kg = c0 + 64 * wave; kg < c_end; kg += 256) {
-    const int64_t s = kg + lane;
-    if (kg >= n) {
-      if (s < c_end) scores[b * ld + s] = -INFINITY;
-      continue;
-    }
-    v4i raw[4][2];
+  // groups of this wave: kg(i) = c0 + 64*wave + 256*i
+  const int64_t kg0 = c0 + 64 * wave;
+  const int ng = kg0 < c_end ? (int)((c_end - kg0 + 255) / 256) : 0;
+  auto kg_of = [&](int i) { return kg0 + 256 * (int64_t)i; };
+  auto base_of = [&](int i) -> int64_t {
+    const int64_t kg = kg_of(i);
+    return (i < ng && kg < n) ? addr.group_row(b, kg) : -1;
+  };
+  auto load = [&](int i, int64_t base, v4i (&raw)[4][2]) {
+    const int64_t kg = kg_of(i);
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      const int64_t sk = kg + 16 * blk + col;
-      const int64_t row = sk < n ? addr.row(b, sk) : -1;
-      if (row >= 0) {
-        const v4i* p = (const v4i*)(keys + row * kIdxD + 32 * grp);
+      const int j = 16 * blk + col;
+      if (base >= 0 && kg + j < n) {
+        const v4i* p = (const v4i*)(keys + (base + j) * kIdxD + 32 * grp);
         raw[blk][0] = p[0];
         raw[blk][1] = p[1];
       } else {
@@ -258,14 +264,29 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
         raw[blk][1] = raw[blk][0];
       }
     }
+  };
+  auto finish = [&](int i, int64_t base, const v4i (&raw)[4][2]) {
+    const int64_t s = kg_of(i) + lane;
     float part[4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) part[blk] = head_sum<NT>(a, wr, widen32(raw[blk][0], raw[blk][1]));
     const float v = group_transpose_reduce(part[0], part[1], part[2], part[3], grp);
-    if (s < c_end) {
-      const bool cand = s < n && addr.row(b, s) >= 0;
-      scores[b * ld + s] = cand ? v : -INFINITY;
-    }
+    if (s < c_end) scores[b * ld + s] = (s < n && base >= 0) ? v : -INFINITY;
+  };
+
+  v4i ra[4][2], rb[4][2];
+  int64_t base_a = base_of(0), base_b = base_of(1), base_c;
+  load(0, base_a, ra);
+  for (int i = 0; i < ng; i += 2) {
+    base_c = base_of(i + 2);
+    if (i + 1 < ng) load(i + 1, base_b, rb);
+    finish(i, base_a, ra);
+    if (i + 1 >= ng) break;
+    base_a = base_c;
+    base_c = base_of(i + 3);
+    if (i + 2 < ng) load(i + 2, base_a, ra);
+    finish(i + 1, base_b, rb);
+    base_b = base_c;
   }
 }
 
@@ -274,7 +295,7 @@ namespace {
 constexpr int kPrefillNW = 4;
 constexpr int kPrefillQW = 1;
 constexpr int kPrefillChunk = 8192;
-constexpr int kDecodeChunk = 1024;
+constexpr int kDecodeChunk = 4096;  // keys per decode workgroup: 16 groups of 64 per wave
 
 template <int NT>
 hipError_t prefill_nt(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
