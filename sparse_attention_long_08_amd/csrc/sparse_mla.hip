@@ -8,11 +8,10 @@
 //   out[t,h] = sum_s softmax(z)_s * kv[s,:512],  lse[t,h] = ln sum_s exp(z_s)
 //
 // Mapping.  One workgroup of 4 waves owns one query (or one split of its
-// entries); wave w owns heads 32w .. 32w+31 as two 16-head MFMA tiles, keeps
-// their query rows in registers (the B operand of the logit product) and
-// their fp32 output accumulators O^T (512 x 32) in accumulation registers.
-// Every operand read from LDS feeds both head tiles, so the LDS bytes per
-// flop are those of a 32-head tile.
+// entries); wave w owns heads 32w .. 32w+31 as the N side of 32x32x16 MFMAs.
+// It keeps the query rows of its heads in registers (the B operand of the
+// logit product S^T = K Q^T, 32 keys x 32 heads per block) and the fp32
+// output O^T (512 x 32, sixteen 32x32 tiles) in the accumulation registers.
 //
 // Data movement.  Selected latent rows are gathered 32 at a time straight
 // from HBM into LDS with the global->LDS DMA (16 bytes per lane, no staging
@@ -20,24 +19,27 @@
 // (4 KB) holds 16-byte chunks 8b .. 8b+7 of all 32 rows, 128 bytes per row,
 // with an XOR swizzle of the chunk slot by row.  One DMA instruction then
 // moves one band of eight rows, so a wave gathers its eight rows with one
-// row lookup, one address and nine DMAs.  The logits S^T = K Q^T read rows
-// of a stage; the value product O^T = V^T P^T reads the same bytes
-// transposed with ds_read_b64_tr_b16, so one copy serves both.
+// row lookup, one address and nine DMAs.  The logit product reads rows of a
+// stage; the value product O^T = V^T P^T reads the same bytes transposed
+// with ds_read_b64_tr_b16, so one copy serves both.
 //
-// Schedule.  Keys sit on the MFMA rows, so each lane owns single heads and
-// the softmax statistics are per-lane scalars.  The loop is software
-// pipelined by one block: step b issues the value MFMAs of block b and the
-// logit MFMAs of block b+1 interleaved (operand reads a few slots ahead),
-// then the softmax of block b+1.  Probabilities are taken against a fixed
-// reference max per head (the max of its first block with a valid key), so
-// O is never rescaled inside the loop; if a later block max exceeds the
-// reference by more than 2^64 the query is recomputed with the true max,
-// which the first pass tracked.  The gather uses the buffer-addressed form of
-// the DMA when the latent cache spans less than 4 GiB.
+// Schedule.  Keys sit on the MFMA rows, so each lane owns one head and the
+// softmax statistics are per-lane scalars.  The loop is software pipelined
+// by one block: step b runs the logit MFMAs of block b+1 with the softmax of
+// block b spread between them, then the value MFMAs of block b.  Operand
+// tiles are read from LDS a fixed number of tiles ahead of their MFMA.
+// Probabilities are taken against a fixed reference max per head (the max
+// of its first block with a valid key), so O is never rescaled inside the
+// loop; if a later block max exceeds the reference by more than 2^64 the
+// query is recomputed with the true max, which the first pass tracked.  The
+// gather uses the buffer-addressed form of the DMA when the latent cache
+// spans less than 4 GiB.
 //
 // Small batches (decode) split each query's k entries over several
 // workgroups; partial (out, lse) pairs are merged exactly by combine_kernel:
 // lse = ln sum_i e^{lse_i}, out = sum_i e^{lse_i - lse} out_i.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -50,24 +52,88 @@ constexpr int kBufBytes = kBlk * kDqk * 2;   // 36864 bytes per stage
 constexpr int kBand = 4096;                  // bytes per 8-chunk band of a stage
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kHeadsPerWave = 32;            // two 16-head MFMA tiles
+constexpr int kHeadsPerWave = 32;            // the N side of a 32x32x16 MFMA
 constexpr int kDmaPerWave = 9;               // one DMA per band, eight rows per wave
-constexpr int kQReg = 16;                    // query k-steps held in registers (the 512 latent dims)
-constexpr int kQTail = 18 - kQReg;           // query k-steps parked in LDS (the 64 rope dims)
+constexpr int kKSteps = kDqk / 16;           // 36 k-steps of the logit product
+constexpr int kQReg = 28;                    // query k-steps held in registers
+constexpr int kQTail = kKSteps - kQReg;      // query k-steps parked in LDS
+constexpr int kCt = kDv / 32;                // 16 output tiles of 32 latent dims
 constexpr int kMaxK = 4096;                  // entries per query the row table holds
-constexpr int kPfS = 1;                      // logit operand reads issued this many slots ahead
-constexpr int kPfP = 3;                      // value operand reads issued this many slots ahead
+constexpr int kAhead = 6;                    // operand tiles in flight ahead of the one consumed
+
+// ---- the operand stream of one pipeline step.  Slots 0..35 are the logit
+// product of the next block (slot i: k-step s_slot_ks(i)), slots 36..67 the
+// value product of the current block (slot 36+j: output tile j/2, key half
+// j%2).  A slot consumes one "unit" of four registers read from LDS: a key
+// tile (one 16-byte read per lane) or a value tile (two 8-byte transposed
+// reads); a slot on a query k-step parked in LDS also consumes that query
+// tile.  Unit k is read kAhead units before it is consumed.
+constexpr int kSSlots = kKSteps;
+constexpr int kSlots = kSSlots + 2 * kCt;
+constexpr int s_slot_ks(int i) { return i < kQTail ? kQReg + i : i - kQTail; }
+constexpr bool slot_loads_q(int i) { return i < kQTail; }
+constexpr int slot_units(int i) { return slot_loads_q(i) ? 2 : 1; }
+constexpr int slot_first_unit(int i) {
+  int u = 0;
+  for (int s = 0; s < i; ++s) u += slot_units(s);
+  return u;
+}
+constexpr int kUnits = slot_first_unit(kSlots);
+struct UnitDesc {
+  int kind;  // 0: key tile of k-step a; 1: query tile of k-step a; 2: value tile (ct a, key half b)
+  int a, b;
+};
+constexpr UnitDesc unit_desc(int k) {
+  for (int s = 0; s < kSlots; ++s) {
+    const int f = slot_first_unit(s);
+    if (k < f || k >= f + slot_units(s)) continue;
+    if (s >= kSSlots) return {2, (s - kSSlots) >> 1, (s - kSSlots) & 1};
+    if (slot_loads_q(s) && k == f) return {1, s_slot_ks(s), 0};
+    return {0, s_slot_ks(s), 0};
+  }
+  return {-1, 0, 0};
+}
+constexpr int unit_reads(int k) { return unit_desc(k).kind == 2 ? 2 : 1; }
+constexpr int reads_in(int lo, int hi) {
+  int n = 0;
+  for (int k = lo; k < hi; ++k) n += unit_reads(k);
+  return n;
+}
+constexpr int imin(int a, int b) { return a < b ? a : b; }
+// units issued before slot 0, and in slot i (before its MFMAs)
+constexpr int issue_lo(int i) { return i == 0 ? kAhead : imin(slot_first_unit(i) + kAhead, kUnits); }
+constexpr int issue_hi(int i) { return imin(slot_first_unit(i + 1) + kAhead, kUnits); }
+// every unit is read in an earlier slot than the one consuming it
+static_assert(kAhead >= 2, "a slot consumes up to two units");
 
 typedef short v4s __attribute__((ext_vector_type(4)));
-typedef float v8f __attribute__((ext_vector_type(8)));
 typedef short v8s_t __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) uint8_t* lds_u8_ptr;
 
+// Calls f(integral_constant<int, I>) for I = B .. E-1, each as its own
+// straight-line code with I a compile-time constant.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // XOR swizzle of the chunk slot within a 128-byte band row: the rows read
 // together by an operand load land on distinct banks.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 7; }
+
+// O^T tile += V^T tile * P^T with the accumulator pinned to the accumulation
+// registers (the compiler would otherwise shuttle the 256 accumulators
+// between register files around the VALU work of the loop).
+__device__ __forceinline__ void mfma_acc_32x32x16(v16f& acc, v8bf a, v8bf b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
 
 struct MlaParams {
   const uint16_t* q;
@@ -108,10 +174,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   __shared__ __attribute__((aligned(16))) uint8_t kb0[kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t kb1[kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t kb2[kBufBytes];
-  __shared__ v8bf qtail[kQTail * 2 * kWaves * 64];  // query steps kQReg..17 of every head tile
-  __shared__ int32_t rows[kMaxK];                      // latent row of every entry (-1: skipped)
+  __shared__ v8bf qtail[kQTail * kWaves * 64];  // query k-steps kQReg..35 of every wave
+  __shared__ int32_t rows[kMaxK];                 // latent row of every entry (-1: skipped)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g4 = lane >> 4, hl = lane & 15;
+  const int hn = lane & 31, hh = lane >> 5;  // MFMA column (head) and k-half of this lane
   const int64_t t = blockIdx.x / p.n_split;
   const int sp = blockIdx.x % p.n_split;
   const int j0 = sp * p.per_split;
@@ -135,29 +201,29 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
     rows[e] = row;
   }
 
-  // ---- query rows of this wave's head tiles: step st covers dims
-  // 32*st + 8*g4 .. +7.  Lanes past the last head read head H-1 and zero it.
-  v8bf qf[2][kQReg];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int head = kHeadsPerWave * wave + 16 * nt + hl;
+  // ---- query rows of this wave's heads in the B layout of the logit
+  // MFMA: k-step ks of lane (head hn, half hh) is dims 16*ks + 8*hh .. +7.
+  // Lanes past the last head read head H-1 and zero it.
+  v8bf qf[kQReg];
+  {
+    const int head = kHeadsPerWave * wave + hn;
     const bool hv = head < p.H;
-    const uint16_t* qrow = p.q + (t * p.H + (hv ? head : p.H - 1)) * (int64_t)kDqk + 8 * g4;
+    const uint16_t* qrow = p.q + (t * p.H + (hv ? head : p.H - 1)) * (int64_t)kDqk + 8 * hh;
 #pragma unroll
-    for (int st = 0; st < kQReg; ++st) {
-      const v8bf v = *(const v8bf*)(qrow + 32 * st);
-      qf[nt][st] = hv ? v : (v8bf){};
+    for (int ks = 0; ks < kQReg; ++ks) {
+      const v8bf v = *(const v8bf*)(qrow + 16 * ks);
+      qf[ks] = hv ? v : (v8bf){};
     }
 #pragma unroll
-    for (int st = kQReg; st < 18; ++st) {
-      const v8bf v = *(const v8bf*)(qrow + 32 * st);
-      qtail[(((st - kQReg) * 2 + nt) * kWaves + wave) * 64 + lane] = hv ? v : (v8bf){};
+    for (int ks = kQReg; ks < kKSteps; ++ks) {
+      const v8bf v = *(const v8bf*)(qrow + 16 * ks);
+      qtail[((ks - kQReg) * kWaves + wave) * 64 + lane] = hv ? v : (v8bf){};
     }
   }
   __syncthreads();
 
-  // Gather block `blk` into stage `base`: this wave moves rows 8w .. 8w+7,
-  // one DMA per band; lane L carries row 8w + L/8, chunk slot L%8 of the band.
+  // Gather one block into stage `base`: this wave moves rows 8w .. 8w+7, one
+  // DMA per band; lane L carries row 8w + L/8, chunk slot L%8 of the band.
   const int g_row = 8 * wave + (lane >> 3);
   const int g_chunk = (lane & 7) ^ swz(g_row);
   // Buffer-addressed DMA when the latent cache spans less than 4 GiB (the
@@ -165,8 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   // counting exact, so operand prefetches are not flushed by every gather.
   const __amdgpu_buffer_rsrc_t kv_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)0, (int)p.kv_bytes, 0x00020000);
-  auto gather = [&](uint8_t* base, int blk) {
-    int32_t row = rows[blk * kBlk + g_row];
+  auto gather = [&](uint8_t* base, int32_t row) {
     row = row < 0 ? 0 : row;  // skipped entries read row 0 (masked later)
     if constexpr (kBufDma) {
       const uint32_t voff = (uint32_t)row * (kDqk * 2) + 16 * g_chunk;
@@ -184,75 +249,64 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   };
 
   // ---- per-lane LDS byte offsets of the operand reads (the rest are
-  // compile-time immediates).  Logits: M-tile mt reads key row 16*mt + hl,
-  // chunk 4*st + g4, i.e. band st/2, band slot 4*(st%2) + g4.
-  uint32_t s_addr[2][2];
+  // compile-time immediates).  Key tile of k-step ks: lane (row hn, half hh)
+  // reads chunk 2*ks + hh of its row = band ks/4, slot 2*(ks%4) + hh.
+  uint32_t k_addr[4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int r = 16 * mt + hl;
-#pragma unroll
-    for (int par = 0; par < 2; ++par) s_addr[mt][par] = (uint32_t)(r * 128 + (((4 * par + g4) ^ swz(r)) << 4));
-  }
-  // Values: for c'-tile ct, lane (g4, 4*rq + qq) supplies columns
-  // 16*ct + 4*qq .. +3 of key rows 4*g4 + rq (k-slots 0..3) and
-  // 16 + 4*g4 + rq (k-slots 4..7): chunk 2*ct + qq/2 = band ct/4, slot
-  // 2*(ct%4) + qq/2, byte 8*(qq%2) within the chunk.
-  uint32_t v_addr[2][4];
+  for (int q = 0; q < 4; ++q) k_addr[q] = (uint32_t)(hn * 128 + (((2 * q + hh) ^ swz(hn)) << 4));
+  // Value tile (ct, kt), read hr: the A operand of lane (column c' = 32*ct +
+  // hn, half hh) holds keys 16*kt + 8*hr + 4*hh + 0..3.  ds_read_b64_tr_b16
+  // hands lane i of a 16-lane group column i of the 4 x 16 block whose rows
+  // lane 4*rho + q addresses at columns 4*q .. 4*q+3: lane (group G, rho, q)
+  // reads row 16*kt + 8*hr + 4*(G/2) + rho, columns 32*ct + 16*(G%2) + 4*q,
+  // i.e. band ct/2, chunk slot 4*(ct%2) + 2*(G%2) + q/2, byte 8*(q%2).  The
+  // swizzle of that row is swz(4*(G/2) + rho) ^ 4*kt ^ 2*hr, so the slot is
+  // a per-lane base XOR a compile-time mask m = 4*((ct%2)^kt) + 2*hr.
+  uint32_t v_addr[4];
   {
-    const int rq = hl >> 2, qq = hl & 3;
+    const int grp = lane >> 4, rho = (lane >> 2) & 3, q = lane & 3;
+    const int r0 = 4 * (grp >> 1) + rho;
+    const int s0 = (2 * (grp & 1) + (q >> 1)) ^ swz(r0);
 #pragma unroll
-    for (int hv = 0; hv < 2; ++hv) {
-      const int r = 16 * hv + 4 * g4 + rq;
-#pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4)
-        v_addr[hv][m4] = (uint32_t)(r * 128 + (((2 * m4 + (qq >> 1)) ^ swz(r)) << 4) + 8 * (qq & 1));
-    }
+    for (int m = 0; m < 4; ++m) v_addr[m] = (uint32_t)(r0 * 128 + ((s0 ^ (2 * m)) << 4) + 8 * (q & 1));
   }
 
-  v4f o[2][32];
-  float m_ref[2] = {-INFINITY, -INFINITY};  // reference max of each head (log2 units)
-  float m_max[2] = {-INFINITY, -INFINITY};  // largest block max seen
-  float l_run[2];
-  bool over = false;                         // a logit exceeded its reference by more than 2^64
-  v8bf pb[2];                                // probabilities of the block whose value product is next
-  v4f sacc[2][2];
+  v16f o[kCt];
+  float m_ref = -INFINITY;  // reference max of this lane's head (log2 units)
+  float m_max = -INFINITY;  // largest block max seen
+  float l_run;
+  bool over = false;        // a logit exceeded its reference by more than 2^64
+  uint32_t pbw[2][4];       // bf16 probabilities of the block whose value product is next
+  v16f sacc;                // logits of the block whose softmax is next
 
-  auto read_a = [&](const lds_u8_ptr base, int st, int mt) {
-    return *(const __attribute__((address_space(3))) v8bf*)(base + s_addr[mt][st & 1] + kBand * (st >> 1));
+  auto read_k = [&](const lds_u8_ptr base, int ks) {
+    return *(const __attribute__((address_space(3))) v8bf*)(base + k_addr[ks & 3] + kBand * (ks >> 2));
   };
-  auto read_q = [&](int st, int nt) {
-    return st < kQReg ? qf[nt][st < kQReg ? st : 0]
-                      : qtail[(((st < kQReg ? 0 : st - kQReg) * 2 + nt) * kWaves + wave) * 64 + lane];
+  auto read_q = [&](int ks) {
+    return ks < kQReg ? qf[ks < kQReg ? ks : 0] : qtail[((ks < kQReg ? 0 : ks - kQReg) * kWaves + wave) * 64 + lane];
   };
-  auto read_v = [&](const lds_u8_ptr base, int ct) {
-    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + v_addr[0][ct & 3] + kBand * (ct >> 2)));
-    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + v_addr[1][ct & 3] + kBand * (ct >> 2)));
+  auto read_v = [&](const lds_u8_ptr base, int ct, int kt) {
+    const uint32_t off = kBand * (ct >> 1) + 2048 * kt;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + v_addr[2 * ((ct & 1) ^ kt)] + off));
+    const v4s hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + v_addr[2 * ((ct & 1) ^ kt) + 1] + off + 1024));
     return __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   };
 
   // Logits of one block alone (first block of the pipeline).
   auto logits = [&](const lds_u8_ptr base) {
+    constexpr int kPf = 3;  // key-tile reads in flight
+    v16f acc = {};
+    v8bf abuf[kPf + 1];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int ks = 0; ks < kPf; ++ks) abuf[ks] = read_k(base, ks);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
-    v8bf abuf[kPfS + 1][2];
-#pragma unroll
-    for (int st = 0; st < kPfS; ++st)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) abuf[st][mt] = read_a(base, st, mt);
-#pragma unroll
-    for (int st = 0; st < 18; ++st) {
-      if (st + kPfS < 18)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) abuf[(st + kPfS) % (kPfS + 1)][mt] = read_a(base, st + kPfS, mt);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          sacc[mt][nt] = mfma_bf16_16x16x32(abuf[st % (kPfS + 1)][mt], read_q(st, nt), sacc[mt][nt]);
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (ks + kPf < kKSteps) abuf[(ks + kPf) % (kPf + 1)] = read_k(base, ks + kPf);
+      acc = mfma_bf16_32x32x16(abuf[ks % (kPf + 1)], read_q(ks), acc);
       __builtin_amdgcn_sched_barrier(0);
     }
+    sacc = acc;
   };
 
   // Softmax of the block in sacc (validity bits in `valid`), against a fixed
@@ -260,41 +314,49 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   // m_ref is the max of the head's first block with a valid key (until then
   // nothing has been accumulated, so setting it changes nothing).  A later
   // block max more than 64 above m_ref flags the query; it is then redone with
-  // m_ref = the true max, which keeps every p <= 1.  lane: heads (nt, hl);
-  // sacc[mt][nt][i] is key 16*mt + 4*g4 + i of the block.
-  auto softmax = [&](uint32_t valid) {
+  // m_ref = the true max, which keeps every p <= 1.  Lane (head hn, half hh)
+  // holds keys 8*(r/4) + 4*hh + r%4 of the block in sacc[r].
+  //
+  // The work is cut into pieces issued one per logit MFMA of the next block,
+  // so the VALU and the matrix cores overlap: piece c runs after slot c.
+  // Probabilities overwrite sacc; their sum is taken after pb is formed.
+  float sm_m = 0.f, sm_neg = 0.f;
+  auto sm_piece = [&](auto cc, uint32_t valid) {
+    constexpr int c = decltype(cc)::value;
+    if constexpr (c == 0) {
+      if (valid != 0xFFFFFFFFu) {  // uniform: only partial blocks pay for the mask
+        const uint32_t lv = valid >> (4 * hh);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mloc = -INFINITY;
+        for (int r = 0; r < 16; ++r)
+          sacc[r] = ((lv >> (8 * (r >> 2) + (r & 3))) & 1) ? sacc[r] : -INFINITY;
+      }
+    } else if constexpr (c == 1) {
+      float m = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * mt + 4 * g4 + i;
-          sacc[mt][nt][i] = ((valid >> key) & 1) ? sacc[mt][nt][i] : -INFINITY;
-          mloc = fmaxf(mloc, sacc[mt][nt][i]);
-        }
-      mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-      mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-      mloc *= p.scale_log2;  // scale > 0 keeps the order
-      m_max[nt] = fmaxf(m_max[nt], mloc);
-      if (m_ref[nt] == -INFINITY) m_ref[nt] = mloc;
-      over |= mloc > m_ref[nt] + 64.0f;
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[r]);
+      sm_m = m;
+    } else if constexpr (c == 2) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm_m), __float_as_uint(sm_m), false, false);
+      sm_m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    } else if constexpr (c == 3) {
+      const float mloc = sm_m * p.scale_log2;  // scale > 0 keeps the order
+      m_max = fmaxf(m_max, mloc);
+      if (m_ref == -INFINITY) m_ref = mloc;
+      over |= mloc > m_ref + 64.0f;
       // masked keys: fma(-inf, s, -m) = -inf -> 2^-inf = 0; while m_ref is
       // -inf every logit is -inf, so the bias is 0
-      const float mneg = (m_ref[nt] == -INFINITY) ? 0.f : -m_ref[nt];
-      v8f pf;
-      float lsum = 0.f;
+      sm_neg = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    } else if constexpr (c >= 4 && c < 20) {
+      sacc[c - 4] = __builtin_amdgcn_exp2f(fmaf(sacc[c - 4], p.scale_log2, sm_neg));
+    } else if constexpr (c >= 20 && c < 24) {
+      // B operand of the value MFMA for key half kt: k-slot 8*hh + j is key
+      // 16*kt + 8*(j/4) + 4*hh + j%4, i.e. this lane's sacc[8*kt + j]
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 2][nt][i & 3], p.scale_log2, mneg));
-        lsum += pv;
-        pf[i] = pv;
-      }
-      l_run[nt] += lsum;
-      // B operand of the value MFMA: k-slot 8*g4 + j <-> key 4*g4 + j (j < 4),
-      // 16 + 4*g4 + (j - 4) (j >= 4): exactly this lane's probabilities
-      pb[nt] = __builtin_convertvector(pf, v8bf);
+      for (int w = 2 * (c - 20); w < 2 * (c - 20) + 2; ++w)
+        pbw[w >> 2][w & 3] = __builtin_bit_cast(
+            uint32_t, __builtin_convertvector((v2f){sacc[2 * w], sacc[2 * w + 1]}, v2bf));
+    } else if constexpr (c >= 24 && c < 32) {
+      l_run += sacc[2 * (c - 24)] + sacc[2 * (c - 24) + 1];
     }
   };
 
@@ -302,87 +364,82 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
     return (uint32_t)(__ballot(rows[blk * kBlk + (lane & 31)] >= 0) & 0xFFFFFFFFull);
   };
 
+  // Row-table values the next step needs, read one step early so that no
+  // LDS wait sits between a barrier and the first operand reads: the row
+  // this lane gathers for block blk+2, and the entry behind the validity bit
+  // of block blk+1 (indexes clamped into the table; values past the last
+  // block are never used).
+  int32_t g_next = 0, v_next = 0;
+  auto read_meta = [&](int blk) {
+    g_next = rows[imin((blk + 2) * kBlk + g_row, kMaxK - 1)];
+    v_next = rows[imin((blk + 1) * kBlk + (lane & 31), kMaxK - 1)];
+  };
+
   // One pipeline step: wait for this wave's DMA of block blk+1, barrier
   // (every wave's DMA of blk+1 landed and stage (blk+2)%3 -- last read by
   // the value product of blk-1 -- is free), launch the DMA of blk+2 into it,
-  // then value product of blk interleaved with the logits of blk+1, and the
-  // softmax of blk+1.  s_barrier is used bare: a fenced __syncthreads()
-  // would also wait for the DMA just issued.
+  // then 68 MFMA slots: 36 of the logit product of blk+1 with the softmax of
+  // blk (whose logits the previous step left in sacc) spread over them, then
+  // 32 of the value product of blk.  s_barrier is used bare: a fenced
+  // __syncthreads() would also wait for the DMA just issued.
+  uint32_t valid_cur = 0;
   auto step = [&](uint8_t* cur, uint8_t* nxt, uint8_t* nx2, int blk) {
     const bool more = blk + 1 < nb;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    if (blk + 2 < nb) gather(nx2, blk + 2);
-    const uint32_t valid_next = block_valid(more ? blk + 1 : blk);
     const lds_u8_ptr vb = (lds_u8_ptr)cur;
     const lds_u8_ptr kb = (lds_u8_ptr)nxt;
-    // 36 slots: slot i issues the logit MFMAs of one (k-step, M-tile) pair
-    // of block blk+1 and, for i < 32, the value MFMAs of c'-tile i of block
-    // blk.  The logit k-steps run in the order 16, 17, 0, 1, .., 15 so the
-    // two query steps parked in LDS are read with the initial prefetch.  Each
-    // slot first issues the LDS reads of slot i + PF, then its four MFMAs.
-    // On the last block the logits read a stale stage and are discarded.
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
-    auto slot_st = [](int i) { return (i >> 1) < kQTail ? kQReg + (i >> 1) : (i >> 1) - kQTail; };
-    v8bf qt[kQTail][2];
-#pragma unroll
-    for (int j = 0; j < kQTail; ++j)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) qt[j][nt] = read_q(kQReg + j, nt);
-    v8bf abuf[kPfS + 1];
-    v8bf vbuf[kPfP + 1];
-#pragma unroll
-    for (int i = 0; i < kPfS; ++i) abuf[i] = read_a(kb, slot_st(i), i & 1);
-#pragma unroll
-    for (int i = 0; i < kPfP; ++i) vbuf[i] = read_v(vb, i);
-#pragma unroll
-    for (int i = 0; i < 36; ++i) {
-      int nreads = 0;
-      if (i + kPfS < 36) {
-        abuf[(i + kPfS) % (kPfS + 1)] = read_a(kb, slot_st(i + kPfS), (i + kPfS) & 1);
-        nreads += 1;
+    v8bf u[kUnits];
+    auto issue = [&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr UnitDesc d = unit_desc(k);
+      if constexpr (d.kind == 0)
+        u[k] = read_k(kb, d.a);
+      else if constexpr (d.kind == 1)
+        u[k] = read_q(d.a);
+      else
+        u[k] = read_v(vb, d.a, d.b);
+    };
+    static_for<0, kAhead>(issue);
+    const int32_t grow = g_next;
+    const uint32_t valid_now = valid_cur;
+    valid_cur = more ? (uint32_t)(__ballot(v_next >= 0) & 0xFFFFFFFFull) : 0u;
+    read_meta(blk + 1);
+    if (blk + 2 < nb) gather(nx2, grow);
+    v16f snx = {};
+    // Each slot first issues the LDS reads of later units, then its MFMA,
+    // then its softmax piece.  On the last block the logits read a stale
+    // stage and are discarded.
+    static_for<0, kSlots>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int f = slot_first_unit(i);
+      static_for<issue_lo(i), issue_hi(i)>(issue);
+      if constexpr (i < kSSlots) {
+        constexpr int ks = s_slot_ks(i);
+        const v8bf qb = ks < kQReg ? qf[ks < kQReg ? ks : 0] : u[f];
+        snx = mfma_bf16_32x32x16(u[slot_loads_q(i) ? f + 1 : f], qb, snx);
+      } else {
+        constexpr int j = i - kSSlots;
+        mfma_acc_32x32x16(o[j >> 1], u[f], __builtin_bit_cast(v8bf, pbw[j & 1]));
       }
-      if (i + kPfP < 32) {
-        vbuf[(i + kPfP) % (kPfP + 1)] = read_v(vb, i + kPfP);
-        nreads += 2;
-      }
-      const int st = slot_st(i), mt = i & 1;
-      int nmfma = 0;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const v8bf qb = st < kQReg ? qf[nt][st < kQReg ? st : 0] : qt[st < kQReg ? 0 : st - kQReg][nt];
-        sacc[mt][nt] = mfma_bf16_16x16x32(abuf[i % (kPfS + 1)], qb, sacc[mt][nt]);
-        nmfma += 1;
-      }
-      if (i < 32) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o[nt][i] = mfma_bf16_16x16x32(vbuf[i % (kPfP + 1)], pb[nt], o[nt][i]);
-        nmfma += 2;
-      }
-      // pin the slot's order: its LDS reads, then its MFMAs
-      if (nreads == 3) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-      if (nreads == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if (nreads == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (nmfma == 4) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (nmfma == 2) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      // pin the slot's order: its LDS reads, then its MFMA, then the VALU piece
+      constexpr int nreads = reads_in(issue_lo(i), issue_hi(i));
+      if constexpr (nreads > 0) __builtin_amdgcn_sched_group_barrier(0x100, nreads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      sm_piece(ic, valid_now);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) softmax(valid_next);
+    });
+    sacc = snx;
   };
 
   for (int pass = 0;; ++pass) {
+    l_run = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      l_run[nt] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) o[nt][i] = (v4f){0.f, 0.f, 0.f, 0.f};
-    }
-    // ---- prologue: blocks 0 and 1 in flight, logits and softmax of block 0
-    if (nb > 0) gather(kb0, 0);
-    if (nb > 1) gather(kb1, 1);
+    for (int ct = 0; ct < kCt; ++ct) o[ct] = (v16f){};
+    // ---- prologue: blocks 0 and 1 in flight, logits of block 0
+    if (nb > 0) gather(kb0, rows[g_row]);
+    if (nb > 1) gather(kb1, rows[kBlk + g_row]);
+    read_meta(0);
     if (nb > 1)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");
     else
@@ -390,40 +447,46 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
     __builtin_amdgcn_s_barrier();
     if (nb > 0) {
       logits((lds_u8_ptr)kb0);
-      softmax(block_valid(0));
+      valid_cur = block_valid(0);
     }
     run_ring(kb0, kb1, kb2, nb, step);
+    // the value MFMAs are inline asm, so the compiler does not know that
+    // their accumulators are written late: cover the MFMA-write to
+    // VALU-read/write distance before O is read or cleared
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     // every wave is past its last read of the stages here, and no DMA is outstanding
     if (pass > 0 || !__syncthreads_or(over ? 1 : 0)) break;
-    m_ref[0] = m_max[0];
-    m_ref[1] = m_max[1];
+    m_ref = m_max;
     over = false;
   }
 
   if (!active) return;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int head = kHeadsPerWave * wave + 16 * nt + hl;
-    float l_tot = l_run[nt] + shfl_xor_f(l_run[nt], 16);
-    l_tot += shfl_xor_f(l_tot, 32);
-    if (head >= p.H) continue;
-    const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_tot;
-    const float lse_v = empty ? -INFINITY : (m_ref[nt] + log2f(l_tot)) * 0.69314718055994530942f;
-    float* orow;
-    float* lrow;
-    if (p.n_split == 1) {
-      orow = p.out + (t * p.H + head) * (int64_t)kDv;
-      lrow = p.lse + t * p.H + head;
-    } else {
-      orow = p.part_o + ((t * p.n_split + sp) * p.H + head) * (int64_t)kDv;
-      lrow = p.part_lse + (t * p.n_split + sp) * p.H + head;
-    }
-    // O^T layout: lane (g4, head hl) holds c' = 16*ct + 4*g4 + i
-#pragma unroll
-    for (int ct = 0; ct < 32; ++ct) *(v4f*)(orow + 16 * ct + 4 * g4) = o[nt][ct] * inv;
-    if (g4 == 0) *lrow = lse_v;
+  const int head = kHeadsPerWave * wave + hn;
+  const auto lr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(lr[0]) + __uint_as_float(lr[1]);
+  if (head >= p.H) return;
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  const float lse_v = empty ? -INFINITY : (m_ref + log2f(l_tot)) * 0.69314718055994530942f;
+  float* orow;
+  float* lrow;
+  if (p.n_split == 1) {
+    orow = p.out + (t * p.H + head) * (int64_t)kDv;
+    lrow = p.lse + t * p.H + head;
+  } else {
+    orow = p.part_o + ((t * p.n_split + sp) * p.H + head) * (int64_t)kDv;
+    lrow = p.part_lse + (t * p.n_split + sp) * p.H + head;
   }
+  // O^T tile ct: lane (head hn, half hh) holds c' = 32*ct + 8*(r/4) + 4*hh + r%4
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *(v4f*)(orow + 32 * ct + 8 * r4 + 4 * hh) =
+          (v4f){o[ct][4 * r4], o[ct][4 * r4 + 1], o[ct][4 * r4 + 2], o[ct][4 * r4 + 3]} * inv;
+  if (hh == 0) *lrow = lse_v;
 }
 
 // Exact merge of split partials; one workgroup of 128 threads per (t, head).
