@@ -43,12 +43,12 @@ PEAK_HBM_GBS = 8000.0
 # the hash of the kernel sources the counters were taken on; once a source changes, the
 # figure no longer describes the kernel and the roofline reports traffic as null.
 COUNTER_TRAFFIC = {
-    ("prefill_L128k", "indexer"): ("405db5745fd97c6b", ("indexer.hip", "common.h", "launch.h"), 1130.24e6),
-    ("prefill_L128k", "topk"): ("37e0d6361a587fae", ("topk.hip", "common.h", "launch.h"), 1117.57e6),
-    ("prefill_L128k", "sparse_mla"): ("17949ff47ce3c62f", ("sparse_mla.hip", "common.h", "launch.h"), 206030.07e6),
-    ("paged_decode_b32_ctx4k_128k", "indexer"): ("405db5745fd97c6b", ("indexer.hip", "common.h", "launch.h"),
-                                                 278.34e6),
-    ("paged_decode_b32_ctx4k_128k", "topk"): ("37e0d6361a587fae", ("topk.hip", "common.h", "launch.h"), 8.64e6),
+    ("prefill_L128k", "indexer"): ("b42b5075f28ed96d", ("indexer.hip", "common.h", "launch.h"), 1126.01e6),
+    ("prefill_L128k", "topk"): ("9324c7a29d590212", ("topk.hip", "common.h", "launch.h"), 582.68e6),
+    ("prefill_L128k", "sparse_mla"): ("095056b82127bcd9", ("sparse_mla.hip", "common.h", "launch.h"), 219733.72e6),
+    ("paged_decode_b32_ctx4k_128k", "indexer"): ("b42b5075f28ed96d", ("indexer.hip", "common.h", "launch.h"), 278.27e6),
+    ("paged_decode_b32_ctx4k_128k", "topk"): ("9324c7a29d590212", ("topk.hip", "common.h", "launch.h"), 8.87e6),
+    ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("095056b82127bcd9", ("sparse_mla.hip", "common.h", "launch.h"), 197.56e6),
 }
 
 
