@@ -124,9 +124,12 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// XOR swizzle of the chunk slot within a 128-byte band row: the rows read
-// together by an operand load land on distinct banks.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 7; }
+// XOR swizzle of the chunk slot within a 128-byte band row, chosen by
+// measuring LDS bank conflicts of both operand reads: the 16-byte key-tile
+// reads (32 rows, one chunk each) and the transposed 8-byte value-tile reads
+// (4 rows x 16 columns per 16-lane group) are conflict-free with it.  For a
+// row 16a + 8b + r0 (r0 < 8) it equals swz(r0) ^ 4a ^ 2b.
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (2 * r)) & 7; }
 
 // O^T tile += V^T tile * P^T with the accumulator pinned to the accumulation
 // registers (the compiler would otherwise shuttle the 256 accumulators
