@@ -242,51 +242,56 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
   float wr[NT][4];
   load_query<NT>(q_idx, w, b, true, H_I, col, grp, a, wr);
 
-  // groups of this wave: kg(i) = c0 + 64*wave + 256*i
+  // groups of this wave: kg(i) = c0 + 64*wave + 256*i.  Lane i resolves the
+  // row of group i up front (one page lookup per 64-key group, which always
+  // lies in one page), so no key load waits on a lookup.
   const int64_t kg0 = c0 + 64 * wave;
   const int ng = kg0 < c_end ? (int)((c_end - kg0 + 255) / 256) : 0;
   auto kg_of = [&](int i) { return kg0 + 256 * (int64_t)i; };
+  int64_t my_base = -1;
+  if (lane < ng && kg_of(lane) < n) my_base = addr.group_row(b, kg_of(lane));
   auto base_of = [&](int i) -> int64_t {
-    const int64_t kg = kg_of(i);
-    return (i < ng && kg < n) ? addr.group_row(b, kg) : -1;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)my_base, i);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)my_base >> 32), i);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
   };
-  auto load = [&](int i, int64_t base, v4i (&raw)[4][2]) {
-    const int64_t kg = kg_of(i);
+  // Unpredicated loads: keys past the context re-read the group's last valid
+  // key (same page), and a group without a row reads row 0; their scores
+  // are masked in finish().
+  auto load = [&](int i, v4i (&raw)[4][2]) {
+    const int64_t base = base_of(i);
+    const int64_t last = n - 1 - kg_of(i);  // >= 0 whenever base >= 0
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      const int j = 16 * blk + col;
-      if (base >= 0 && kg + j < n) {
-        const v4i* p = (const v4i*)(keys + (base + j) * kIdxD + 32 * grp);
-        raw[blk][0] = p[0];
-        raw[blk][1] = p[1];
-      } else {
-        raw[blk][0] = (v4i){0, 0, 0, 0};
-        raw[blk][1] = raw[blk][0];
-      }
+      const int64_t j = 16 * blk + col;
+      const int64_t r = base >= 0 ? base + (j < last ? j : last) : 0;
+      const v4i* p = (const v4i*)(keys + r * kIdxD + 32 * grp);
+      raw[blk][0] = p[0];
+      raw[blk][1] = p[1];
     }
   };
-  auto finish = [&](int i, int64_t base, const v4i (&raw)[4][2]) {
+  auto finish = [&](int i, const v4i (&raw)[4][2]) {
     const int64_t s = kg_of(i) + lane;
     float part[4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) part[blk] = head_sum<NT>(a, wr, widen32(raw[blk][0], raw[blk][1]));
     const float v = group_transpose_reduce(part[0], part[1], part[2], part[3], grp);
-    if (s < c_end) scores[b * ld + s] = (s < n && base >= 0) ? v : -INFINITY;
+    if (s < c_end) scores[b * ld + s] = (s < n && base_of(i) >= 0) ? v : -INFINITY;
   };
 
-  v4i ra[4][2], rb[4][2];
-  int64_t base_a = base_of(0), base_b = base_of(1), base_c;
-  load(0, base_a, ra);
-  for (int i = 0; i < ng; i += 2) {
-    base_c = base_of(i + 2);
-    if (i + 1 < ng) load(i + 1, base_b, rb);
-    finish(i, base_a, ra);
+  // keys of the next two groups in flight while one group is on the matrix cores
+  v4i ra[4][2], rb[4][2], rc[4][2];
+  if (ng > 0) load(0, ra);
+  if (ng > 1) load(1, rb);
+  for (int i = 0; i < ng; i += 3) {
+    if (i + 2 < ng) load(i + 2, rc);
+    finish(i, ra);
     if (i + 1 >= ng) break;
-    base_a = base_c;
-    base_c = base_of(i + 3);
-    if (i + 2 < ng) load(i + 2, base_a, ra);
-    finish(i + 1, base_b, rb);
-    base_b = base_c;
+    if (i + 3 < ng) load(i + 3, ra);
+    finish(i + 1, rb);
+    if (i + 2 >= ng) break;
+    if (i + 4 < ng) load(i + 4, rb);
+    finish(i + 2, rc);
   }
 }
 
