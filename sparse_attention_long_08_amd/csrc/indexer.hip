@@ -37,15 +37,17 @@ __device__ __forceinline__ int kchunk(int key, int c) { return c ^ (((key & 3) <
 // On entry lane (g, c) = (lane/16, lane%16) holds its partial for key
 // 16*b + c of a 64-key group in p[b]; returns the sum over all four lane
 // groups for key 16*g + c.
-__device__ __forceinline__ float group_transpose_reduce(float p0, float p1, float p2, float p3, int g) {
-  const bool hi = (g & 2) != 0;
-  float y0 = shfl_xor_f(hi ? p0 : p2, 32);
-  float y1 = shfl_xor_f(hi ? p1 : p3, 32);
-  float a0 = (hi ? p2 : p0) + y0;
-  float a1 = (hi ? p3 : p1) + y1;
-  const bool odd = (g & 1) != 0;
-  float z = shfl_xor_f(odd ? a0 : a1, 16);
-  return (odd ? a1 : a0) + z;
+// The exchanges are VALU lane swaps: v_permlane32_swap(x, y) trades the upper
+// half-wave of x with the lower half-wave of y, so after swapping (p0, p2)
+// every lower lane holds (p0, partner p0) and every upper lane (partner p2,
+// p2); v_permlane16_swap does the same between odd and even 16-lane rows.
+__device__ __forceinline__ float group_transpose_reduce(float p0, float p1, float p2, float p3, int) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+  const float a0 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // rows 0-1: keys of p0; rows 2-3: of p2
+  const float a1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // A lane's 32 FP8 values (dims 32*g .. 32*g+31 of one vector) as the four
