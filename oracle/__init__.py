@@ -56,6 +56,9 @@ def _load():
         lib.oracle_dense_mla_row.restype = None
         lib.oracle_dense_mla_row.argtypes = [_u16p, _u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_double, _f64p, _f64p]
+        lib.oracle_indexer_kl_row.restype = ctypes.c_double
+        lib.oracle_indexer_kl_row.argtypes = [_u16p, _u16p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_double, _f64p]
         _lib = lib
     return _lib
 
@@ -110,6 +113,17 @@ def dense_mla_row(q: np.ndarray, kv: np.ndarray, n: int, scale: float, D_v: int)
     lse = np.empty(H, dtype=np.float64)
     _load().oracle_dense_mla_row(q, kv, kv.shape[0], n, H, D_qk, D_v, float(scale), out, lse)
     return out, lse
+
+
+def indexer_kl_row(q: np.ndarray, kv_rows: np.ndarray, scale: float, iscore: np.ndarray) -> float:
+    """Indexer KL loss of one query over its selected rows [m, D_qk] with indexer
+    scores iscore [m] ("DeepSeek-V3.2" walk-through §2.3.2)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kv_rows = np.ascontiguousarray(kv_rows, dtype=np.uint16).reshape(-1, q.shape[1])
+    iscore = np.ascontiguousarray(iscore, dtype=np.float64)
+    assert iscore.shape[0] == kv_rows.shape[0]
+    H, D_qk = q.shape
+    return float(_load().oracle_indexer_kl_row(q, kv_rows, kv_rows.shape[0], H, D_qk, float(scale), iscore))
 
 
 # ------------------------------------------------------------------ row drivers

@@ -16,6 +16,9 @@
  *       equation u_t = Attn(h_t, {c_s | I_{t,s} in Top-k(I_{t,:})})),
  *       §2.2 "DSA instantiated in MLA" (MQA mode: each latent KV entry is
  *       shared by all query heads of a token).
+ *       §2.3.2 "Sparse training stage" (the indexer's KL loss over the
+ *       selected set S_t, with the target built as in §2.3.1: attention
+ *       scores summed over heads, L1-normalised along the sequence).
  *  [P2] "DeepSeek v3.2" analysis article (2048ai.net), §1.2: indexer keys are
  *       one 128-dim vector per token and run in FP8.
  *
@@ -205,4 +208,53 @@ void oracle_dense_mla_row(const uint16_t* q, const uint16_t* kv, int64_t N, int6
     lse[h] = mx + log(sum);
   }
   free(logits);
+}
+
+/* Indexer KL loss of one query over its selected set ([P1] §2.3.2, with the
+ * target of §2.3.1 restricted to S_t).  The m selected latent rows are
+ * kv_rows[m][D_qk] (bf16 bits); iscore[s] is the indexer score I_{t,s} of
+ * selected entry s.
+ *   P_h(s) = softmax over S_t of scale * q[h] . kv[s]   (head h's attention)
+ *   p(s)   = sum_h P_h(s) / sum_{s'} sum_h P_h(s')      (heads summed, L1-normalised)
+ *   r(s)   = softmax over S_t of I_{t,s}
+ *   KL     = sum_s p(s) * (ln p(s) - ln r(s)),  with 0 * ln 0 = 0.
+ * m == 0 gives 0. */
+double oracle_indexer_kl_row(const uint16_t* q, const uint16_t* kv_rows, int64_t m, int32_t H, int32_t D_qk,
+                             double scale, const double* iscore) {
+  if (m == 0) return 0.0;
+  double* kvd = (double*)malloc(sizeof(double) * (size_t)m * (size_t)D_qk);
+  double* z = (double*)malloc(sizeof(double) * (size_t)m);
+  double* agg = (double*)calloc((size_t)m, sizeof(double));
+  double* qd = (double*)malloc(sizeof(double) * (size_t)D_qk);
+  for (int64_t i = 0; i < m * D_qk; ++i) kvd[i] = oracle_bf16_to_double(kv_rows[i]);
+  for (int h = 0; h < H; ++h) {
+    for (int c = 0; c < D_qk; ++c) qd[c] = oracle_bf16_to_double(q[(int64_t)h * D_qk + c]);
+    double zmax = -INFINITY;
+    for (int64_t s = 0; s < m; ++s) {
+      double dot = 0.0;
+      for (int c = 0; c < D_qk; ++c) dot += qd[c] * kvd[s * D_qk + c];
+      z[s] = scale * dot;
+      if (z[s] > zmax) zmax = z[s];
+    }
+    double denom = 0.0;
+    for (int64_t s = 0; s < m; ++s) denom += exp(z[s] - zmax);
+    for (int64_t s = 0; s < m; ++s) agg[s] += exp(z[s] - zmax) / denom;
+  }
+  double total = 0.0;
+  for (int64_t s = 0; s < m; ++s) total += agg[s];
+  double imax = -INFINITY;
+  for (int64_t s = 0; s < m; ++s) imax = iscore[s] > imax ? iscore[s] : imax;
+  double isum = 0.0;
+  for (int64_t s = 0; s < m; ++s) isum += exp(iscore[s] - imax);
+  const double log_norm = imax + log(isum); /* ln sum_s e^{I_s} */
+  double kl = 0.0;
+  for (int64_t s = 0; s < m; ++s) {
+    const double ps = agg[s] / total;
+    if (ps > 0.0) kl += ps * (log(ps) - (iscore[s] - log_norm));
+  }
+  free(qd);
+  free(agg);
+  free(z);
+  free(kvd);
+  return kl;
 }

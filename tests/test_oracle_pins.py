@@ -274,3 +274,65 @@ def test_tiny_chain_invariants_and_k_covering_all():
     r0 = oracle.prefill_row(wl, 0, keys)
     kvd = _bf16_to_np(kv[0])
     assert np.array_equal(r0["out"], np.broadcast_to(kvd[: wl.D_v], (wl.H, wl.D_v)))
+
+
+# ------------------------------------------------------------------ indexer KL loss
+# "DeepSeek-V3.2" walk-through §2.3.2: KL(p_{t,S_t} || Softmax(I_{t,S_t})), with p the
+# attention scores summed over heads and L1-normalised along the selected tokens (§2.3.1).
+
+def test_indexer_kl_hand_cases():
+    # one head, D_qk = 2, scale 1, two selected rows with logits (0, 1):
+    # p = (1, e)/(1+e).  Against I = (0, 0), r = (1/2, 1/2) and
+    # KL = sum p ln(2p) = ln 2 + p0 ln p0 + p1 ln p1.
+    q = gen.f32_to_bf16_bits(np.array([[1.0, 0.0]], np.float32))
+    kv = gen.f32_to_bf16_bits(np.array([[0.0, 2.0], [1.0, 4.0]], np.float32))
+    e = math.e
+    p0, p1 = 1 / (1 + e), e / (1 + e)
+    want = math.log(2) + p0 * math.log(p0) + p1 * math.log(p1)
+    assert oracle.indexer_kl_row(q, kv, 1.0, np.array([0.0, 0.0])) == pytest.approx(want, rel=1e-14)
+    # an indexer that reproduces the logits up to a constant has zero loss
+    assert abs(oracle.indexer_kl_row(q, kv, 1.0, np.array([3.0, 4.0]))) < 1e-15
+    # with I = (1, 0) the model distribution is r = (e, 1)/(1+e): KL = sum p ln(p/r)
+    r0, r1 = e / (1 + e), 1 / (1 + e)
+    want = p0 * math.log(p0 / r0) + p1 * math.log(p1 / r1)
+    assert oracle.indexer_kl_row(q, kv, 1.0, np.array([1.0, 0.0])) == pytest.approx(want, rel=1e-13)
+
+
+def test_indexer_kl_heads_are_summed_then_normalised():
+    # two heads with logits (0, 1) and (1, 0): their probabilities sum to (1, 1) per
+    # position, so the L1-normalised target is uniform whatever the per-head shapes
+    q = gen.f32_to_bf16_bits(np.array([[1.0, 0.0], [0.0, 1.0]], np.float32))
+    kv = gen.f32_to_bf16_bits(np.array([[0.0, 1.0], [1.0, 0.0]], np.float32))
+    iscore = np.array([0.25, -1.5])
+    r = np.exp(iscore) / np.exp(iscore).sum()
+    want = float(np.sum(0.5 * np.log(0.5 / r)))
+    assert oracle.indexer_kl_row(q, kv, 1.0, iscore) == pytest.approx(want, rel=1e-13)
+
+
+def test_indexer_kl_single_row_and_empty_are_zero():
+    rng = np.random.default_rng(5)
+    q = _rand_bf16(rng, (4, 16))
+    kv = _rand_bf16(rng, (1, 16))
+    assert oracle.indexer_kl_row(q, kv, 0.4, np.array([2.5])) == 0.0
+    assert oracle.indexer_kl_row(q, kv[:0], 0.4, np.zeros(0)) == 0.0
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_indexer_kl_matches_torch_kl_div(seed):
+    # an independent route: torch's fp64 softmax per head and its kl_div
+    rng = np.random.default_rng(10 + seed)
+    H, D_qk, m = 5, 40, 23
+    q = _rand_bf16(rng, (H, D_qk))
+    kv = _rand_bf16(rng, (m, D_qk))
+    iscore = rng.standard_normal(m) * 3
+    scale = 0.2
+    z = torch.from_numpy(_bf16_to_np(q)) @ torch.from_numpy(_bf16_to_np(kv)).T * scale   # [H, m]
+    target = torch.softmax(z, dim=1).sum(0)
+    target = target / target.sum()
+    log_r = torch.log_softmax(torch.from_numpy(iscore), dim=0)
+    want = torch.nn.functional.kl_div(log_r, target, reduction="sum").item()
+    got = oracle.indexer_kl_row(q, kv, scale, iscore)
+    assert got == pytest.approx(want, rel=1e-12, abs=1e-14)
+    assert got >= 0.0
+    # invariant under a shift of every indexer score
+    assert oracle.indexer_kl_row(q, kv, scale, iscore + 7.0) == pytest.approx(got, rel=1e-10, abs=1e-13)
