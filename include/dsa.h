@@ -139,6 +139,27 @@ dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, 
                                     float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Indexer KL loss of the sparse training stage, [P1] §2.3.2 (target built as
+ * in §2.3.1: the attention scores of all heads summed, then L1-normalised
+ * along the selected tokens).  For each query t, with S_t its valid entries
+ * of idx:
+ *   P_h(s) = exp(scale * q[t,h] . kv[s] - lse[t,h])   (head h's attention)
+ *   p(s)   = (1/H) sum_h P_h(s),   r(s) = softmax over S_t of scores[t, s]
+ *   kl[t]  = sum_{s in S_t} p(s) * (ln p(s) - ln r(s))
+ * The loss is sum_t kl[t].
+ *   q [T, H, D_qk] bf16, kv [N, D_qk] bf16, idx [T, k] int32 (entries < 0 or
+ *   >= N skip), lse [T, H] fp32 as written by dsa_sparse_mla_fwd for the same
+ *   q, kv and idx, scores [T, ld] fp32 with row t holding I[t, s] at column s
+ *   (as dsa_indexer_scores writes it; only the selected columns are read),
+ *   kl [T] fp32 out.  A row with no valid entry gives 0.
+ * Logit products are bf16 x bf16 with fp32 accumulation; the rest is fp32.
+ * No workspace; errors as for the other calls.
+ */
+dsa_status dsa_indexer_kl_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* lse,
+                              const float* scores, int64_t ld, int64_t T, int64_t N, int32_t H, int32_t D_qk,
+                              int32_t k, float scale, float* kl, dsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Fused prefill of one sequence: indexer -> top-k -> sparse attention for the
  * T queries at positions q_pos0 .. q_pos0+T-1 over keys 0 .. N-1 (N >= q_pos0+T
  * is not required; candidates are capped at N).  The L x L score matrix is

@@ -32,6 +32,8 @@ SIGNATURES = {
     "dsa_sparse_mla_fwd_paged_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
     "dsa_sparse_mla_fwd_paged": (_c_i32, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i64, _c_i32,
                                           _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "dsa_indexer_kl_fwd": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                    _c_f32, _c_p, _c_p]),
     "dsa_forward_prefill_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32]),
     "dsa_forward_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_i64, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
@@ -133,6 +135,11 @@ def dsa_sparse_mla_fwd_paged(q, kv_pool, n_pages, page_table, max_pages, ctx_len
     _call("dsa_sparse_mla_fwd_paged", _ptr(q), _ptr(kv_pool), n_pages, _ptr(page_table), max_pages, _ptr(ctx_len),
           page_size, _ptr(idx), B, H, D_qk, D_v, k, scale, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
           _stream(stream))
+
+
+def dsa_indexer_kl_fwd(q, kv, idx, lse, scores, ld, T, N, H, D_qk, k, scale, kl, stream=None):
+    _call("dsa_indexer_kl_fwd", _ptr(q), _ptr(kv), _ptr(idx), _ptr(lse), _ptr(scores), ld, T, N, H, D_qk, k, scale,
+          _ptr(kl), _stream(stream))
 
 
 def dsa_forward_prefill_workspace_bytes(T, N, H, D_v, k) -> int:

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip"]
+SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "indexer_kl.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -24,7 +24,7 @@ HIPCC_FLAGS = [
 # the accumulation registers; the indexer's epilogue reads every accumulator
 # with VALU instructions, which cannot read accumulation registers directly.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-SOURCE_FLAGS = {"sparse_mla.hip": _VGPR_FORM, "indexer.hip": _VGPR_FORM}
+SOURCE_FLAGS = {"sparse_mla.hip": _VGPR_FORM, "indexer.hip": _VGPR_FORM, "indexer_kl.hip": _VGPR_FORM}
 
 
 def _run(cmd):

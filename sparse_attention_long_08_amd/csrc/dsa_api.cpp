@@ -205,6 +205,20 @@ dsa_status dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32
                  (hipStream_t)stream);
 }
 
+dsa_status dsa_indexer_kl_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* lse,
+                              const float* scores, int64_t ld, int64_t T, int64_t N, int32_t H, int32_t D_qk,
+                              int32_t k, float scale, float* kl, dsa_stream_t stream) {
+  REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "T must be >= 0 and N >= 1");
+  if (dsa_status s = check_mla_shape(H, D_qk, 512, k)) return s;
+  REQUIRE(ld >= N, DSA_ERR_INVALID_ARG, "ld (%lld) must be >= N (%lld)", (long long)ld, (long long)N);
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (T == 0) return ok();
+  REQUIRE_PTR(q); REQUIRE_PTR(kv); REQUIRE_PTR(idx); REQUIRE_PTR(lse); REQUIRE_PTR(scores); REQUIRE_PTR(kl);
+  REQUIRE_AL(q); REQUIRE_AL(kv); REQUIRE_AL(idx);
+  return hip_check(dsa::launch_indexer_kl(q, kv, N, idx, lse, scores, ld, T, H, k, scale, kl, (hipStream_t)stream),
+                   "indexer KL launch");
+}
+
 size_t dsa_sparse_mla_fwd_paged_workspace_bytes(int64_t B, int32_t H, int32_t /*D_v*/, int32_t k) {
   return mla_ws(B, H, k);
 }

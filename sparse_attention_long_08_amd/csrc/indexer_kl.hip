@@ -1,0 +1,273 @@
+// Indexer KL loss of DeepSeek-V3.2's sparse training stage on gfx950.
+//
+// "DeepSeek-V3.2" report walk-through §2.3.2: with the selected set S_t of
+// query t fixed, the indexer is trained with
+//   L^I = sum_t KL( p_{t,S_t} || Softmax(I_{t,S_t}) ),
+// where the target p_{t,:} is built as in §2.3.1: the main attention scores
+// of all heads are summed and L1-normalised along the sequence.  Here the
+// attention scores are each head's softmax over S_t, so with lse_h the
+// attention's log-sum-exp of head h:
+//   P_h(s) = exp(scale * q_h . kv_s - lse_h),   p(s) = (1/H) sum_h P_h(s),
+//   KL_t   = sum_s p(s) ln p(s) - sum_s p(s) I(s) + LSE_I * sum_s p(s),
+// LSE_I = ln sum_{s in S_t} exp(I(s)).  (sum_s p(s) is 1 up to rounding; it
+// is kept so the loss is the divergence of the normalised distributions the
+// kernel actually formed.)
+//
+// Mapping.  One workgroup of 4 waves per query.  Wave w owns heads
+// 32w .. 32w+31 as the N side of 32x32x16 bf16 MFMAs and keeps all 36 query
+// k-steps in registers; selected latent rows arrive 32 at a time in a
+// two-stage LDS ring through the global->LDS DMA (the band-major, swizzled
+// layout of the attention kernel).  Per block the logit product gives each
+// lane one head over 16 keys; the probabilities go to an LDS tile
+// [32 keys x 128 heads] and eight threads per key sum them over the heads.
+// The indexer scores of the selected entries are gathered once into LDS.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+
+namespace {
+constexpr int kDqk = 576;
+constexpr int kBlk = 32;
+constexpr int kBufBytes = kBlk * kDqk * 2;  // 36864 bytes per stage
+constexpr int kBand = 4096;                 // bytes per 8-chunk band of a stage
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kHeadsPerWave = 32;
+constexpr int kMaxHeads = kWaves * kHeadsPerWave;
+constexpr int kDmaPerWave = 9;
+constexpr int kKSteps = kDqk / 16;
+constexpr int kMaxK = 4096;
+constexpr int kPf = 3;  // key-tile reads in flight
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) uint8_t* lds_u8_ptr;
+
+// chunk-slot swizzle of a 128-byte band row (as in the attention kernel:
+// conflict-free for the 16-byte key-tile reads of 32 rows)
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (2 * r)) & 7; }
+
+// The two stages arrive restrict-qualified so the compiler sees that the
+// stage being read is not the one a DMA is writing.
+template <class Step>
+__device__ __forceinline__ void run_pair(uint8_t* __restrict__ sa, uint8_t* __restrict__ sb, int nb, Step& step) {
+  for (int blk = 0; blk < nb; blk += 2) {
+    step(sa, sb, blk);
+    if (blk + 1 < nb) step(sb, sa, blk + 1);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+}  // namespace
+
+struct KlParams {
+  const uint16_t* q;
+  const uint16_t* kv;
+  uint32_t kv_bytes;  // extent of the latent rows when below 4 GiB (buffer DMA), else 0
+  const int32_t* idx;
+  const float* lse;
+  const float* scores;
+  int64_t ld;
+  int64_t N;
+  int32_t H;
+  int32_t k;
+  float scale_log2;  // scale * log2(e)
+  float* kl;
+};
+
+template <bool kBufDma>
+__global__ __launch_bounds__(kThreads, 1) void indexer_kl_kernel(KlParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kBufBytes];
+  __shared__ int32_t rows[kMaxK];                          // latent row of every entry (-1: skipped)
+  __shared__ float isel[kMaxK];                            // indexer score of every entry
+  __shared__ __attribute__((aligned(16))) float pbuf[kBlk * kMaxHeads];  // P of one block, [key][head]
+  __shared__ float red[3 * kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hn = lane & 31, hh = lane >> 5;
+  const int64_t t = blockIdx.x;
+  const int32_t* idx_row = p.idx + t * (int64_t)p.k;
+  const int nb = (p.k + kBlk - 1) / kBlk;
+
+  // ---- selected rows and their indexer scores; LSE_I over the valid ones
+  float imax = -INFINITY;
+  for (int e = tid; e < nb * kBlk; e += kThreads) {
+    int32_t row = -1;
+    float sc = -INFINITY;
+    if (e < p.k) {
+      const int32_t s = idx_row[e];
+      if (s >= 0 && s < p.N) {
+        row = s;
+        sc = p.scores[t * p.ld + s];
+      }
+    }
+    rows[e] = row;
+    isel[e] = sc;
+    imax = fmaxf(imax, sc);
+  }
+  imax = wave_max(imax);
+  if (lane == 0) red[wave] = imax;
+  __syncthreads();
+  imax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float isum = 0.f;
+  for (int e = tid; e < nb * kBlk; e += kThreads)
+    if (rows[e] >= 0) isum += expf(isel[e] - imax);
+  isum = wave_sum(isum);
+  __syncthreads();
+  if (lane == 0) red[wave] = isum;
+
+  // ---- query rows of this wave's heads (all 36 k-steps; B layout of the
+  // logit MFMA: k-step ks of lane (head hn, half hh) is dims 16ks + 8hh ..)
+  const int head = kHeadsPerWave * wave + hn;
+  const bool hv = head < p.H;
+  v8bf qf[kKSteps];
+  {
+    const uint16_t* qrow = p.q + (t * p.H + (hv ? head : p.H - 1)) * (int64_t)kDqk + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const v8bf v = *(const v8bf*)(qrow + 16 * ks);
+      qf[ks] = hv ? v : (v8bf){};
+    }
+  }
+  const float lse_l2 = hv ? p.lse[t * p.H + head] * 1.44269504088896340736f : 0.f;
+  __syncthreads();
+  const float lse_i = imax + logf(red[0] + red[1] + red[2] + red[3]);  // -inf for an empty row
+
+  // ---- gather: wave w moves rows 8w .. 8w+7 of a block, one DMA per band
+  const int g_row = 8 * wave + (lane >> 3);
+  const int g_chunk = (lane & 7) ^ swz(g_row);
+  const __amdgpu_buffer_rsrc_t kv_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)0, (int)p.kv_bytes, 0x00020000);
+  auto gather = [&](uint8_t* base, int blk) {
+    int32_t row = rows[blk * kBlk + g_row];
+    row = row < 0 ? 0 : row;  // skipped entries read row 0 (masked later)
+    if constexpr (kBufDma) {
+      const uint32_t voff = (uint32_t)row * (kDqk * 2) + 16 * g_chunk;
+#pragma unroll
+      for (int bd = 0; bd < kDmaPerWave; ++bd)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (lds_ptr)(base + bd * kBand + wave * 1024), 16,
+                                                 voff + 128 * bd, 0, 0, 0);
+    } else {
+      const uint16_t* src = p.kv + ((uint64_t)(uint32_t)row * kDqk + 8 * g_chunk);
+#pragma unroll
+      for (int bd = 0; bd < kDmaPerWave; ++bd)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 64 * bd), (lds_ptr)(base + bd * kBand + wave * 1024),
+                                         16, 0, 0);
+    }
+  };
+  // key tile of k-step ks: lane (row hn, half hh) reads chunk 2ks + hh of its row
+  uint32_t k_addr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) k_addr[q] = (uint32_t)(hn * 128 + (((2 * q + hh) ^ swz(hn)) << 4));
+  auto read_k = [&](const lds_u8_ptr base, int ks) {
+    return *(const __attribute__((address_space(3))) v8bf*)(base + k_addr[ks & 3] + kBand * (ks >> 2));
+  };
+
+  float ent = 0.f, cross = 0.f, psum = 0.f;  // per key-owning thread, over all blocks
+  const int rkey = tid >> 3, rpart = tid & 7;  // head-sum role: key rkey, heads 16*rpart .. +15
+
+  auto step = [&](uint8_t* cur, uint8_t* nxt, int blk) {
+    // this wave's DMA of blk landed; the barrier makes every wave's land and
+    // frees nxt (read in the previous step) and pbuf (read there too)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (blk + 1 < nb) gather(nxt, blk + 1);
+    const lds_u8_ptr kb = (lds_u8_ptr)cur;
+    v16f acc = {};
+    v8bf abuf[kPf + 1];
+#pragma unroll
+    for (int ks = 0; ks < kPf; ++ks) abuf[ks] = read_k(kb, ks);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if (ks + kPf < kKSteps) abuf[(ks + kPf) % (kPf + 1)] = read_k(kb, ks + kPf);
+      acc = mfma_bf16_32x32x16(abuf[ks % (kPf + 1)], qf[ks], acc);
+    }
+    // lane (head, hh) holds keys 8*(r/4) + 4*hh + r%4 of the block
+    const uint32_t valid = (uint32_t)(__ballot(rows[blk * kBlk + (lane & 31)] >= 0) & 0xFFFFFFFFull);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const bool ok = hv && ((valid >> key) & 1);
+      pbuf[key * kMaxHeads + head] = ok ? __builtin_amdgcn_exp2f(fmaf(acc[r], p.scale_log2, -lse_l2)) : 0.f;
+    }
+    // bare barrier after the LDS writes: a fenced one would also wait for the DMA just issued
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    // sum over the heads: 8 threads per key, 16 heads each
+    const v4f* src = (const v4f*)(pbuf + rkey * kMaxHeads + 16 * rpart);
+    const v4f a = src[0], b2 = src[1], c = src[2], d = src[3];
+    float v = ((a[0] + a[1]) + (a[2] + a[3])) + ((b2[0] + b2[1]) + (b2[2] + b2[3])) +
+              (((c[0] + c[1]) + (c[2] + c[3])) + ((d[0] + d[1]) + (d[2] + d[3])));
+    v += shfl_xor_f(v, 1);
+    v += shfl_xor_f(v, 2);
+    v += shfl_xor_f(v, 4);
+    const int e = blk * kBlk + rkey;
+    if (rpart == 0 && rows[e] >= 0) {
+      const float ps = v / (float)p.H;
+      if (ps > 0.f) ent += ps * logf(ps);
+      cross += ps * isel[e];
+      psum += ps;
+    }
+  };
+  if (nb > 0) gather(st0, 0);
+  run_pair(st0, st1, nb, step);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  ent = wave_sum(ent);
+  cross = wave_sum(cross);
+  psum = wave_sum(psum);
+  __syncthreads();
+  if (lane == 0) {
+    red[wave] = ent;
+    red[kWaves + wave] = cross;
+    red[2 * kWaves + wave] = psum;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float se = 0.f, sc = 0.f, sp = 0.f;
+    for (int w = 0; w < kWaves; ++w) {
+      se += red[w];
+      sc += red[kWaves + w];
+      sp += red[2 * kWaves + w];
+    }
+    p.kl[t] = sp > 0.f ? se - sc + sp * lse_i : 0.f;
+  }
+}
+
+hipError_t launch_indexer_kl(const uint16_t* q, const uint16_t* kv, int64_t N, const int32_t* idx,
+                             const float* lse, const float* scores, int64_t ld, int64_t T, int32_t H, int32_t k,
+                             float scale, float* kl, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  KlParams p;
+  p.q = q;
+  p.kv = kv;
+  const uint64_t extent = (uint64_t)N * kDqk * 2;
+  p.kv_bytes = extent < 0xFFFFFFFFull ? (uint32_t)extent : 0u;
+  p.idx = idx;
+  p.lse = lse;
+  p.scores = scores;
+  p.ld = ld;
+  p.N = N;
+  p.H = H;
+  p.k = k;
+  p.scale_log2 = scale * 1.44269504088896340736f;
+  p.kl = kl;
+  if (p.kv_bytes != 0)
+    hipLaunchKernelGGL(indexer_kl_kernel<true>, dim3((unsigned)T), dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(indexer_kl_kernel<false>, dim3((unsigned)T), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

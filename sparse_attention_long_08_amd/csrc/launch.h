@@ -59,6 +59,12 @@ struct MlaArgs {
 };
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 
+// Indexer KL loss per query over its selected entries (one workgroup per
+// query; lse from the attention of the same q, kv and idx).
+hipError_t launch_indexer_kl(const uint16_t* q, const uint16_t* kv, int64_t N, const int32_t* idx,
+                             const float* lse, const float* scores, int64_t ld, int64_t T, int32_t H, int32_t k,
+                             float scale, float* kl, hipStream_t st);
+
 // Number of key splits used for T queries of H heads with k entries each.
 int32_t sparse_mla_splits(int64_t T, int32_t H, int32_t k);
 
