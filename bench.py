@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=60, help="query rows the CPU oracle baseline times")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--kl", action="store_true",
+                    help="time the sparse-stage indexer KL loss instead of the forward path (prefill_L32k unless "
+                         "--workload names another prefill workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -120,8 +123,17 @@ def main():
 
     from dsa_inputs import configs
 
+    if args.kl and args.workload == ap.get_default("workload"):
+        args.workload = "prefill_L32k"
     wl = configs.WORKLOADS[args.workload]
     decode = wl.kind != "prefill"
+    if args.kl:
+        if decode:
+            print("--kl needs a prefill workload", file=sys.stderr)
+            sys.exit(2)
+        args.steps = 3 if args.steps is None else args.steps
+        args.warmup = 1 if args.warmup is None else args.warmup
+        return bench_kl(args, wl)
     if args.steps is None:
         args.steps = 200 if decode else 3
     if args.warmup is None:
@@ -267,6 +279,124 @@ def bench_prefill(args, wl):
     if not args.no_cpu:
         print(f"[bench] CPU oracle baseline on {args.cpu_rows} rows", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+def kl_cpu_baseline(wl, rows: int):
+    """The oracle's KL loss (single thread) on `rows` seeded-random query rows; the
+    oracle's own scores and selection feed it and are computed outside the timed part."""
+    import numpy as np
+    import oracle
+    from dsa_inputs import configs
+    sample = configs.sample_rows(wl, rows)
+    keys = configs.k_idx_bytes(wl, 0, np.arange(int(sample.max()) + 1))
+    jobs = []
+    for t in sample:
+        r = oracle.prefill_row(wl, int(t), keys)
+        sel = r["idx"][r["idx"] >= 0]
+        jobs.append((configs.q_bf16(wl, [int(t)])[0], oracle.gather_kv(wl, 0, r["idx"]), r["scores"][sel]))
+    t0 = time.perf_counter()
+    for q, kv_rows, isc in jobs:
+        oracle.indexer_kl_row(q, kv_rows, wl.scale, isc)
+    dt = time.perf_counter() - t0
+    return {"value": len(sample) / dt, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(sample)} seeded-random query rows of {wl.name} (positions "
+                      f"{int(sample.min())}..{int(sample.max())}), KL loss per row on the oracle's own "
+                      f"selection, single-threaded C oracle in fp64, {dt:.1f} s"}
+
+
+def bench_kl(args, wl):
+    """Sparse-stage indexer KL loss over every query row of a prefill workload.  Per
+    row tile the indexer scores and top-k are computed first (untimed); the
+    attention LSE comes from one attention call over all rows (untimed); the
+    timed part is the KL kernel over all tiles."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_long_08_amd as dsa
+    from dsa_inputs import device
+
+    dsa.load()
+    T, N, k, H = wl.T, wl.N, wl.k, wl.H
+    print(f"[bench] generating {wl.name} inputs on the GPU", file=sys.stderr, flush=True)
+    inp = device.make_prefill_inputs(wl)
+    stream = torch.cuda.current_stream()
+    tile_rows, ld = dsa.dsa_forward_prefill_plan(T, N)
+    n_tiles = (T + tile_rows - 1) // tile_rows
+    scores = torch.empty((n_tiles, tile_rows, ld), dtype=torch.float32, device="cuda") if n_tiles * tile_rows * ld \
+        * 4 <= (8 << 30) else None
+    if scores is None:
+        print("[bench] --kl keeps every score tile resident; this workload's tiles exceed 8 GiB", file=sys.stderr)
+        sys.exit(2)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    for i in range(n_tiles):
+        r0 = i * tile_rows
+        tr = min(tile_rows, T - r0)
+        dsa.dsa_indexer_scores(inp["q_idx"][r0:], inp["w"][r0:], inp["k_idx"], tr, N, wl.H_I, wl.d_I, r0,
+                               scores[i], ld)
+        dsa.dsa_topk(scores[i], ld, tr, N, r0, None, k, idx[r0:])
+    out = torch.empty((T, H, wl.D_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    nb = dsa.dsa_sparse_mla_fwd_workspace_bytes(T, H, wl.D_v, k)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_fwd(inp["q"], inp["kv"], idx, T, N, H, wl.D_qk, wl.D_v, k, wl.scale, out, lse, ws, nb)
+    del out
+    kl = torch.empty((T,), dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_tiles)]
+
+    def step(record):
+        for i in range(n_tiles):
+            r0 = i * tile_rows
+            tr = min(tile_rows, T - r0)
+            if record:
+                ev[2 * i].record(stream)
+            dsa.dsa_indexer_kl_fwd(inp["q"][r0:], inp["kv"], idx[r0:], lse[r0:], scores[i], ld, tr, N, H,
+                                   wl.D_qk, k, wl.scale, kl[r0:])
+            if record:
+                ev[2 * i + 1].record(stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    kl_ms = 0.0
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        kl_ms += sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_tiles))
+        print(f"[bench] KL step {s_ + 1}/{args.steps} done", file=sys.stderr, flush=True)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kl_ms /= args.steps
+    w = algorithmic_work(wl, T)
+    flops = w["selected"] * 2 * H * wl.D_qk
+    ach = flops / (kl_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "DSA sparse-stage indexer KL loss query-tokens/s",
+        "value": T / (kl_ms * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": kl_ms,
+        "host_wall_ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator, device-resident)",
+        "config": {"workload": wl.name, "L": T, "k": k, "H": H, "D_qk": wl.D_qk, "causal": True,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "indexer_kl", "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                     "traffic": counter_traffic(wl.name, "indexer_kl"), "launches_per_step": n_tiles,
+                     "avg_launch_ms": kl_ms / n_tiles},
+        "loss": float(kl.sum().item()),
+    }
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline on 12 rows", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = kl_cpu_baseline(wl, 12)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec))
