@@ -304,10 +304,15 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
 }
 
 // ------------------------------------------------------------------ fused decode
+// scratch of the multi-workgroup top-k (few long rows), 0 when it is not used
+static size_t decode_topk_ws(int64_t B, int64_t max_ctx) {
+  return dsa::topk_rows_preferred(B, max_ctx) ? round_up(dsa::topk_rows_scratch_bytes(B, max_ctx)) : 0;
+}
+
 static size_t decode_ws(int64_t B, int64_t max_ctx, int32_t H, int32_t k) {
   if (B <= 0 || max_ctx <= 0 || k <= 0) return 0;
   return round_up(sizeof(float) * (size_t)B * score_ld(max_ctx)) + round_up(sizeof(int32_t) * (size_t)B * k) +
-         mla_ws(B, H, k);
+         decode_topk_ws(B, max_ctx) + mla_ws(B, H, k);
 }
 
 size_t dsa_forward_decode_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t /*D_v*/, int32_t k) {
@@ -334,12 +339,16 @@ static dsa_status run_decode(const uint8_t* q_idx, const float* w, const uint8_t
   int32_t* idx_ws = (int32_t*)p;
   p += round_up(sizeof(int32_t) * (size_t)B * k);
   int32_t* sel = idx ? idx : idx_ws;
+  void* topk_scratch = p;
+  const size_t topk_bytes = decode_topk_ws(B, max_ctx);
+  p += topk_bytes;
   if (dsa_status s = hip_check(dsa::launch_indexer_decode(q_idx, w, keys, stride, paged, ctx_len, B, max_ctx, H_I,
                                                           scores, ld, st),
                                "decode indexer launch"))
     return s;
-  if (dsa_status s = hip_check(dsa::launch_topk(scores, ld, B, max_ctx, 0, ctx_len, k, sel, st), "top-k launch"))
-    return s;
+  const hipError_t te = topk_bytes ? dsa::launch_topk_rows(scores, ld, B, max_ctx, ctx_len, k, sel, topk_scratch, st)
+                                   : dsa::launch_topk(scores, ld, B, max_ctx, 0, ctx_len, k, sel, st);
+  if (dsa_status s = hip_check(te, "top-k launch")) return s;
   const int64_t seq_len = paged ? (int64_t)paged->max_pages * paged->page_size : stride;
   return run_mla(q, kv, sel, B, H, k, scale, out, lse, p, ws_bytes - (size_t)(p - (char*)ws), true, stride,
                  seq_len, ctx_len, paged, st);

@@ -31,6 +31,14 @@ hipError_t launch_indexer_decode(const uint8_t* q_idx, const float* w, const uin
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0,
                        const int32_t* n_valid, int32_t k, int32_t* idx, hipStream_t st);
 
+// Top-k for a few long rows (decode): the full-row passes run over
+// 4096-key chunks in parallel; needs topk_rows_scratch_bytes(T, N) of device
+// scratch and n_valid.  Same selection as launch_topk.
+bool topk_rows_preferred(int64_t T, int64_t N);
+size_t topk_rows_scratch_bytes(int64_t T, int64_t N);
+hipError_t launch_topk_rows(const float* scores, int64_t ld, int64_t T, int64_t N, const int32_t* n_valid,
+                            int32_t k, int32_t* idx, void* scratch, hipStream_t st);
+
 // Sparse MLA-MQA attention.  Query t reads latent rows of sequence
 // (seq_per_query ? t : 0) through the given addressing: contiguous rows
 // (kv + row*D_qk with row = b*stride + s, s < seq_len) or paged.

@@ -243,11 +243,14 @@ __device__ __forceinline__ void refine_list(TopkShared& sh, int nl, uint32_t& lo
 // nothing, when the gathered list misses [k, capacity]; the caller then takes
 // the exact path.  Needs a 16-byte aligned row with n >= kSampleMinN; the
 // bitmap area (n_words * 8 bytes >= n / 4 bytes) doubles as the sample buffer.
-__device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __restrict__ row, int64_t n, int32_t k,
-                                             uint32_t* gt_bits, uint32_t* eq_bits, int n_words,
-                                             int32_t* __restrict__ out) {
+// The sampled threshold estimate: 1/16 of the row (64-key chunks spread
+// over the whole row) is read into `sample` (at least n/4 + 240 bytes of
+// LDS) and its exact r-th largest key returned, with r chosen so that about
+// 1.37k keys of the full row are expected at or above it.  Needs a 16-byte
+// aligned row with n >= kSampleMinN.
+__device__ __forceinline__ uint32_t sample_estimate(TopkShared& sh, const float* __restrict__ row, int64_t n,
+                                                    int32_t k, uint32_t* sample) {
   const int tid = threadIdx.x;
-  uint32_t* sample = gt_bits;
   // sampled chunk j: keys 64*(16*j + (5*j % 16)) .. +63, whole chunks inside the row
   const int64_t n_chunks = n / 64;
   const int m_chunks = (int)((n_chunks + kSampleStride - 1) / kSampleStride);
@@ -275,7 +278,15 @@ __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __rest
   if (rs > m) rs = m;
   uint32_t lo = 0u, hi = 0xFFFFFFFFu;
   refine_list(sh, m, lo, hi, 0u, 0, (uint32_t)rs, sample);
-  const uint32_t t_est = lo;
+  return lo;
+}
+
+__device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __restrict__ row, int64_t n, int32_t k,
+                                             uint32_t* gt_bits, uint32_t* eq_bits, int n_words,
+                                             int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  const uint32_t t_est = sample_estimate(sh, row, n, k, gt_bits);
+  uint32_t lo, hi;
 
   if (tid == 0) sh.list_n = 0;
   __syncthreads();
@@ -310,29 +321,12 @@ __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __rest
   return true;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t ld,
-                                                             int64_t T, int64_t N, int64_t q_pos0,
-                                                             const int32_t* __restrict__ n_valid, int32_t k,
-                                                             int32_t* __restrict__ idx, int32_t n_words) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
-  uint32_t* gt_bits = reinterpret_cast<uint32_t*>(smem + sizeof(TopkShared));
-  uint32_t* eq_bits = gt_bits + n_words;
-
+// Exact path of one row (see the file comment): radix refinement over the
+// row in global memory, then the LDS list, then the ordered emit.
+__device__ __forceinline__ void topk_exact_row(TopkShared& sh, const float* __restrict__ row, int64_t n, bool vec,
+                                               int32_t k, uint32_t* gt_bits, uint32_t* eq_bits, int n_words,
+                                               int32_t* __restrict__ out) {
   const int tid = threadIdx.x;
-  const int64_t t = blockIdx.x;
-  int64_t n = n_valid ? (int64_t)n_valid[t] : q_pos0 + t + 1;
-  n = n < 0 ? 0 : (n > N ? N : n);
-  int32_t* out = idx + t * (int64_t)k;
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
-    return;
-  }
-  const float* row = scores + t * ld;
-  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
-  if (vec && n >= kSampleMinN && topk_sampled(sh, row, n, k, gt_bits, eq_bits, n_words, out)) return;
-
-  // ------------------------------------------------------------ global refinement
   // Current candidate key range [lo, hi]; `above` keys are > hi.
   uint32_t lo = 0u, hi = 0xFFFFFFFFu, above = 0u, in_range = (uint32_t)n;
   int level = 0;  // 0: bits 31..20, 1: bits 19..8, 2: bits 7..0
@@ -394,6 +388,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   emit_selection(sh, gt_bits, eq_bits, n_words, (uint32_t)k, out);
 }
 
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t ld,
+                                                             int64_t T, int64_t N, int64_t q_pos0,
+                                                             const int32_t* __restrict__ n_valid, int32_t k,
+                                                             int32_t* __restrict__ idx, int32_t n_words) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
+  uint32_t* gt_bits = reinterpret_cast<uint32_t*>(smem + sizeof(TopkShared));
+  uint32_t* eq_bits = gt_bits + n_words;
+
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  int64_t n = n_valid ? (int64_t)n_valid[t] : q_pos0 + t + 1;
+  n = n < 0 ? 0 : (n > N ? N : n);
+  int32_t* out = idx + t * (int64_t)k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* row = scores + t * ld;
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
+  if (vec && n >= kSampleMinN && topk_sampled(sh, row, n, k, gt_bits, eq_bits, n_words, out)) return;
+  topk_exact_row(sh, row, n, vec, k, gt_bits, eq_bits, n_words, out);
+}
+
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0,
                        const int32_t* n_valid, int32_t k, int32_t* idx, hipStream_t st) {
   if (T <= 0) return hipSuccess;
@@ -411,6 +429,190 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, in
   }
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, T, N, q_pos0,
                      n_valid, k, idx, n_words);
+  return hipGetLastError();
+}
+
+
+// ------------------------------------------------------------ few long rows
+// Decode has a handful of rows, each up to 2^18 keys long: one workgroup per
+// row would stream each row through one CU and leave most CUs idle.  Here the
+// full-row pass is split over 4096-key chunks:
+//   estimate: per row, the sampled threshold estimate t_est of topk_sampled
+//             (1/16 of the row);
+//   collect:  every chunk appends its keys >= t_est to the row's candidate
+//             list (about 1.37k keys per row);
+//   finish:   per row, theta = the k-th largest candidate, "> theta" and
+//             "== theta" marked in LDS bitmaps and emitted in ascending
+//             position order -- the selection rule of topk_kernel.  A row
+//             whose list missed [k, capacity], or too short to sample, takes
+//             topk_kernel's exact path.
+constexpr int kRowChunk = 4096;
+
+struct RowsMeta {
+  uint32_t t_est;   // sampled threshold estimate (0: row takes the exact path)
+  uint32_t n_cand;  // keys >= t_est appended so far
+};
+
+__device__ __forceinline__ int64_t row_len(const int32_t* n_valid, int64_t t, int64_t N) {
+  int64_t n = n_valid[t];
+  return n < 0 ? 0 : (n > N ? N : n);
+}
+
+__device__ __forceinline__ bool row_sampled(const float* row, int64_t n, int32_t k) {
+  return n > k && n >= kSampleMinN && (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_estimate_kernel(const float* __restrict__ scores,
+                                                                          int64_t ld, int64_t N,
+                                                                          const int32_t* __restrict__ n_valid,
+                                                                          int32_t k, RowsMeta* __restrict__ meta) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
+  uint32_t* sample = reinterpret_cast<uint32_t*>(smem + sizeof(TopkShared));
+  const int64_t t = blockIdx.x;
+  const int64_t n = row_len(n_valid, t, N);
+  const float* row = scores + t * ld;
+  uint32_t t_est = 0u;
+  if (row_sampled(row, n, k)) t_est = sample_estimate(sh, row, n, k, sample);
+  if (threadIdx.x == 0) meta[t] = RowsMeta{t_est, 0u};
+}
+
+__global__ __launch_bounds__(256) void topk_rows_collect_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                 int64_t N, const int32_t* __restrict__ n_valid,
+                                                                 int32_t k, RowsMeta* __restrict__ meta,
+                                                                 uint32_t* __restrict__ cand_key,
+                                                                 int32_t* __restrict__ cand_idx) {
+  __shared__ uint32_t lkey[kRowChunk];
+  __shared__ int32_t lidx[kRowChunk];
+  __shared__ uint32_t ln, base;
+  const int64_t t = blockIdx.y, c = blockIdx.x;
+  const int64_t n = row_len(n_valid, t, N);
+  const int64_t s0 = c * kRowChunk;
+  const float* row = scores + t * ld;
+  if (s0 >= n || !row_sampled(row, n, k)) return;
+  const uint32_t t_est = meta[t].t_est;
+  if (threadIdx.x == 0) ln = 0;
+  __syncthreads();
+  const int64_t s1 = min(s0 + kRowChunk, n);
+  auto visit = [&](int64_t s, float f) {
+    const uint32_t key = order_key(f);
+    if (key >= t_est) {
+      const uint32_t slot = atomicAdd(&ln, 1u);
+      lkey[slot] = key;
+      lidx[slot] = (int32_t)s;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t s = s0 + 4 * (threadIdx.x + 256 * u);
+    if (s + 3 < s1) {
+      const v4f v = *(const v4f*)(row + s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) visit(s + j, v[j]);
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (s + j < s1) visit(s + j, row[s + j]);
+    }
+  }
+  __syncthreads();
+  if (ln == 0) return;
+  if (threadIdx.x == 0) base = atomicAdd(&meta[t].n_cand, ln);
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < ln; i += 256) {
+    const uint32_t slot = base + i;
+    if (slot < (uint32_t)kTopkCap) {
+      cand_key[t * kTopkCap + slot] = lkey[i];
+      cand_idx[t * kTopkCap + slot] = lidx[i];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_finish_kernel(
+    const float* __restrict__ scores, int64_t ld, int64_t N, const int32_t* __restrict__ n_valid, int32_t k,
+    const RowsMeta* __restrict__ meta, const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_idx,
+    int32_t* __restrict__ idx, int32_t n_words_max) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
+  uint32_t* gt_bits = reinterpret_cast<uint32_t*>(smem + sizeof(TopkShared));
+  uint32_t* eq_bits = gt_bits + n_words_max;
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const int64_t n = row_len(n_valid, t, N);
+  int32_t* out = idx + t * (int64_t)k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* row = scores + t * ld;
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  const uint32_t c = row_sampled(row, n, k) ? meta[t].n_cand : 0u;
+  if (c < (uint32_t)k || c > (uint32_t)kTopkCap) {  // uniform: the exact path over the row
+    topk_exact_row(sh, row, n, vec, k, gt_bits, eq_bits, n_words_max, out);
+    return;
+  }
+  const int n_words = (int)((n + 31) / 32);
+  for (int i = tid; i < 2 * n_words_max; i += kTopkThreads) gt_bits[i] = 0u;  // gt and eq maps are adjacent
+  for (int i = tid; i < (int)c; i += kTopkThreads) {
+    sh.list_key[i] = cand_key[t * kTopkCap + i];
+    sh.list_idx[i] = cand_idx[t * kTopkCap + i];
+  }
+  __syncthreads();
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
+  refine_list(sh, (int)c, lo, hi, 0u, 0, (uint32_t)k, sh.list_key);
+  for (int i = tid; i < (int)c; i += kTopkThreads) {
+    const uint32_t key = sh.list_key[i];
+    const int32_t s = sh.list_idx[i];
+    if (key > hi)
+      atomicOr(&gt_bits[s >> 5], 1u << (s & 31));
+    else if (key == hi)
+      atomicOr(&eq_bits[s >> 5], 1u << (s & 31));
+  }
+  __syncthreads();
+  emit_selection(sh, gt_bits, eq_bits, n_words, (uint32_t)k, out);
+}
+
+size_t topk_rows_scratch_bytes(int64_t T, int64_t /*N*/) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  return al(sizeof(RowsMeta) * (size_t)T) + al(sizeof(uint32_t) * (size_t)T * kTopkCap) +
+         al(sizeof(int32_t) * (size_t)T * kTopkCap);
+}
+
+// measured on MI355X: the split pays for rows of 64K keys and more (a 127K
+// row: 48 us against 61 us in one workgroup); at 32K the two are even
+bool topk_rows_preferred(int64_t T, int64_t N) { return T <= 1024 && N >= 65536; }
+
+hipError_t launch_topk_rows(const float* scores, int64_t ld, int64_t T, int64_t N, const int32_t* n_valid,
+                            int32_t k, int32_t* idx, void* scratch, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  const int64_t n_chunks = (N + kRowChunk - 1) / kRowChunk;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* p = (char*)scratch;
+  RowsMeta* meta = (RowsMeta*)p;
+  p += al(sizeof(RowsMeta) * (size_t)T);
+  uint32_t* cand_key = (uint32_t*)p;
+  p += al(sizeof(uint32_t) * (size_t)T * kTopkCap);
+  int32_t* cand_idx = (int32_t*)p;
+  const int32_t n_words = (int32_t)((N + 31) / 32);
+  // the estimate's sample (at most n/4 + 240 bytes) and the finish's bitmaps
+  // (2 x n_words words) both fit the same dynamic LDS as topk_kernel
+  const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words + 256;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const int cap = (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192 + 256);
+    hipError_t e = hipFuncSetAttribute((const void*)topk_rows_finish_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)topk_rows_estimate_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              cap);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(topk_rows_estimate_kernel, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, N,
+                     n_valid, k, meta);
+  hipLaunchKernelGGL(topk_rows_collect_kernel, dim3((unsigned)n_chunks, (unsigned)T), dim3(256), 0, st, scores, ld,
+                     N, n_valid, k, meta, cand_key, cand_idx);
+  hipLaunchKernelGGL(topk_rows_finish_kernel, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, N,
+                     n_valid, k, meta, cand_key, cand_idx, idx, n_words);
   return hipGetLastError();
 }
 

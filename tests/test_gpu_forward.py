@@ -7,8 +7,8 @@ import torch
 
 import oracle
 from oracle import jobs
-from dsa_inputs import configs, device
-from dsa_run import check_attention, check_selection, decode, paged_decode, prefill
+from dsa_inputs import configs, device, gen
+from dsa_run import check_attention, check_selection, decode, paged_decode, prefill, ws_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -105,3 +105,39 @@ def test_prefill_128k_sampled(dsa):
     rows = np.unique(np.concatenate([configs.sample_rows(wl, wl.oracle_rows), np.arange(8), [2047, 2048],
                                      [wl.T - 1]]))
     _prefill_sampled(wl.name, rows)
+
+
+def test_decode_heavy_ties_and_mixed_lengths(dsa):
+    """Long decode rows go through the multi-workgroup top-k.  Keys 0..4095 of
+    every sequence are equal (one shared score) and the rest are zero (score 0),
+    so a row's threshold bin holds thousands of equal scores.
+    Sequences 0 and 3 have 4096 tied keys, more than the candidate list holds,
+    and take the exact path; sequence 1 has 3000.  Contexts also cover a short
+    row (n <= k) and a partial last chunk."""
+    B, N, H_I, H, k = 4, 70000, 4, 8, 2048
+    _case("decode heavy ties")
+    ctx = np.array([70000, 66003, 1500, 65536], dtype=np.int32)
+    key = np.zeros((B, N, 128), dtype=np.uint8)
+    key[:, :4096, :] = 0x38  # 1.0 in every dim
+    key[1, 3000:4096, :] = 0  # sequence 1: 3000 tied keys, few enough for the candidate list
+    key[1, 5000:5100, :] = 0x40  # 2.0: a hundred larger scores in sequence 1
+    q_idx = np.full((B, H_I, 128), 0x38, dtype=np.uint8)  # 1.0
+    w = np.full((B, H_I), 0.5, dtype=np.float32)
+    rng = np.random.default_rng(4)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, H, 576)).astype(np.float32))
+    kv = np.zeros((B, N, 576), dtype=np.uint16)  # the selection does not depend on it
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    nb = dsa.dsa_forward_decode_workspace_bytes(B, N, H, 512, k)
+    ws = ws_tensor(nb)
+    dsa.dsa_forward_decode(dev(q_idx), dev(w), dev(key), dev(q), dev(kv), dev(ctx), B, N, H_I, 128, H, 576, 512, k,
+                           1.0 / np.sqrt(192.0), idx, out, lse, ws, nb)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    for b in range(B):
+        n = int(ctx[b])
+        keys_b = key[b, :n]
+        o = oracle.topk_row(oracle.indexer_row(q_idx[b], w[b], keys_b), k)
+        assert np.array_equal(g[b], o), f"sequence {b}"
