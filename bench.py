@@ -157,6 +157,23 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 3}))
 
 
+def launch_times(dsa, torch, stream, fused, steps: int):
+    """Runs `steps` more fused calls with the library's launch timing on: each
+    kernel stage is bracketed by two HIP events on the stream it is launched on.
+    Returns ({kind: (summed ms, launches)}, ms per step of these calls)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    dsa.dsa_timing_begin()
+    e0.record(stream)
+    for _ in range(steps):
+        fused()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rec = dsa.dsa_timing_end()
+    print(f"[bench] {steps} fused steps with launch events done", file=sys.stderr, flush=True)
+    return rec, e0.elapsed_time(e1) / steps
+
+
 def bench_prefill(args, wl):
     import numpy as np
     import torch
@@ -170,70 +187,61 @@ def bench_prefill(args, wl):
     inp = device.make_prefill_inputs(wl)
     stream = torch.cuda.current_stream()
     tile_rows, ld = dsa.dsa_forward_prefill_plan(T, N)
-    scores = torch.empty((tile_rows, ld), dtype=torch.float32, device="cuda")
-    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    out = torch.empty((T, wl.H, wl.D_v), dtype=torch.float32, device="cuda")
-    lse = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
-    mla_ws_bytes = dsa.dsa_sparse_mla_fwd_workspace_bytes(T, wl.H, wl.D_v, k)
-    mla_ws = torch.empty(max(mla_ws_bytes, 256), dtype=torch.uint8, device="cuda")
     n_tiles = (T + tile_rows - 1) // tile_rows
-
-    ev = {name: [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_tiles)] for name in ("idx", "topk")}
-    ev_mla = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-
-    def step(record: bool):
-        for i in range(n_tiles):
-            r0 = i * tile_rows
-            tr = min(tile_rows, T - r0)
-            if record:
-                ev["idx"][2 * i].record(stream)
-            dsa.dsa_indexer_scores(inp["q_idx"][r0:], inp["w"][r0:], inp["k_idx"], tr, N, wl.H_I, wl.d_I, r0,
-                                   scores, ld)
-            if record:
-                ev["idx"][2 * i + 1].record(stream)
-                ev["topk"][2 * i].record(stream)
-            dsa.dsa_topk(scores, ld, tr, N, r0, None, k, idx[r0:])
-            if record:
-                ev["topk"][2 * i + 1].record(stream)
-        if record:
-            ev_mla[0].record(stream)
-        dsa.dsa_sparse_mla_fwd(inp["q"], inp["kv"], idx, T, N, wl.H, wl.D_qk, wl.D_v, k, wl.scale, out, lse, mla_ws,
-                               mla_ws_bytes)
-        if record:
-            ev_mla[1].record(stream)
-
-    # one fused call: the staged replay must reproduce it bit for bit
-    print("[bench] fused reference call", file=sys.stderr, flush=True)
     fws_bytes = dsa.dsa_forward_prefill_workspace_bytes(T, N, wl.H, wl.D_v, k)
     fws = torch.empty(fws_bytes, dtype=torch.uint8, device="cuda")
-    f_idx = torch.empty_like(idx)
-    f_lse = torch.empty_like(lse)
-    f_out = torch.empty_like(out)
-    t0 = time.perf_counter()
-    dsa.dsa_forward_prefill(inp["q_idx"], inp["w"], inp["k_idx"], inp["q"], inp["kv"], T, N, wl.H_I, wl.d_I, wl.H,
-                            wl.D_qk, wl.D_v, k, 0, wl.scale, f_idx, f_out, f_lse, fws, fws_bytes)
-    torch.cuda.synchronize()
-    fused_ms = (time.perf_counter() - t0) * 1e3
-    del fws
-    print(f"[bench] fused call {fused_ms:.1f} ms; warmup {args.warmup}", file=sys.stderr, flush=True)
+    f_idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    f_out = torch.empty((T, wl.H, wl.D_v), dtype=torch.float32, device="cuda")
+    f_lse = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
 
+    def fused():
+        dsa.dsa_forward_prefill(inp["q_idx"], inp["w"], inp["k_idx"], inp["q"], inp["kv"], T, N, wl.H_I, wl.d_I,
+                                wl.H, wl.D_qk, wl.D_v, k, 0, wl.scale, f_idx, f_out, f_lse, fws, fws_bytes)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step(False)
+        fused()
     torch.cuda.synchronize()
-    stage_ms = {"indexer": 0.0, "topk": 0.0, "sparse_mla": 0.0}
+    # phase A, the timed region: K fused calls
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(True)
-        torch.cuda.synchronize()
-        stage_ms["indexer"] += sum(ev["idx"][2 * i].elapsed_time(ev["idx"][2 * i + 1]) for i in range(n_tiles))
-        stage_ms["topk"] += sum(ev["topk"][2 * i].elapsed_time(ev["topk"][2 * i + 1]) for i in range(n_tiles))
-        stage_ms["sparse_mla"] += ev_mla[0].elapsed_time(ev_mla[1])
-        print(f"[bench] step {s + 1}/{args.steps} done", file=sys.stderr, flush=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fused()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    stage_ms = {kk: v / args.steps for kk, v in stage_ms.items()}
+    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} fused prefill steps done: {ms_per_step:.1f} ms per step", file=sys.stderr,
+          flush=True)
+    # phase B: K more fused calls with the library bracketing each kernel stage by
+    # HIP events on the stream it runs on (the events would perturb phase A)
+    rec_t, ev_ms_per_step = launch_times(dsa, torch, stream, fused, args.steps)
+    stage_ms = {"indexer": rec_t["indexer"][0] / args.steps, "topk": rec_t["topk"][0] / args.steps,
+                "sparse_mla": rec_t["attention"][0] / args.steps}
+    stage_launches = {"indexer": rec_t["indexer"][1] // args.steps, "topk": rec_t["topk"][1] // args.steps,
+                      "sparse_mla": rec_t["attention"][1] // args.steps}
 
+    # the same path replayed stage by stage through the single-stage calls
+    # (untimed): it must reproduce the fused call bit for bit
+    print("[bench] staged replay check", file=sys.stderr, flush=True)
+    scores = torch.empty((tile_rows, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty_like(f_idx)
+    out = torch.empty_like(f_out)
+    lse = torch.empty_like(f_lse)
+    mla_ws_bytes = dsa.dsa_sparse_mla_fwd_workspace_bytes(T, wl.H, wl.D_v, k)
+    mla_ws = torch.empty(max(mla_ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    for i in range(n_tiles):
+        r0 = i * tile_rows
+        tr = min(tile_rows, T - r0)
+        dsa.dsa_indexer_scores(inp["q_idx"][r0:], inp["w"][r0:], inp["k_idx"], tr, N, wl.H_I, wl.d_I, r0, scores, ld)
+        dsa.dsa_topk(scores, ld, tr, N, r0, None, k, idx[r0:])
+    dsa.dsa_sparse_mla_fwd(inp["q"], inp["kv"], idx, T, N, wl.H, wl.D_qk, wl.D_v, k, wl.scale, out, lse, mla_ws,
+                           mla_ws_bytes)
+    torch.cuda.synchronize()
+    del scores, fws
     same = bool(torch.equal(f_idx, idx) and torch.equal(f_lse, lse) and torch.equal(f_out, out))
     del f_out
     w = algorithmic_work(wl, T)
@@ -249,7 +257,7 @@ def bench_prefill(args, wl):
     }
     dom = max(stage_ms, key=stage_ms.get)
     bound, ach, peak, unit = kernels[dom]
-    launches = 1 if dom == "sparse_mla" else n_tiles
+    launches = stage_launches[dom]
     rec = {
         "metric": METRIC,
         "value": T / (ms_per_step * 1e-3),
@@ -258,6 +266,8 @@ def bench_prefill(args, wl):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "gpu_ms_per_step": gpu_ms_per_step,
+        "ms_per_step_with_launch_events": ev_ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -273,7 +283,6 @@ def bench_prefill(args, wl):
         "path_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_per_step,
                           "t_roof_bf16_indexer_ms": t_roof_bf16 * 1e3,
                           "frac_bf16_indexer": t_roof_bf16 * 1e3 / ms_per_step},
-        "fused_call_ms": fused_ms,
         "staged_equals_fused": same,
     }
     if not args.no_cpu:
@@ -381,6 +390,7 @@ def bench_kl(args, wl):
         "warmup": args.warmup,
         "ms_per_step": kl_ms,
         "host_wall_ms_per_step": wall_ms,
+        "ms_per_step_with_launch_events": ev_ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -465,26 +475,18 @@ def bench_decode(args, wl):
     s_lse = torch.empty_like(lse)
     mla_nb = dsa.dsa_sparse_mla_fwd_paged_workspace_bytes(B, wl.H, wl.D_v, k)
     mla_ws = torch.empty(max(mla_nb, 256), dtype=torch.uint8, device="cuda")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
 
-    def staged(record):
-        if record:
-            ev[0].record(stream)
+    def staged():
         dsa.dsa_indexer_scores_paged(inp["q_idx"], inp["w"], k_pool, n_pages, page_table, max_pages, inp["ctx_len"],
                                      wl.page, B, wl.H_I, wl.d_I, max_ctx, scores, ld)
-        if record:
-            ev[1].record(stream)
         dsa.dsa_topk(scores, ld, B, max_ctx, 0, inp["ctx_len"], k, s_idx)
-        if record:
-            ev[2].record(stream)
         dsa.dsa_sparse_mla_fwd_paged(inp["q"], kv_pool, n_pages, page_table, max_pages, inp["ctx_len"], wl.page,
                                      s_idx, B, wl.H, wl.D_qk, wl.D_v, k, wl.scale, s_out, s_lse, mla_ws, mla_nb)
-        if record:
-            ev[3].record(stream)
 
     for _ in range(args.warmup):
         fused()
     torch.cuda.synchronize()
+    # phase A, the timed region: K fused calls
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -496,17 +498,14 @@ def bench_decode(args, wl):
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_per_step = e0.elapsed_time(e1) / args.steps
     print(f"[bench] {args.steps} fused decode steps done", file=sys.stderr, flush=True)
+    # phase B: per-kernel-stage durations from the library's launch events
+    rec_t, ev_ms_per_step = launch_times(dsa, torch, stream, fused, args.steps)
+    stage_ms = {"indexer": rec_t["indexer"][0] / args.steps, "topk": rec_t["topk"][0] / args.steps,
+                "sparse_mla": rec_t["attention"][0] / args.steps}
 
-    for _ in range(args.warmup):
-        staged(False)
-    stage_ms = {"indexer": 0.0, "topk": 0.0, "sparse_mla": 0.0}
-    for _ in range(args.steps):
-        staged(True)
-        torch.cuda.synchronize()
-        stage_ms["indexer"] += ev[0].elapsed_time(ev[1])
-        stage_ms["topk"] += ev[1].elapsed_time(ev[2])
-        stage_ms["sparse_mla"] += ev[2].elapsed_time(ev[3])
-    stage_ms = {kk: v / args.steps for kk, v in stage_ms.items()}
+    # the same step through the single-stage paged calls (untimed) must give the same bits
+    staged()
+    torch.cuda.synchronize()
     same = bool(torch.equal(s_idx, idx) and torch.equal(s_out, out) and torch.equal(s_lse, lse))
 
     w = decode_work(wl, ctx)
@@ -529,6 +528,7 @@ def bench_decode(args, wl):
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "host_wall_ms_per_step": wall_ms,
+        "ms_per_step_with_launch_events": ev_ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -65,6 +65,29 @@ const char* dsa_status_string(dsa_status s);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* dsa_last_error_message(void);
 
+/* Launch timing (a measurement aid; off by default).  After
+ * dsa_timing_begin(), every call below made on the same host thread brackets
+ * each of its kernel stages with two HIP events recorded on the stream the
+ * stage is launched on; dsa_timing_end() stops recording, waits for the
+ * recorded events and writes, for each stage kind i < n_kinds, the summed
+ * durations ms[i] (milliseconds) and the number of launches[i].  A stage is
+ * one kernel, except that the attention stage includes the split combine and
+ * the multi-workgroup decode top-k is its three kernels.  The events add a
+ * few microseconds per launch.  n_kinds may be 0 (just stop); otherwise ms
+ * and launches are host arrays of n_kinds entries.  dsa_timing_begin() drops
+ * any record still pending on the thread.  Errors: DSA_ERR_INVALID_ARG for a
+ * bad n_kinds or NULL array, DSA_ERR_HIP when an event failed (the other
+ * records are still summed). */
+enum {
+  DSA_KERNEL_INDEXER = 0,    /* lightning-indexer scores (prefill and decode) */
+  DSA_KERNEL_TOPK = 1,       /* per-row top-k */
+  DSA_KERNEL_ATTENTION = 2,  /* sparse MLA-MQA attention (+ split combine) */
+  DSA_KERNEL_INDEXER_KL = 3, /* indexer KL loss */
+  DSA_KERNEL_KINDS = 4
+};
+dsa_status dsa_timing_begin(void);
+dsa_status dsa_timing_end(double* ms, int64_t* launches, int32_t n_kinds);
+
 /* ---------------------------------------------------------------------------
  * Lightning-indexer scores, [P1] §2.1.1 (index-score equation).
  *   q_idx  [T, H_I, d_I] FP8   query-side indexer vectors q^I_{t,j}

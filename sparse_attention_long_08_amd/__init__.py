@@ -22,6 +22,8 @@ SIGNATURES = {
     "dsa_abi_version": (_c_i32, []),
     "dsa_status_string": (ctypes.c_char_p, [_c_i32]),
     "dsa_last_error_message": (ctypes.c_char_p, []),
+    "dsa_timing_begin": (_c_i32, []),
+    "dsa_timing_end": (_c_i32, [_c_p, _c_p, _c_i32]),
     "dsa_indexer_scores": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64, _c_p, _c_i64, _c_p]),
     "dsa_indexer_scores_paged": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32, _c_i64, _c_i32,
                                           _c_i32, _c_i64, _c_p, _c_i64, _c_p]),
@@ -100,6 +102,23 @@ def _call(name: str, *args) -> None:
 
 def dsa_abi_version() -> int:
     return load().dsa_abi_version()
+
+
+# stage kinds of dsa_timing_end
+TIMING_KINDS = ("indexer", "topk", "attention", "indexer_kl")
+
+
+def dsa_timing_begin() -> None:
+    _call("dsa_timing_begin")
+
+
+def dsa_timing_end():
+    """Stops launch timing; returns {kind: (summed ms, launches)} for TIMING_KINDS."""
+    n = len(TIMING_KINDS)
+    ms = (ctypes.c_double * n)()
+    launches = (ctypes.c_int64 * n)()
+    _call("dsa_timing_end", ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(launches, ctypes.c_void_p), n)
+    return {kind: (ms[i], launches[i]) for i, kind in enumerate(TIMING_KINDS)}
 
 
 def dsa_indexer_scores(q_idx, w, k_idx, T, N, H_I, d_I, q_pos0, scores, ld, stream=None):

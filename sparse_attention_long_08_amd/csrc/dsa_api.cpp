@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "../../include/dsa.h"
 #include "launch.h"
@@ -31,6 +32,43 @@ dsa_status ok() {
 dsa_status hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// ---- launch timing (dsa_timing_begin / dsa_timing_end): per host thread
+struct TimedLaunch {
+  int32_t kind;
+  hipEvent_t start, stop;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimedLaunch> g_timed;
+
+// Runs `launch` (which enqueues one stage's kernels on st); while timing is
+// on, brackets it with two events recorded on st.
+template <class F>
+hipError_t timed(int32_t kind, hipStream_t st, F&& launch) {
+  if (!g_timing) return launch();
+  TimedLaunch t{kind, nullptr, nullptr};
+  hipError_t e = hipEventCreate(&t.start);
+  if (e != hipSuccess) return e;
+  e = hipEventCreate(&t.stop);
+  if (e == hipSuccess) e = hipEventRecord(t.start, st);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(t.stop, st);
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(t.start);
+    if (t.stop) (void)hipEventDestroy(t.stop);
+    return e;
+  }
+  g_timed.push_back(t);
+  return hipSuccess;
+}
+
+void drop_timed() {
+  for (const TimedLaunch& t : g_timed) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  g_timed.clear();
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -112,6 +150,44 @@ const char* dsa_status_string(dsa_status s) {
 
 const char* dsa_last_error_message(void) { return g_err; }
 
+dsa_status dsa_timing_begin(void) {
+  drop_timed();
+  g_timing = true;
+  return ok();
+}
+
+dsa_status dsa_timing_end(double* ms, int64_t* launches, int32_t n_kinds) {
+  g_timing = false;
+  REQUIRE(n_kinds >= 0 && n_kinds <= DSA_KERNEL_KINDS, DSA_ERR_INVALID_ARG, "n_kinds must be in [0, %d]",
+          DSA_KERNEL_KINDS);
+  if (n_kinds > 0) {
+    if (!ms || !launches) {
+      drop_timed();
+      return fail(DSA_ERR_INVALID_ARG, "ms and launches must not be NULL");
+    }
+    for (int32_t i = 0; i < n_kinds; ++i) {
+      ms[i] = 0.0;
+      launches[i] = 0;
+    }
+  }
+  hipError_t err = hipSuccess;
+  for (const TimedLaunch& t : g_timed) {
+    float f = 0.f;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&f, t.start, t.stop);
+    if (e != hipSuccess) {
+      if (err == hipSuccess) err = e;
+      continue;
+    }
+    if (t.kind < n_kinds) {
+      ms[t.kind] += f;
+      launches[t.kind] += 1;
+    }
+  }
+  drop_timed();
+  return hip_check(err, "timing events");
+}
+
 dsa_status dsa_indexer_scores(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
                               int32_t H_I, int32_t d_I, int64_t q_pos0, float* scores, int64_t ld,
                               dsa_stream_t stream) {
@@ -122,8 +198,12 @@ dsa_status dsa_indexer_scores(const uint8_t* q_idx, const float* w, const uint8_
   if (T == 0) return ok();
   REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(k_idx); REQUIRE_PTR(scores);
   REQUIRE_AL(q_idx); REQUIRE_AL(k_idx); REQUIRE_AL(w); REQUIRE_AL(scores);
-  return hip_check(dsa::launch_indexer_prefill(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, true,
-                                               (hipStream_t)stream),
+  hipStream_t st = (hipStream_t)stream;
+  return hip_check(timed(DSA_KERNEL_INDEXER, st,
+                         [&] {
+                           return dsa::launch_indexer_prefill(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, true,
+                                                              st);
+                         }),
                    "indexer launch");
 }
 
@@ -139,8 +219,12 @@ dsa_status dsa_indexer_scores_paged(const uint8_t* q_idx, const float* w, const 
   REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(scores);
   REQUIRE_AL(q_idx); REQUIRE_AL(w); REQUIRE_AL(scores);
   dsa::PagedArgs pa{page_table, max_pages, page_size, n_pages};
-  return hip_check(dsa::launch_indexer_decode(q_idx, w, k_pool, 0, &pa, ctx_len, B, max_ctx, H_I, scores, ld,
-                                              (hipStream_t)stream),
+  hipStream_t st = (hipStream_t)stream;
+  return hip_check(timed(DSA_KERNEL_INDEXER, st,
+                         [&] {
+                           return dsa::launch_indexer_decode(q_idx, w, k_pool, 0, &pa, ctx_len, B, max_ctx, H_I,
+                                                             scores, ld, st);
+                         }),
                    "paged indexer launch");
 }
 
@@ -154,8 +238,10 @@ dsa_status dsa_topk(const float* scores, int64_t ld, int64_t T, int64_t N, int64
   if (T == 0) return ok();
   REQUIRE_PTR(scores); REQUIRE_PTR(idx);
   REQUIRE_AL(scores); REQUIRE_AL(idx);
-  return hip_check(dsa::launch_topk(scores, ld, T, N, q_pos0, n_valid, k, idx, (hipStream_t)stream),
-                   "top-k launch");
+  hipStream_t st = (hipStream_t)stream;
+  return hip_check(
+      timed(DSA_KERNEL_TOPK, st, [&] { return dsa::launch_topk(scores, ld, T, N, q_pos0, n_valid, k, idx, st); }),
+      "top-k launch");
 }
 
 size_t dsa_sparse_mla_fwd_workspace_bytes(int64_t T, int32_t H, int32_t /*D_v*/, int32_t k) {
@@ -189,7 +275,8 @@ static dsa_status run_mla(const uint16_t* q, const uint16_t* kv, const int32_t* 
     a.part_o = (float*)ws;
     a.part_lse = (float*)((char*)ws + round_up(sizeof(float) * (size_t)T * a.n_split * H * 512));
   }
-  return hip_check(dsa::launch_sparse_mla(a, st), "sparse attention launch");
+  return hip_check(timed(DSA_KERNEL_ATTENTION, st, [&] { return dsa::launch_sparse_mla(a, st); }),
+                   "sparse attention launch");
 }
 
 dsa_status dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int64_t T, int64_t N,
@@ -215,7 +302,9 @@ dsa_status dsa_indexer_kl_fwd(const uint16_t* q, const uint16_t* kv, const int32
   if (T == 0) return ok();
   REQUIRE_PTR(q); REQUIRE_PTR(kv); REQUIRE_PTR(idx); REQUIRE_PTR(lse); REQUIRE_PTR(scores); REQUIRE_PTR(kl);
   REQUIRE_AL(q); REQUIRE_AL(kv); REQUIRE_AL(idx);
-  return hip_check(dsa::launch_indexer_kl(q, kv, N, idx, lse, scores, ld, T, H, k, scale, kl, (hipStream_t)stream),
+  hipStream_t st = (hipStream_t)stream;
+  return hip_check(timed(DSA_KERNEL_INDEXER_KL, st,
+                         [&] { return dsa::launch_indexer_kl(q, kv, N, idx, lse, scores, ld, T, H, k, scale, kl, st); }),
                    "indexer KL launch");
 }
 
@@ -291,11 +380,19 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
   int32_t* sel = idx ? idx : idx_ws;
   for (int64_t r0 = 0; r0 < T; r0 += rows) {
     const int64_t tr = std::min(rows, T - r0);
-    if (dsa_status s = hip_check(dsa::launch_indexer_prefill(q_idx + r0 * H_I * 128, w + r0 * H_I, k_idx, tr, N,
-                                                              H_I, q_pos0 + r0, scores, ld, false, st),
+    if (dsa_status s = hip_check(timed(DSA_KERNEL_INDEXER, st,
+                                       [&] {
+                                         return dsa::launch_indexer_prefill(q_idx + r0 * H_I * 128, w + r0 * H_I,
+                                                                            k_idx, tr, N, H_I, q_pos0 + r0, scores,
+                                                                            ld, false, st);
+                                       }),
                                  "indexer launch"))
       return s;
-    if (dsa_status s = hip_check(dsa::launch_topk(scores, ld, tr, N, q_pos0 + r0, nullptr, k, sel + r0 * k, st),
+    if (dsa_status s = hip_check(timed(DSA_KERNEL_TOPK, st,
+                                       [&] {
+                                         return dsa::launch_topk(scores, ld, tr, N, q_pos0 + r0, nullptr, k,
+                                                                 sel + r0 * k, st);
+                                       }),
                                  "top-k launch"))
       return s;
   }
@@ -342,12 +439,17 @@ static dsa_status run_decode(const uint8_t* q_idx, const float* w, const uint8_t
   void* topk_scratch = p;
   const size_t topk_bytes = decode_topk_ws(B, max_ctx);
   p += topk_bytes;
-  if (dsa_status s = hip_check(dsa::launch_indexer_decode(q_idx, w, keys, stride, paged, ctx_len, B, max_ctx, H_I,
-                                                          scores, ld, st),
+  if (dsa_status s = hip_check(timed(DSA_KERNEL_INDEXER, st,
+                                     [&] {
+                                       return dsa::launch_indexer_decode(q_idx, w, keys, stride, paged, ctx_len, B,
+                                                                         max_ctx, H_I, scores, ld, st);
+                                     }),
                                "decode indexer launch"))
     return s;
-  const hipError_t te = topk_bytes ? dsa::launch_topk_rows(scores, ld, B, max_ctx, ctx_len, k, sel, topk_scratch, st)
-                                   : dsa::launch_topk(scores, ld, B, max_ctx, 0, ctx_len, k, sel, st);
+  const hipError_t te = timed(DSA_KERNEL_TOPK, st, [&] {
+    return topk_bytes ? dsa::launch_topk_rows(scores, ld, B, max_ctx, ctx_len, k, sel, topk_scratch, st)
+                      : dsa::launch_topk(scores, ld, B, max_ctx, 0, ctx_len, k, sel, st);
+  });
   if (dsa_status s = hip_check(te, "top-k launch")) return s;
   const int64_t seq_len = paged ? (int64_t)paged->max_pages * paged->page_size : stride;
   return run_mla(q, kv, sel, B, H, k, scale, out, lse, p, ws_bytes - (size_t)(p - (char*)ws), true, stride,

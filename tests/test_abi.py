@@ -97,3 +97,19 @@ def test_binding_raises():
     with pytest.raises(dsa.DsaError) as e:
         dsa.dsa_indexer_scores(FAKE, FAKE, FAKE, 4, 8, 4, 64, 0, FAKE, 8, stream=0)
     assert e.value.status == 2
+
+
+def test_timing_end_validation():
+    """dsa_timing_end rejects a bad kind count or missing arrays; with nothing
+    recorded it returns zeros (no HIP call is made)."""
+    n = len(dsa.TIMING_KINDS)
+    lib = dsa.load()
+    assert lib.dsa_timing_begin() == 0
+    ms = (ctypes.c_double * 8)()
+    launches = (ctypes.c_int64 * 8)()
+    assert lib.dsa_timing_end(ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(launches, ctypes.c_void_p), n + 1) == 1
+    assert "n_kinds" in lib.dsa_last_error_message().decode()
+    assert lib.dsa_timing_end(None, None, n) == 1
+    assert lib.dsa_timing_end(None, None, 0) == 0
+    assert lib.dsa_timing_begin() == 0
+    assert dsa.dsa_timing_end() == {kind: (0.0, 0) for kind in dsa.TIMING_KINDS}

@@ -141,3 +141,26 @@ def test_decode_heavy_ties_and_mixed_lengths(dsa):
         keys_b = key[b, :n]
         o = oracle.topk_row(oracle.indexer_row(q_idx[b], w[b], keys_b), k)
         assert np.array_equal(g[b], o), f"sequence {b}"
+
+
+def test_launch_timing_counts_and_leaves_results_unchanged(dsa):
+    """With launch timing on, the fused prefill gives the same bits and one
+    record per kernel stage: an indexer and a top-k per row tile, one attention."""
+    wl = configs.WORKLOADS["prefill_L32k"]
+    _case(f"{wl.name} fused prefill with and without launch timing")
+    inp = device.make_prefill_inputs(wl)
+    idx0, out0, lse0 = prefill(wl, inp)
+    dsa.dsa_timing_begin()
+    idx1, out1, lse1 = prefill(wl, inp)
+    rec = dsa.dsa_timing_end()
+    tile_rows, _ = dsa.dsa_forward_prefill_plan(wl.T, wl.N)
+    n_tiles = (wl.T + tile_rows - 1) // tile_rows
+    assert torch.equal(idx0, idx1) and torch.equal(out0, out1) and torch.equal(lse0, lse1)
+    assert rec["indexer"][1] == n_tiles and rec["topk"][1] == n_tiles and rec["attention"][1] == 1
+    assert rec["indexer_kl"] == (0.0, 0)
+    assert all(rec[kk][0] > 0 for kk in ("indexer", "topk", "attention"))
+    # records stop with dsa_timing_end
+    prefill(wl, inp)
+    assert dsa.dsa_timing_end() == {kind: (0.0, 0) for kind in dsa.TIMING_KINDS}
+    del inp, idx0, out0, lse0, idx1, out1, lse1
+    _free()
