@@ -43,6 +43,8 @@ class Workload:
     ctx_lo: int = 0            # paged decode: context lengths uniform in [ctx_lo, ctx_hi]
     ctx_hi: int = 0
     oracle_rows: int = 0       # seeded random rows checked by the oracle (prefill)
+    ctxs: tuple = ()           # paged prefill: tokens of each sequence in the cache, chunk included
+    chunks: tuple = ()         # paged prefill: new query tokens of each sequence (its last ones)
 
     @property
     def seed(self) -> int:
@@ -60,6 +62,8 @@ class Workload:
     @property
     def T(self) -> int:
         """Number of query rows."""
+        if self.kind == "paged_prefill":
+            return int(sum(self.chunks))
         return self.N if self.kind == "prefill" else self.B
 
     def with_k(self, k: int) -> "Workload":
@@ -78,6 +82,15 @@ WORKLOADS = {
                               oracle_rows=256),
     "paged_decode_b32_ctx4k_128k": Workload("paged_decode_b32_ctx4k_128k", "paged_decode", 5, B=32,
                                             N=131072, H_I=64, H=128, k=2048, ctx_lo=4096, ctx_hi=131072),
+    # chunked prefill into a paged cache, several sequences per call: a chunk
+    # after earlier context, a whole prompt, a short chunk after a long
+    # context and a one-token chunk
+    "paged_prefill_mixed": Workload("paged_prefill_mixed", "paged_prefill", 6, B=4, N=16384, H_I=64, H=128,
+                                    k=2048, ctxs=(9000, 2100, 16384, 700), chunks=(1500, 2100, 256, 1),
+                                    oracle_rows=40),
+    # the same call at serving size: 4 sequences of 32K tokens, the last 8K new
+    "paged_prefill_b4_ctx32k_q8k": Workload("paged_prefill_b4_ctx32k_q8k", "paged_prefill", 7, B=4, N=32768,
+                                            H_I=64, H=128, k=2048, ctxs=(32768,) * 4, chunks=(8192,) * 4),
 }
 
 
@@ -135,12 +148,26 @@ def kv_bf16(wl: Workload, seq: int, positions) -> np.ndarray:
 
 
 def ctx_lens(wl: Workload) -> np.ndarray:
-    """Context length of each sequence; the query sits at position ctx-1."""
+    """Context length of each sequence; the (last) query sits at position ctx-1."""
+    if wl.kind == "paged_prefill":
+        return np.array(wl.ctxs, dtype=np.int32)
     if wl.kind == "paged_decode":
         return gen.int_range(wl.seed, gen.STREAM_CTX, np.arange(wl.B), wl.ctx_lo, wl.ctx_hi).astype(np.int32)
     if wl.kind == "decode":
         return np.full(wl.B, wl.N, dtype=np.int32)
     return np.array([wl.N], dtype=np.int32)
+
+
+def chunk_rows(wl: Workload):
+    """Paged prefill query rows: ``(q_start [B+1], seq [T], pos [T])``.  Row r is
+    the query of sequence seq[r] at position pos[r]; its generated values use the
+    logical token index ``seq*S + pos`` as the row index."""
+    ctx = np.array(wl.ctxs, dtype=np.int64)
+    nq = np.array(wl.chunks, dtype=np.int64)
+    q_start = np.concatenate([[0], np.cumsum(nq)]).astype(np.int64)
+    seq = np.repeat(np.arange(wl.B, dtype=np.int64), nq)
+    pos = np.concatenate([np.arange(c - n, c, dtype=np.int64) for c, n in zip(ctx, nq)])
+    return q_start, seq, pos
 
 
 def page_layout(wl: Workload):

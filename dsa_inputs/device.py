@@ -113,3 +113,28 @@ def make_paged_inputs(wl: Workload, device="cuda"):
     return dict(q_idx=q_idx, w=w, k_pool=k_pool, q=q, kv_pool=kv_pool,
                 page_table=torch.from_numpy(pt).to(device), ctx_len=torch.from_numpy(ctx_lens(wl)).to(device),
                 n_pages=P, page_table_host=pt)
+
+
+def make_paged_prefill_inputs(wl: Workload, device="cuda"):
+    """Chunked paged prefill: query rows [T, ...] (row r = token seq*S + pos of
+    the chunks), key/latent pools [P, page, dim] through a shuffled page table."""
+    import torch
+    from .configs import chunk_rows
+    pt, P = page_layout(wl)
+    q_start, seq, pos = chunk_rows(wl)
+    T = int(q_start[-1])
+    qmap = torch.from_numpy(seq * wl.S + pos).to(device)
+    rowmap = torch.from_numpy(pool_rowmap(wl, pt, P)).to(device)
+    q_idx = torch.empty((T, wl.H_I, wl.d_I), dtype=torch.uint8, device=device)
+    w = torch.empty((T, wl.H_I), dtype=torch.float32, device=device)
+    k_pool = torch.empty((P, wl.page, wl.d_I), dtype=torch.uint8, device=device)
+    q = torch.empty((T, wl.H, wl.D_qk), dtype=torch.uint16, device=device)
+    kv_pool = torch.empty((P, wl.page, wl.D_qk), dtype=torch.uint16, device=device)
+    fill(q_idx, T, wl.H_I * wl.d_I, E4M3_NORMAL, wl.seed, gen.STREAM_Q_IDX, rowmap=qmap)
+    fill(w, T, wl.H_I, F32_UNIFORM, wl.seed, gen.STREAM_W, rowmap=qmap)
+    fill(q, T, wl.H * wl.D_qk, BF16_NORMAL, wl.seed, gen.STREAM_Q, rowmap=qmap)
+    fill(k_pool, P * wl.page, wl.d_I, E4M3_NORMAL, wl.seed, gen.STREAM_K_IDX, rowmap=rowmap)
+    fill(kv_pool, P * wl.page, wl.D_qk, BF16_NORMAL, wl.seed, gen.STREAM_KV, div=wl.kv_div, rowmap=rowmap)
+    del rowmap, qmap
+    return dict(q_idx=q_idx, w=w, k_pool=k_pool, q=q, kv_pool=kv_pool, page_table=torch.from_numpy(pt).to(device),
+                n_pages=P, page_table_host=pt, q_start=q_start, ctx_len=ctx_lens(wl).astype(np.int64))

@@ -204,6 +204,39 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
  * kernel).  Host pointers; returns DSA_ERR_INVALID_ARG for T < 1 or N < 1. */
 dsa_status dsa_forward_prefill_plan(int64_t T, int64_t N, int64_t* tile_rows, int64_t* score_ld);
 
+/* Fused chunked prefill of B sequences over paged caches (64-token pages),
+ * several sequences per call.  Sequence b holds ctx_len[b] tokens in the
+ * pools (its new chunk already written there) and contributes the
+ * n_b = q_start[b+1] - q_start[b] query rows q_start[b] .. q_start[b+1]-1,
+ * which are its last n_b tokens: row q_start[b] + i is the query at position
+ * p = ctx_len[b] - n_b + i.  Each query is the one of dsa_forward_prefill at
+ * position p: the indexer scores keys 0..p of its own sequence, the top-k
+ * keeps k of them (ties to the lower position, ascending, -1 padded) and the
+ * attention runs over them.  A chunk with n_b == ctx_len[b] is a whole prompt;
+ * n_b == 1 is a decode step.
+ *   q_idx [total_q, H_I, d_I] FP8, w [total_q, H_I] fp32, q [total_q, H, D_qk]
+ *   bf16, with total_q = q_start[B];
+ *   k_pool [n_pages, page_size, d_I], kv_pool [n_pages, page_size, D_qk];
+ *   page_table [B, max_pages] int32 (device): page j of sequence b, which must
+ *   be a valid page for every j < ceil(ctx_len[b] / page_size);
+ *   q_start [B+1] int64 and ctx_len [B] int64 are HOST arrays (they size the
+ *   launches): q_start[0] == 0, non-decreasing, and
+ *   n_b <= ctx_len[b] <= min(max_pages * page_size, 262144);
+ *   idx [total_q, k] out (logical positions; may be NULL), out
+ *   [total_q, H, D_v] fp32, lse [total_q, H] fp32.
+ * The workspace query takes total_q and the largest ctx_len.  Sequences run
+ * one after another on `stream`, each in row tiles as in dsa_forward_prefill.
+ */
+size_t dsa_forward_prefill_paged_workspace_bytes(int64_t total_q, int64_t max_ctx, int32_t H, int32_t D_v,
+                                                 int32_t k);
+dsa_status dsa_forward_prefill_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool,
+                                     const uint16_t* q, const uint16_t* kv_pool, int64_t n_pages,
+                                     const int32_t* page_table, int32_t max_pages, int32_t page_size,
+                                     const int64_t* q_start, const int64_t* ctx_len, int64_t B, int32_t H_I,
+                                     int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v, int32_t k, float scale,
+                                     int32_t* idx, float* out, float* lse, void* ws, size_t ws_bytes,
+                                     dsa_stream_t stream);
+
 /* Fused decode of B sequences with contiguous caches, one query each:
  *   k_idx [B, N, d_I], kv [B, N, D_qk]; ctx_len [B] (device) with
  *   1 <= ctx_len[b] <= N.  Other arguments as in the calls above.

@@ -168,3 +168,22 @@ def decode_row(wl, b: int, k: int | None = None):
     q = configs.q_bf16(wl, [b])[0]
     out, lse = sparse_mla_row(q, gather_kv(wl, b, idx), wl.scale, wl.D_v)
     return dict(scores=scores, idx=idx, out=out, lse=lse)
+
+
+def paged_prefill_row(wl, b: int, pos: int, keys: np.ndarray | None = None, k: int | None = None):
+    """Oracle chain for the chunked-prefill query of sequence b at position pos:
+    the prefill chain over keys 0..pos of sequence b (row index b*S + pos for
+    the generated query values).  ``keys`` may hold the sequence's key rows
+    (at least pos+1 of them).  The paged layout does not enter the oracle."""
+    from dsa_inputs import configs
+    k = wl.k if k is None else k
+    row = b * wl.S + pos
+    if keys is None:
+        keys = configs.k_idx_bytes(wl, b, np.arange(pos + 1))
+    q_i = configs.q_idx_bytes(wl, [row])[0]
+    w = configs.w_f32(wl, [row])[0]
+    scores = indexer_row(q_i, w, keys[: pos + 1])
+    idx = topk_row(scores, k)
+    q = configs.q_bf16(wl, [row])[0]
+    out, lse = sparse_mla_row(q, gather_kv(wl, b, idx), wl.scale, wl.D_v)
+    return dict(scores=scores, idx=idx, out=out, lse=lse)

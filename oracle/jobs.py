@@ -49,6 +49,21 @@ def decode_job(args):
     return oracle.decode_row(wl, int(b))
 
 
+def paged_prefill_job(args):
+    """args = (workload name, sequence b, position, k or None) -> oracle chain dict."""
+    import oracle
+    from dsa_inputs import configs
+    name, b, pos, k = args
+    wl = _workload(name, k)
+    key = (wl.name, int(b))
+    keys = _keys_cache.get(key)
+    if keys is None:
+        _keys_cache.clear()
+        keys = configs.k_idx_bytes(wl, int(b), np.arange(int(configs.ctx_lens(wl)[b])))
+        _keys_cache[key] = keys
+    return oracle.paged_prefill_row(wl, int(b), int(pos), keys)
+
+
 def default_procs() -> int:
     n = os.cpu_count() or 1
     return max(1, min(16, n))

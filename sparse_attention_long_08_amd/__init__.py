@@ -40,6 +40,10 @@ SIGNATURES = {
     "dsa_forward_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_i64, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "dsa_forward_prefill_plan": (_c_i32, [_c_i64, _c_i64, _c_p, _c_p]),
+    "dsa_forward_prefill_paged_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32]),
+    "dsa_forward_prefill_paged": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i32, _c_i32, _c_p, _c_p,
+                                           _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p,
+                                           _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "dsa_forward_decode_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32]),
     "dsa_forward_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
@@ -169,6 +173,21 @@ def dsa_forward_prefill(q_idx, w, k_idx, q, kv, T, N, H_I, d_I, H, D_qk, D_v, k,
                         ws_bytes, stream=None):
     _call("dsa_forward_prefill", _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(q), _ptr(kv), T, N, H_I, d_I, H, D_qk,
           D_v, k, q_pos0, scale, _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def dsa_forward_prefill_paged_workspace_bytes(total_q, max_ctx, H, D_v, k) -> int:
+    return load().dsa_forward_prefill_paged_workspace_bytes(total_q, max_ctx, H, D_v, k)
+
+
+def dsa_forward_prefill_paged(q_idx, w, k_pool, q, kv_pool, n_pages, page_table, max_pages, page_size, q_start,
+                              ctx_len, B, H_I, d_I, H, D_qk, D_v, k, scale, idx, out, lse, ws, ws_bytes,
+                              stream=None):
+    """q_start ([B+1]) and ctx_len ([B]) are host sequences of ints."""
+    qs = (ctypes.c_int64 * (B + 1))(*[int(x) for x in q_start])
+    cl = (ctypes.c_int64 * max(B, 1))(*[int(x) for x in ctx_len])
+    _call("dsa_forward_prefill_paged", _ptr(q_idx), _ptr(w), _ptr(k_pool), _ptr(q), _ptr(kv_pool), n_pages,
+          _ptr(page_table), max_pages, page_size, ctypes.cast(qs, ctypes.c_void_p), ctypes.cast(cl, ctypes.c_void_p),
+          B, H_I, d_I, H, D_qk, D_v, k, scale, _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def dsa_forward_prefill_plan(T, N):

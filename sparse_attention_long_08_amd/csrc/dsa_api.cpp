@@ -202,7 +202,7 @@ dsa_status dsa_indexer_scores(const uint8_t* q_idx, const float* w, const uint8_
   return hip_check(timed(DSA_KERNEL_INDEXER, st,
                          [&] {
                            return dsa::launch_indexer_prefill(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, true,
-                                                              st);
+                                                              nullptr, st);
                          }),
                    "indexer launch");
 }
@@ -384,7 +384,7 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
                                        [&] {
                                          return dsa::launch_indexer_prefill(q_idx + r0 * H_I * 128, w + r0 * H_I,
                                                                             k_idx, tr, N, H_I, q_pos0 + r0, scores,
-                                                                            ld, false, st);
+                                                                            ld, false, nullptr, st);
                                        }),
                                  "indexer launch"))
       return s;
@@ -398,6 +398,101 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
   }
   return run_mla(q, kv, sel, T, H, k, scale, out, lse, p, ws_bytes - (size_t)(p - (char*)ws), false, N, N,
                  nullptr, nullptr, st);
+}
+
+// ------------------------------------------------------------------ ragged paged prefill
+// Largest split-attention workspace of one sequence's chunk of at most
+// total_q rows (only chunks of fewer than 256 rows are split).
+static size_t chunk_mla_ws(int64_t total_q, int32_t H, int32_t k) {
+  size_t m = 0;
+  for (int64_t t = 1; t <= std::min<int64_t>(total_q, 256); ++t) m = std::max(m, mla_ws(t, H, k));
+  return m;
+}
+
+size_t dsa_forward_prefill_paged_workspace_bytes(int64_t total_q, int64_t max_ctx, int32_t H, int32_t /*D_v*/,
+                                                 int32_t k) {
+  if (total_q <= 0 || max_ctx <= 0 || k <= 0) return 0;
+  const int64_t rows = prefill_tile_rows(total_q, max_ctx);
+  return round_up(sizeof(float) * (size_t)rows * score_ld(max_ctx)) +
+         round_up(sizeof(int32_t) * (size_t)total_q * k) + chunk_mla_ws(total_q, H, k);
+}
+
+dsa_status dsa_forward_prefill_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool,
+                                     const uint16_t* q, const uint16_t* kv_pool, int64_t n_pages,
+                                     const int32_t* page_table, int32_t max_pages, int32_t page_size,
+                                     const int64_t* q_start, const int64_t* ctx_len, int64_t B, int32_t H_I,
+                                     int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v, int32_t k, float scale,
+                                     int32_t* idx, float* out, float* lse, void* ws, size_t ws_bytes,
+                                     dsa_stream_t stream) {
+  REQUIRE(B >= 0, DSA_ERR_INVALID_ARG, "B must be >= 0");
+  if (dsa_status s = check_indexer_shape(H_I, d_I)) return s;
+  if (dsa_status s = check_mla_shape(H, D_qk, D_v, k)) return s;
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (B == 0) return ok();
+  REQUIRE_PTR(q_start);
+  REQUIRE_PTR(ctx_len);
+  REQUIRE(page_size == 64, DSA_ERR_UNSUPPORTED, "page_size must be 64 (got %d)", page_size);
+  REQUIRE(n_pages >= 1 && max_pages >= 1, DSA_ERR_INVALID_ARG, "n_pages and max_pages must be >= 1");
+  REQUIRE(q_start[0] == 0, DSA_ERR_INVALID_ARG, "q_start[0] must be 0 (got %lld)", (long long)q_start[0]);
+  int64_t max_ctx = 1;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t nq = q_start[b + 1] - q_start[b], n = ctx_len[b];
+    REQUIRE(nq >= 0, DSA_ERR_INVALID_ARG, "q_start must be non-decreasing (sequence %lld)", (long long)b);
+    REQUIRE(n >= nq && n <= (int64_t)max_pages * page_size && n <= kMaxCtx, DSA_ERR_INVALID_ARG,
+            "ctx_len[%lld] = %lld must be in [new rows (%lld), min(max_pages*page_size, %lld)]", (long long)b,
+            (long long)n, (long long)nq, (long long)kMaxCtx);
+    max_ctx = std::max(max_ctx, n);
+  }
+  const int64_t total_q = q_start[B];
+  if (total_q == 0) return ok();
+  REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(k_pool); REQUIRE_PTR(q); REQUIRE_PTR(kv_pool);
+  REQUIRE_PTR(page_table); REQUIRE_PTR(out); REQUIRE_PTR(lse);
+  REQUIRE_AL(q_idx); REQUIRE_AL(w); REQUIRE_AL(k_pool); REQUIRE_AL(q); REQUIRE_AL(kv_pool); REQUIRE_AL(out);
+  REQUIRE_AL(lse);
+  if (idx) REQUIRE_AL(idx);
+  const size_t need = dsa_forward_prefill_paged_workspace_bytes(total_q, max_ctx, H, D_v, k);
+  REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  REQUIRE(ws != nullptr, DSA_ERR_INVALID_ARG, "ws is NULL");
+  REQUIRE_AL(ws);
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t rows = prefill_tile_rows(total_q, max_ctx);
+  const int64_t ld = score_ld(max_ctx);
+  char* p = (char*)ws;
+  float* scores = (float*)p;
+  p += round_up(sizeof(float) * (size_t)rows * ld);
+  int32_t* idx_ws = (int32_t*)p;
+  p += round_up(sizeof(int32_t) * (size_t)total_q * k);
+  int32_t* sel = idx ? idx : idx_ws;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t q0 = q_start[b], nq = q_start[b + 1] - q0, n = ctx_len[b];
+    if (nq == 0) continue;
+    // the sequence's page-table row as row 0 of a one-sequence table
+    const dsa::PagedArgs pa{page_table + b * (int64_t)max_pages, max_pages, page_size, n_pages};
+    const int64_t pos0 = n - nq;  // position of the chunk's first query
+    for (int64_t r0 = 0; r0 < nq; r0 += rows) {
+      const int64_t tr = std::min(rows, nq - r0);
+      const int64_t g = q0 + r0;  // first global query row of the tile
+      if (dsa_status s = hip_check(timed(DSA_KERNEL_INDEXER, st,
+                                         [&] {
+                                           return dsa::launch_indexer_prefill(q_idx + g * H_I * 128, w + g * H_I,
+                                                                              k_pool, tr, n, H_I, pos0 + r0, scores,
+                                                                              ld, false, &pa, st);
+                                         }),
+                                   "indexer launch"))
+        return s;
+      if (dsa_status s = hip_check(timed(DSA_KERNEL_TOPK, st,
+                                         [&] {
+                                           return dsa::launch_topk(scores, ld, tr, n, pos0 + r0, nullptr, k,
+                                                                   sel + g * k, st);
+                                         }),
+                                   "top-k launch"))
+        return s;
+    }
+    if (dsa_status s = run_mla(q + q0 * H * 576, kv_pool, sel + q0 * k, nq, H, k, scale, out + q0 * H * 512,
+                               lse + q0 * H, p, ws_bytes - (size_t)(p - (char*)ws), false, 0, n, nullptr, &pa, st))
+      return s;
+  }
+  return ok();
 }
 
 // ------------------------------------------------------------------ fused decode

@@ -117,10 +117,13 @@ __device__ __forceinline__ float head_sum(const Frag (&a)[NT], const float (&wr)
 
 // ---------------------------------------------------------------- prefill
 // Workgroup = NW waves x QW query rows, one key chunk of `key_chunk` keys.
-// grid.x: query blocks of NW*QW rows; grid.y: key chunks.
-template <int NW, int QW, int NT>
+// grid.x: query blocks of NW*QW rows; grid.y: key chunks.  Key s of the
+// sequence is row addr.row(0, s) of k_idx (a contiguous sequence, or pages
+// of a pool through one page-table row); a key without a backing row scores
+// as a zero key.
+template <int NW, int QW, int NT, class Addr>
 __global__ __launch_bounds__(64 * NW, 1) void indexer_prefill_kernel(
-    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx, Addr addr,
     int64_t T, int64_t N, int32_t H_I, int64_t q_pos0, float* __restrict__ scores, int64_t ld,
     int32_t key_chunk, int32_t fill_masked) {
   constexpr int QB = NW * QW;
@@ -158,8 +161,9 @@ __global__ __launch_bounds__(64 * NW, 1) void indexer_prefill_kernel(
     const int64_t s = kg + st_key;
     s0 = (v4i){0, 0, 0, 0};
     s1 = s0;
-    if (s < n_comp) {
-      const v4i* p = (const v4i*)(k_idx + s * kIdxD + st_off);
+    const int64_t row = s < n_comp ? addr.row(0, s) : -1;
+    if (row >= 0) {
+      const v4i* p = (const v4i*)(k_idx + row * kIdxD + st_off);
       s0 = p[0];
       if (kStageBytes == 32) s1 = p[1];
     }
@@ -304,16 +308,28 @@ constexpr int kPrefillQW = 1;
 constexpr int kPrefillChunk = 8192;
 constexpr int kDecodeChunk = 4096;  // keys per decode workgroup: 16 groups of 64 per wave
 
-template <int NT>
-hipError_t prefill_nt(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
+template <int NT, class Addr>
+hipError_t prefill_nt(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, Addr addr, int64_t T, int64_t N,
                       int32_t H_I, int64_t q_pos0, float* scores, int64_t ld, bool fill, hipStream_t st) {
   constexpr int QB = kPrefillNW * kPrefillQW;
   const int64_t n_all = fill ? N : std::min<int64_t>(q_pos0 + T, N);
   dim3 grid((unsigned)((T + QB - 1) / QB), (unsigned)((n_all + kPrefillChunk - 1) / kPrefillChunk));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((indexer_prefill_kernel<kPrefillNW, kPrefillQW, NT>), grid, dim3(64 * kPrefillNW), 0, st, q_idx, w, k_idx, T, N,
-                     H_I, q_pos0, scores, ld, kPrefillChunk, fill ? 1 : 0);
+  hipLaunchKernelGGL((indexer_prefill_kernel<kPrefillNW, kPrefillQW, NT, Addr>), grid, dim3(64 * kPrefillNW), 0, st,
+                     q_idx, w, k_idx, addr, T, N, H_I, q_pos0, scores, ld, kPrefillChunk, fill ? 1 : 0);
   return hipGetLastError();
+}
+
+template <class Addr>
+hipError_t prefill_dispatch(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, Addr addr, int64_t T,
+                            int64_t N, int32_t H_I, int64_t q_pos0, float* scores, int64_t ld, bool fill,
+                            hipStream_t st) {
+  switch ((H_I + 15) / 16) {
+    case 1: return prefill_nt<1>(q_idx, w, k_idx, addr, T, N, H_I, q_pos0, scores, ld, fill, st);
+    case 2: return prefill_nt<2>(q_idx, w, k_idx, addr, T, N, H_I, q_pos0, scores, ld, fill, st);
+    case 3: return prefill_nt<3>(q_idx, w, k_idx, addr, T, N, H_I, q_pos0, scores, ld, fill, st);
+    default: return prefill_nt<4>(q_idx, w, k_idx, addr, T, N, H_I, q_pos0, scores, ld, fill, st);
+  }
 }
 
 template <int NT, class Addr>
@@ -343,14 +359,12 @@ hipError_t decode_dispatch(const uint8_t* q_idx, const float* w, const uint8_t* 
 
 hipError_t launch_indexer_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T,
                                   int64_t N, int32_t H_I, int64_t q_pos0, float* scores, int64_t ld,
-                                  bool fill_masked, hipStream_t st) {
-  const int nt = (H_I + 15) / 16;
-  switch (nt) {
-    case 1: return prefill_nt<1>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
-    case 2: return prefill_nt<2>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
-    case 3: return prefill_nt<3>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
-    default: return prefill_nt<4>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
+                                  bool fill_masked, const PagedArgs* paged, hipStream_t st) {
+  if (paged) {
+    AddrPaged ad{paged->page_table, paged->max_pages, __builtin_ctz((unsigned)paged->page_size), paged->n_pages};
+    return prefill_dispatch(q_idx, w, k_idx, ad, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
   }
+  return prefill_dispatch(q_idx, w, k_idx, AddrSingle{N}, T, N, H_I, q_pos0, scores, ld, fill_masked, st);
 }
 
 hipError_t launch_indexer_decode(const uint8_t* q_idx, const float* w, const uint8_t* keys, int64_t stride,

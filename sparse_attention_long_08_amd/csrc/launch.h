@@ -16,9 +16,11 @@ struct PagedArgs {
 // Lightning-indexer scores for T query rows of one sequence (rows at
 // positions q_pos0 + t) over keys 0..N-1.  fill_masked: also write -inf to
 // the non-candidate keys s < N; otherwise only candidates are written.
+// Keys are rows 0..N-1 of k_idx, or (paged != nullptr) pool rows through
+// page-table row 0 of `paged`.
 hipError_t launch_indexer_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T,
                                   int64_t N, int32_t H_I, int64_t q_pos0, float* scores, int64_t ld,
-                                  bool fill_masked, hipStream_t st);
+                                  bool fill_masked, const PagedArgs* paged, hipStream_t st);
 
 // Indexer scores for B decode queries; keys of sequence b are either rows
 // b*stride + s of k_idx (paged == nullptr) or pool rows via the page table.

@@ -113,3 +113,22 @@ def test_timing_end_validation():
     assert lib.dsa_timing_end(None, None, 0) == 0
     assert lib.dsa_timing_begin() == 0
     assert dsa.dsa_timing_end() == {kind: (0.0, 0) for kind in dsa.TIMING_KINDS}
+
+
+@pytest.mark.parametrize("q_start,ctx,page_size,status,needle", [
+    ([1, 4], [8], 64, 1, "q_start[0]"),
+    ([0, 4, 2], [8, 8], 64, 1, "non-decreasing"),
+    ([0, 9], [8], 64, 1, "ctx_len[0]"),            # more new rows than tokens
+    ([0, 4], [64 * 4 + 1], 64, 1, "ctx_len[0]"),   # beyond max_pages * page_size
+    ([0, 4], [8], 32, 2, "page_size"),
+])
+def test_paged_prefill_validation(q_start, ctx, page_size, status, needle):
+    B = len(ctx)
+    qs = (ctypes.c_int64 * (B + 1))(*q_start)
+    cl = (ctypes.c_int64 * B)(*ctx)
+    lib = dsa.load()
+    st = lib.dsa_forward_prefill_paged(FAKE, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 4, page_size,
+                                       ctypes.cast(qs, ctypes.c_void_p), ctypes.cast(cl, ctypes.c_void_p), B, 64,
+                                       128, 8, 576, 512, 32, 0.07, 0, FAKE, FAKE, FAKE, 1 << 30, 0)
+    assert st == status
+    assert needle in lib.dsa_last_error_message().decode()

@@ -164,3 +164,52 @@ def test_launch_timing_counts_and_leaves_results_unchanged(dsa):
     assert dsa.dsa_timing_end() == {kind: (0.0, 0) for kind in dsa.TIMING_KINDS}
     del inp, idx0, out0, lse0, idx1, out1, lse1
     _free()
+
+
+def test_paged_prefill_mixed(dsa):
+    """Chunked prefill of four sequences into a paged cache in one call: a chunk
+    after 7500 cached tokens, a whole 2100-token prompt, 256 new tokens after
+    16128 and a one-token chunk.  Sequences 0 and 1 must equal the contiguous
+    fused prefill of the same keys bit for bit (only the key addressing differs);
+    sampled rows of every sequence are checked against the oracle."""
+    wl = configs.WORKLOADS["paged_prefill_mixed"]
+    _case(f"{wl.name}: forward_prefill_paged")
+    inp = device.make_paged_prefill_inputs(wl)
+    q_start, seq, pos = configs.chunk_rows(wl)
+    T, k, ctx = wl.T, wl.k, inp["ctx_len"]
+    pt = inp["page_table"]
+    nb = dsa.dsa_forward_prefill_paged_workspace_bytes(T, int(ctx.max()), wl.H, wl.D_v, k)
+    ws = ws_tensor(nb)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, wl.H, wl.D_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, wl.H), dtype=torch.float32, device="cuda")
+    dsa.dsa_forward_prefill_paged(inp["q_idx"], inp["w"], inp["k_pool"], inp["q"], inp["kv_pool"], inp["n_pages"], pt,
+                                  pt.shape[1], wl.page, q_start, ctx, wl.B, wl.H_I, wl.d_I, wl.H, wl.D_qk, wl.D_v, k,
+                                  wl.scale, idx, out, lse, ws, nb)
+    torch.cuda.synchronize()
+    for b in (0, 1):
+        _case(f"{wl.name}: sequence {b} against the contiguous fused prefill")
+        n, q0, q1 = int(ctx[b]), int(q_start[b]), int(q_start[b + 1])
+        s = np.arange(n)
+        rows = torch.from_numpy(inp["page_table_host"][b][s // wl.page].astype(np.int64) * wl.page + s % wl.page).cuda()
+        k_c = inp["k_pool"].view(-1, wl.d_I)[rows].contiguous()
+        kv_c = inp["kv_pool"].view(torch.int16).view(-1, wl.D_qk)[rows].contiguous().view(torch.uint16)
+        cnb = dsa.dsa_forward_prefill_workspace_bytes(q1 - q0, n, wl.H, wl.D_v, k)
+        cws = ws_tensor(cnb)
+        c_idx = torch.empty((q1 - q0, k), dtype=torch.int32, device="cuda")
+        c_out = torch.empty((q1 - q0, wl.H, wl.D_v), dtype=torch.float32, device="cuda")
+        c_lse = torch.empty((q1 - q0, wl.H), dtype=torch.float32, device="cuda")
+        dsa.dsa_forward_prefill(inp["q_idx"][q0:q1], inp["w"][q0:q1], k_c, inp["q"][q0:q1], kv_c, q1 - q0, n, wl.H_I,
+                                wl.d_I, wl.H, wl.D_qk, wl.D_v, k, n - (q1 - q0), wl.scale, c_idx, c_out, c_lse, cws,
+                                cnb)
+        torch.cuda.synchronize()
+        assert torch.equal(idx[q0:q1], c_idx)
+        assert torch.equal(out[q0:q1], c_out) and torch.equal(lse[q0:q1], c_lse)
+        del k_c, kv_c, cws, c_idx, c_out, c_lse
+    g_idx, g_out, g_lse = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    del inp, idx, out, lse, ws
+    _free()
+    ends = np.concatenate([q_start[:-1], q_start[1:] - 1])
+    rows = np.unique(np.concatenate([configs.sample_rows(wl, wl.oracle_rows), ends]))
+    results = jobs.run(jobs.paged_prefill_job, [(wl.name, int(seq[r]), int(pos[r]), None) for r in rows])
+    _check_rows(wl.name, rows, results, g_idx[rows], g_out[rows], g_lse[rows], wl.k)

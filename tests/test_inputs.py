@@ -84,3 +84,19 @@ def test_sample_rows():
     r = configs.sample_rows(wl, 256)
     assert len(r) == 256 and len(np.unique(r)) == 256 and r.min() >= 0 and r.max() < wl.T
     assert np.array_equal(r, configs.sample_rows(wl, 256))
+
+
+def test_chunk_rows_layout():
+    """Paged-prefill rows: chunk b's rows are the last chunks[b] positions of
+    sequence b, in order, and q_start delimits them."""
+    wl = configs.WORKLOADS["paged_prefill_mixed"]
+    q_start, seq, pos = configs.chunk_rows(wl)
+    assert q_start[0] == 0 and q_start[-1] == wl.T == len(seq) == len(pos)
+    for b, (c, n) in enumerate(zip(wl.ctxs, wl.chunks)):
+        sl = slice(q_start[b], q_start[b + 1])
+        assert np.all(seq[sl] == b)
+        assert np.array_equal(pos[sl], np.arange(c - n, c))
+    assert list(configs.ctx_lens(wl)) == list(wl.ctxs)
+    pt, P = configs.page_layout(wl)
+    assert P == sum((c + wl.page - 1) // wl.page for c in wl.ctxs)
+    assert sorted(pt[pt >= 0].tolist()) == list(range(P))
