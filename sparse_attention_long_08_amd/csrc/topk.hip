@@ -239,6 +239,74 @@ __device__ __forceinline__ void refine_list(TopkShared& sh, int nl, uint32_t& lo
   }
 }
 
+// Smallest and largest of the nl keys in LDS (block-wide; every thread gets
+// both).
+__device__ __forceinline__ void block_minmax(TopkShared& sh, int nl, const uint32_t* keys, uint32_t* mn,
+                                             uint32_t* mx) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
+  for (int i = tid; i < nl; i += kTopkThreads) {
+    const uint32_t key = keys[i];
+    a = min(a, key);
+    b = max(b, key);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    a = min(a, (uint32_t)__shfl_xor((int)a, d, 64));
+    b = max(b, (uint32_t)__shfl_xor((int)b, d, 64));
+  }
+  if (lane == 0) {
+    sh.wave_a[wave] = a;
+    sh.wave_b[wave] = b;
+  }
+  __syncthreads();
+  a = sh.wave_a[0];
+  b = sh.wave_b[0];
+#pragma unroll
+  for (int w = 1; w < kTopkWaves; ++w) {
+    a = min(a, sh.wave_a[w]);
+    b = max(b, sh.wave_b[w]);
+  }
+  *mn = a;
+  *mx = b;
+  __syncthreads();
+}
+
+// Radix selection of the k-th largest of the nl keys in LDS (k <= nl) over
+// the bits in which the keys differ: the bits above the highest bit where the
+// smallest and largest key differ are common to all, and each level
+// histograms the next (up to) 12 bits below them, so the bins spread over the
+// keys' actual range.  After `levels` levels (or when every bit is resolved)
+// returns the lowest key of the window holding the k-th largest: at least k
+// keys are >= it, and it is the k-th largest exactly when the window is a
+// single key, which takes at most three levels.
+__device__ __forceinline__ uint32_t select_in_list(TopkShared& sh, int nl, const uint32_t* keys, uint32_t k,
+                                                   int levels) {
+  const int tid = threadIdx.x;
+  uint32_t mn, mx;
+  block_minmax(sh, nl, keys, &mn, &mx);
+  int top = mn == mx ? 0 : 32 - __clz(mn ^ mx);  // low bits in which keys differ
+  const uint32_t low_mask = top == 32 ? 0xFFFFFFFFu : ((1u << top) - 1u);
+  uint32_t lo = mn & ~low_mask, hi = lo | low_mask, above = 0u;
+  for (int level = 0; level < levels && top > 0; ++level) {
+    const int shift = top > 12 ? top - 12 : 0, nb = 1 << (top - shift);
+    for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < nl; i += kTopkThreads) {
+      const uint32_t key = keys[i];
+      if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_bin(sh, nb, above, k);
+    above = sh.sel_above;
+    lo |= sh.sel_bin << shift;
+    hi = lo | (shift == 0 ? 0u : ((1u << shift) - 1u));
+    top = shift;
+    __syncthreads();
+  }
+  return lo;
+}
+
 // Sampled path (see the file comment).  Returns false, having written
 // nothing, when the gathered list misses [k, capacity]; the caller then takes
 // the exact path.  Needs a 16-byte aligned row with n >= kSampleMinN; the
@@ -276,9 +344,7 @@ __device__ __forceinline__ uint32_t sample_estimate(TopkShared& sh, const float*
   int64_t rs = (target * m + n - 1) / n;
   if (rs < 1) rs = 1;
   if (rs > m) rs = m;
-  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-  refine_list(sh, m, lo, hi, 0u, 0, (uint32_t)rs, sample);
-  return lo;
+  return select_in_list(sh, m, sample, (uint32_t)rs, 2);
 }
 
 __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __restrict__ row, int64_t n, int32_t k,
@@ -286,7 +352,6 @@ __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __rest
                                              int32_t* __restrict__ out) {
   const int tid = threadIdx.x;
   const uint32_t t_est = sample_estimate(sh, row, n, k, gt_bits);
-  uint32_t lo, hi;
 
   if (tid == 0) sh.list_n = 0;
   __syncthreads();
@@ -303,9 +368,7 @@ __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __rest
   const uint32_t c = sh.list_n;
   if (c < (uint32_t)k || c > (uint32_t)kTopkCap) return false;  // uniform across the workgroup
 
-  lo = 0u;
-  hi = 0xFFFFFFFFu;
-  refine_list(sh, (int)c, lo, hi, 0u, 0, (uint32_t)k, sh.list_key);
+  const uint32_t hi = select_in_list(sh, (int)c, sh.list_key, (uint32_t)k, 3);  // theta, the k-th largest
   for (int i = tid; i < 2 * n_words; i += kTopkThreads) gt_bits[i] = 0;  // gt and eq maps are adjacent
   __syncthreads();
   for (int i = tid; i < (int)c; i += kTopkThreads) {
@@ -557,8 +620,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_finish_kernel(
     sh.list_idx[i] = cand_idx[t * kTopkCap + i];
   }
   __syncthreads();
-  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-  refine_list(sh, (int)c, lo, hi, 0u, 0, (uint32_t)k, sh.list_key);
+  const uint32_t hi = select_in_list(sh, (int)c, sh.list_key, (uint32_t)k, 3);  // theta, the k-th largest
   for (int i = tid; i < (int)c; i += kTopkThreads) {
     const uint32_t key = sh.list_key[i];
     const int32_t s = sh.list_idx[i];
