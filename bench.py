@@ -3,10 +3,12 @@
 One step = the whole path (lightning indexer -> top-k -> sparse MLA-MQA) over
 all query rows of the 128K-context causal prefill (L = 131072, k = 2048,
 H_I = 64 FP8 indexer heads, 128 MLA heads over 576-d bf16 latents), with
-inputs already resident in HBM.  The step replays dsa_forward_prefill stage by
-stage through the C ABI (same kernels, same row tiling, same stream), with HIP
-events around every launch to time each kernel; the staged outputs are checked
-bit-identical to one fused call.
+inputs already resident in HBM: one fused dsa_forward_prefill call.  Phase A
+times K fused calls (the headline); phase B runs K more with the library's
+launch timing on, which brackets every kernel stage with HIP events on the
+stream it runs on (dsa_timing_begin / dsa_timing_end) and gives the per-kernel
+durations.  Afterwards a stage-by-stage replay through the single-stage calls
+must reproduce the fused outputs bit for bit (skipped with --fused-only).
 
 Prints one JSON line: query-tokens/s, the dominant kernel's roofline, and the
 CPU oracle's rate on a bounded sample of the same workload.
@@ -14,9 +16,14 @@ CPU oracle's rate on a bounded sample of the same workload.
 Other modes (not the headline line):
   --workload decode_b64_ctx32k | paged_decode_b32_ctx4k_128k
       one step = one fused decode call (indexer -> top-k -> split attention ->
-      combine) for the whole batch; per-kernel times come from a staged replay
-      through the paged entry points (the contiguous cache is addressed through
-      an identity page table for it).
+      combine) for the whole batch, timed in the same two phases; the staged
+      check replays it through the paged entry points (the contiguous cache is
+      addressed through an identity page table for it).
+  --workload paged_prefill_b4_ctx32k_q8k
+      one step = one chunked prefill call into a paged cache (4 sequences of
+      32K tokens, the last 8K of each new).
+  --kl
+      the sparse-stage indexer KL loss over all rows of a prefill workload.
   --copy-calibration
       copies a 1 GiB buffer three times with a plain device copy, so that HBM
       byte counters read under a profiler can be scaled against a known size.
@@ -37,18 +44,25 @@ PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per dispatch read with rocprofv3 (FETCH_SIZE and WRITE_SIZE, one counter per run),
+# HBM bytes per stage launch read with rocprofv3 (FETCH_SIZE and WRITE_SIZE, one counter per run,
+# on the fused calls alone: bench.py --fused-only), summed over the kernels of the stage,
 # scaled by what the same counters read for a plain 1 GiB device copy (bytes read =
 # FETCH_SIZE KiB x 1024 x 2.0, bytes written = WRITE_SIZE KiB x 1024 x 1.0).  Each entry holds
 # the hash of the kernel sources the counters were taken on; once a source changes, the
 # figure no longer describes the kernel and the roofline reports traffic as null.
 COUNTER_TRAFFIC = {
-    ("prefill_L128k", "indexer"): ("b42b5075f28ed96d", ("indexer.hip", "common.h", "launch.h"), 1126.01e6),
-    ("prefill_L128k", "topk"): ("9324c7a29d590212", ("topk.hip", "common.h", "launch.h"), 582.68e6),
-    ("prefill_L128k", "sparse_mla"): ("095056b82127bcd9", ("sparse_mla.hip", "common.h", "launch.h"), 219733.72e6),
-    ("paged_decode_b32_ctx4k_128k", "indexer"): ("b42b5075f28ed96d", ("indexer.hip", "common.h", "launch.h"), 278.27e6),
-    ("paged_decode_b32_ctx4k_128k", "topk"): ("9324c7a29d590212", ("topk.hip", "common.h", "launch.h"), 8.87e6),
-    ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("095056b82127bcd9", ("sparse_mla.hip", "common.h", "launch.h"), 197.56e6),
+    ("prefill_L128k", "indexer"): ("166d27d41cca3337", ('indexer.hip', 'common.h', 'launch.h'), 792.32e6),
+    ("prefill_L128k", "sparse_mla"): ("21b19605f99cb93b", ('sparse_mla.hip', 'common.h', 'launch.h'), 215668.50e6),
+    ("prefill_L128k", "topk"): ("23036cef194f03a5", ('topk.hip', 'common.h', 'launch.h'), 582.57e6),
+    ("decode_b64_ctx32k", "sparse_mla"): ("21b19605f99cb93b", ('sparse_mla.hip', 'common.h', 'launch.h'), 353.93e6),
+    ("decode_b64_ctx32k", "indexer"): ("166d27d41cca3337", ('indexer.hip', 'common.h', 'launch.h'), 281.34e6),
+    ("decode_b64_ctx32k", "topk"): ("23036cef194f03a5", ('topk.hip', 'common.h', 'launch.h'), 9.24e6),
+    ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("21b19605f99cb93b", ('sparse_mla.hip', 'common.h', 'launch.h'), 270.74e6),
+    ("paged_decode_b32_ctx4k_128k", "indexer"): ("166d27d41cca3337", ('indexer.hip', 'common.h', 'launch.h'), 278.36e6),
+    ("paged_decode_b32_ctx4k_128k", "topk"): ("23036cef194f03a5", ('topk.hip', 'common.h', 'launch.h'), 10.68e6),
+    ("paged_prefill_b4_ctx32k_q8k", "indexer"): ("166d27d41cca3337", ('indexer.hip', 'common.h', 'launch.h'), 1385.15e6),
+    ("paged_prefill_b4_ctx32k_q8k", "sparse_mla"): ("21b19605f99cb93b", ('sparse_mla.hip', 'common.h', 'launch.h'), 10637.14e6),
+    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("23036cef194f03a5", ('topk.hip', 'common.h', 'launch.h'), 1024.03e6),
 }
 
 
@@ -108,6 +122,9 @@ def main():
     ap.add_argument("--workload", default="prefill_L128k")
     ap.add_argument("--cpu-rows", type=int, default=60, help="query rows the CPU oracle baseline times")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="run only the fused calls (both timing phases): no staged-replay check and no CPU "
+                         "baseline, so that a profiler sees the product path alone")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kl", action="store_true",
                     help="time the sparse-stage indexer KL loss instead of the forward path (prefill_L32k unless "
@@ -230,23 +247,28 @@ def bench_prefill(args, wl):
 
     # the same path replayed stage by stage through the single-stage calls
     # (untimed): it must reproduce the fused call bit for bit
-    print("[bench] staged replay check", file=sys.stderr, flush=True)
-    scores = torch.empty((tile_rows, ld), dtype=torch.float32, device="cuda")
-    idx = torch.empty_like(f_idx)
-    out = torch.empty_like(f_out)
-    lse = torch.empty_like(f_lse)
-    mla_ws_bytes = dsa.dsa_sparse_mla_fwd_workspace_bytes(T, wl.H, wl.D_v, k)
-    mla_ws = torch.empty(max(mla_ws_bytes, 256), dtype=torch.uint8, device="cuda")
-    for i in range(n_tiles):
-        r0 = i * tile_rows
-        tr = min(tile_rows, T - r0)
-        dsa.dsa_indexer_scores(inp["q_idx"][r0:], inp["w"][r0:], inp["k_idx"], tr, N, wl.H_I, wl.d_I, r0, scores, ld)
-        dsa.dsa_topk(scores, ld, tr, N, r0, None, k, idx[r0:])
-    dsa.dsa_sparse_mla_fwd(inp["q"], inp["kv"], idx, T, N, wl.H, wl.D_qk, wl.D_v, k, wl.scale, out, lse, mla_ws,
-                           mla_ws_bytes)
-    torch.cuda.synchronize()
-    del scores, fws
-    same = bool(torch.equal(f_idx, idx) and torch.equal(f_lse, lse) and torch.equal(f_out, out))
+    del fws
+    same = None
+    if not args.fused_only:
+        print("[bench] staged replay check", file=sys.stderr, flush=True)
+        scores = torch.empty((tile_rows, ld), dtype=torch.float32, device="cuda")
+        idx = torch.empty_like(f_idx)
+        out = torch.empty_like(f_out)
+        lse = torch.empty_like(f_lse)
+        mla_ws_bytes = dsa.dsa_sparse_mla_fwd_workspace_bytes(T, wl.H, wl.D_v, k)
+        mla_ws = torch.empty(max(mla_ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        for i in range(n_tiles):
+            r0 = i * tile_rows
+            tr = min(tile_rows, T - r0)
+            dsa.dsa_indexer_scores(inp["q_idx"][r0:], inp["w"][r0:], inp["k_idx"], tr, N, wl.H_I, wl.d_I, r0,
+                                   scores, ld)
+            dsa.dsa_topk(scores, ld, tr, N, r0, None, k, idx[r0:])
+        dsa.dsa_sparse_mla_fwd(inp["q"], inp["kv"], idx, T, N, wl.H, wl.D_qk, wl.D_v, k, wl.scale, out, lse, mla_ws,
+                               mla_ws_bytes)
+        torch.cuda.synchronize()
+        del scores
+        same = bool(torch.equal(f_idx, idx) and torch.equal(f_lse, lse) and torch.equal(f_out, out))
+        del out
     del f_out
     w = algorithmic_work(wl, T)
     hbm_s = (w["idx_bytes"] + w["topk_bytes"] + w["mla_bytes"]) / (PEAK_HBM_GBS * 1e9)
@@ -289,7 +311,7 @@ def bench_prefill(args, wl):
                           "frac_bf16_indexer": t_roof_bf16 * 1e3 / ms_per_step},
         "staged_equals_fused": same,
     }
-    if not args.no_cpu:
+    if not (args.no_cpu or args.fused_only):
         print(f"[bench] CPU oracle baseline on {args.cpu_rows} rows", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
     else:
@@ -397,7 +419,7 @@ def bench_paged_prefill(args, wl):
         "path_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_per_step},
     }
     del inp, ws, idx, out, lse
-    if args.no_cpu:
+    if args.no_cpu or args.fused_only:
         rec["cpu_baseline"] = None
     else:
         rows = configs.sample_rows(wl, max(1, args.cpu_rows // 4))
@@ -625,9 +647,11 @@ def bench_decode(args, wl):
                 "sparse_mla": rec_t["attention"][0] / args.steps}
 
     # the same step through the single-stage paged calls (untimed) must give the same bits
-    staged()
-    torch.cuda.synchronize()
-    same = bool(torch.equal(s_idx, idx) and torch.equal(s_out, out) and torch.equal(s_lse, lse))
+    same = None
+    if not args.fused_only:
+        staged()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(s_idx, idx) and torch.equal(s_out, out) and torch.equal(s_lse, lse))
 
     w = decode_work(wl, ctx)
     total_bytes = w["idx_bytes"] + w["topk_bytes"] + w["mla_bytes"]
