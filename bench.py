@@ -126,6 +126,9 @@ def main():
                     help="run only the fused calls (both timing phases): no staged-replay check and no CPU "
                          "baseline, so that a profiler sees the product path alone")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--dense-kl", action="store_true",
+                    help="time the dense warm-up indexer KL loss (prefill_L32k unless --workload names another "
+                         "prefill workload)")
     ap.add_argument("--kl", action="store_true",
                     help="time the sparse-stage indexer KL loss instead of the forward path (prefill_L32k unless "
                          "--workload names another prefill workload)")
@@ -140,7 +143,7 @@ def main():
 
     from dsa_inputs import configs
 
-    if args.kl and args.workload == ap.get_default("workload"):
+    if (args.kl or args.dense_kl) and args.workload == ap.get_default("workload"):
         args.workload = "prefill_L32k"
     wl = configs.WORKLOADS[args.workload]
     if wl.kind == "paged_prefill":
@@ -148,6 +151,13 @@ def main():
         args.warmup = 1 if args.warmup is None else args.warmup
         return bench_paged_prefill(args, wl)
     decode = wl.kind != "prefill"
+    if args.dense_kl:
+        if decode:
+            print("--dense-kl needs a prefill workload", file=sys.stderr)
+            sys.exit(2)
+        args.steps = 3 if args.steps is None else args.steps
+        args.warmup = 1 if args.warmup is None else args.warmup
+        return bench_dense_kl(args, wl)
     if args.kl:
         if decode:
             print("--kl needs a prefill workload", file=sys.stderr)
@@ -459,6 +469,94 @@ def kl_cpu_baseline(wl, rows: int):
                       f"selection, single-threaded C oracle in fp64, {dt:.1f} s"}
 
 
+def bench_dense_kl(args, wl):
+    """Dense warm-up indexer KL loss ("DeepSeek-V3.2" walk-through §2.3.1) over
+    every query row of a prefill workload: one fused dsa_dense_warmup_loss call
+    per step (indexer scores over row tiles, then the dense KL kernel on each
+    tile), timed in the two phases of the prefill bench."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import sparse_attention_long_08_amd as dsa
+    from dsa_inputs import configs, device
+
+    dsa.load()
+    T, N, H = wl.T, wl.N, wl.H
+    print(f"[bench] generating {wl.name} inputs on the GPU", file=sys.stderr, flush=True)
+    inp = device.make_prefill_inputs(wl)
+    stream = torch.cuda.current_stream()
+    nb = dsa.dsa_dense_warmup_loss_workspace_bytes(T, N)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    kl = torch.empty((T,), dtype=torch.float32, device="cuda")
+
+    def fused():
+        dsa.dsa_dense_warmup_loss(inp["q_idx"], inp["w"], inp["k_idx"], inp["q"], inp["kv"], T, N, wl.H_I, wl.d_I, H,
+                                  wl.D_qk, 0, wl.scale, kl, None, ws, nb)
+
+    for _ in range(args.warmup):
+        fused()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        fused()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(f"[bench] {args.steps} dense warm-up loss steps done: {ms_per_step:.1f} ms per step", file=sys.stderr,
+          flush=True)
+    rec_t, ev_ms_per_step = launch_times(dsa, torch, stream, fused, args.steps)
+    stage_ms = {"indexer": rec_t["indexer"][0] / args.steps, "dense_kl": rec_t["dense_kl"][0] / args.steps}
+    launches = rec_t["dense_kl"][1] // args.steps
+    w = algorithmic_work(wl, T)
+    # the loss needs every causal logit once (2*H*D_qk flop per pair); the kernel
+    # computes them twice (once for the dense lse, once for the divergence)
+    flops = w["pairs"] * 2 * H * wl.D_qk
+    ach = flops / (stage_ms["dense_kl"] * 1e-3) / 1e12
+    rec = {
+        "metric": "DSA dense warm-up indexer KL loss query-tokens/s",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "gpu_ms_per_step": e0.elapsed_time(e1) / args.steps,
+        "ms_per_step_with_launch_events": ev_ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator, device-resident)",
+        "config": {"workload": wl.name, "L": T, "H_I": wl.H_I, "H": H, "D_qk": wl.D_qk, "causal": True,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "dense_kl", "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "launches_per_step": launches, "avg_launch_ms": stage_ms["dense_kl"] / max(launches, 1),
+                     "mfma_issued_tflops": 2 * ach},
+        "stages_ms": stage_ms,
+    }
+    del inp, ws, kl
+    if args.no_cpu or args.fused_only:
+        rec["cpu_baseline"] = None
+    else:
+        rows = configs.sample_rows(wl, max(1, args.cpu_rows // 15))
+        keys = configs.k_idx_bytes(wl, 0, np.arange(int(rows.max()) + 1))
+        print(f"[bench] CPU oracle baseline on {len(rows)} rows", file=sys.stderr, flush=True)
+        t1 = time.perf_counter()
+        for t in rows:
+            oracle.dense_kl_row(wl, int(t), keys)
+        dt = time.perf_counter() - t1
+        rec["cpu_baseline"] = {"value": len(rows) / dt, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{len(rows)} seeded-random query rows of {wl.name} (positions "
+                                         f"{int(rows.min())}..{int(rows.max())}), indexer row + dense attention "
+                                         f"lse + KL over all causal keys, single-threaded C oracle in fp64, "
+                                         f"{dt:.1f} s"}
+    print(json.dumps(rec))
+
+
 def bench_kl(args, wl):
     """Sparse-stage indexer KL loss over every query row of a prefill workload.  Per
     row tile the indexer scores and top-k are computed first (untimed); the
@@ -533,7 +631,6 @@ def bench_kl(args, wl):
         "warmup": args.warmup,
         "ms_per_step": kl_ms,
         "host_wall_ms_per_step": wall_ms,
-        "ms_per_step_with_launch_events": ev_ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -82,8 +82,9 @@ enum {
   DSA_KERNEL_INDEXER = 0,    /* lightning-indexer scores (prefill and decode) */
   DSA_KERNEL_TOPK = 1,       /* per-row top-k */
   DSA_KERNEL_ATTENTION = 2,  /* sparse MLA-MQA attention (+ split combine) */
-  DSA_KERNEL_INDEXER_KL = 3, /* indexer KL loss */
-  DSA_KERNEL_KINDS = 4
+  DSA_KERNEL_INDEXER_KL = 3, /* indexer KL loss (sparse training stage) */
+  DSA_KERNEL_DENSE_KL = 4,   /* indexer KL loss (dense warm-up stage) */
+  DSA_KERNEL_KINDS = 5
 };
 dsa_status dsa_timing_begin(void);
 dsa_status dsa_timing_end(double* ms, int64_t* launches, int32_t n_kinds);
@@ -181,6 +182,33 @@ dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, 
 dsa_status dsa_indexer_kl_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* lse,
                               const float* scores, int64_t ld, int64_t T, int64_t N, int32_t H, int32_t D_qk,
                               int32_t k, float scale, float* kl, dsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Indexer KL loss of the dense warm-up stage, [P1] §2.3.1: for each query t
+ * at position q_pos0 + t, over every key s < n_t = min(q_pos0 + t + 1, N),
+ *   z_h(s) = scale * q[t,h] . kv[s]   (all D_qk dims),
+ *   lse_h  = ln sum_s exp(z_h(s))      (the dense attention's normaliser),
+ *   p(s)   = (1/H) sum_h exp(z_h(s) - lse_h),   r(s) = softmax over the n_t keys of scores[t, s],
+ *   kl[t]  = sum_s p(s) * (ln p(s) - ln r(s)).
+ *   q [T, H, D_qk] bf16, kv [N, D_qk] bf16, scores [T, ld] fp32 (row t holds
+ *   I[t, s] for s < n_t, as dsa_indexer_scores writes it; ld >= N), kl [T]
+ *   fp32 out, lse [T, H] fp32 out (the dense lse_h; may be NULL).
+ * Logit products are bf16 x bf16 with fp32 accumulation; the rest is fp32.
+ * Cost: two passes of dense logits over all n_t keys per query (O(L^2)).
+ */
+dsa_status dsa_indexer_dense_kl_fwd(const uint16_t* q, const uint16_t* kv, const float* scores, int64_t ld,
+                                    int64_t T, int64_t N, int64_t q_pos0, int32_t H, int32_t D_qk, float scale,
+                                    float* kl, float* lse, dsa_stream_t stream);
+
+/* The dense warm-up loss of one sequence fused: indexer scores over row tiles
+ * (as dsa_forward_prefill tiles them, in a workspace score tile) and
+ * dsa_indexer_dense_kl_fwd on each tile.  Inputs as in dsa_forward_prefill;
+ * kl [T] and lse [T, H] (may be NULL) out.  The loss is sum_t kl[t]. */
+size_t dsa_dense_warmup_loss_workspace_bytes(int64_t T, int64_t N);
+dsa_status dsa_dense_warmup_loss(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                                 const uint16_t* kv, int64_t T, int64_t N, int32_t H_I, int32_t d_I, int32_t H,
+                                 int32_t D_qk, int64_t q_pos0, float scale, float* kl, float* lse, void* ws,
+                                 size_t ws_bytes, dsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Fused prefill of one sequence: indexer -> top-k -> sparse attention for the

@@ -187,3 +187,20 @@ def paged_prefill_row(wl, b: int, pos: int, keys: np.ndarray | None = None, k: i
     q = configs.q_bf16(wl, [row])[0]
     out, lse = sparse_mla_row(q, gather_kv(wl, b, idx), wl.scale, wl.D_v)
     return dict(scores=scores, idx=idx, out=out, lse=lse)
+
+
+def dense_kl_row(wl, t: int, k_all: np.ndarray):
+    """Oracle of the dense warm-up loss for prefill query row t ("DeepSeek-V3.2"
+    walk-through §2.3.1): the indexer scores over every causal key 0..t, the
+    dense attention's per-head log-sum-exp over the same keys, and the KL of the
+    head-averaged dense attention against the indexer softmax (indexer_kl_row
+    over all causal rows).  Returns dict(kl, lse, scores)."""
+    from dsa_inputs import configs
+    n = t + 1
+    q_i = configs.q_idx_bytes(wl, [t])[0]
+    w = configs.w_f32(wl, [t])[0]
+    scores = indexer_row(q_i, w, k_all[:n])
+    q = configs.q_bf16(wl, [t])[0]
+    kv = configs.kv_bf16(wl, 0, np.arange(n))
+    _, lse = dense_mla_row(q, kv, n, wl.scale, wl.D_v)
+    return dict(kl=indexer_kl_row(q, kv, wl.scale, scores), lse=lse, scores=scores)

@@ -49,6 +49,15 @@ def decode_job(args):
     return oracle.decode_row(wl, int(b))
 
 
+def dense_kl_job(args):
+    """args = (workload name, row t) -> oracle dense warm-up loss dict."""
+    import oracle
+    name, t = args
+    wl = _workload(name, None)
+    keys = _prefill_keys(wl, t + 1)
+    return oracle.dense_kl_row(wl, int(t), keys)
+
+
 def paged_prefill_job(args):
     """args = (workload name, sequence b, position, k or None) -> oracle chain dict."""
     import oracle

@@ -36,6 +36,11 @@ SIGNATURES = {
                                           _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "dsa_indexer_kl_fwd": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                     _c_f32, _c_p, _c_p]),
+    "dsa_indexer_dense_kl_fwd": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_f32,
+                                          _c_p, _c_p, _c_p]),
+    "dsa_dense_warmup_loss_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
+    "dsa_dense_warmup_loss": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                       _c_i64, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "dsa_forward_prefill_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32]),
     "dsa_forward_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_i64, _c_f32, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
@@ -109,7 +114,7 @@ def dsa_abi_version() -> int:
 
 
 # stage kinds of dsa_timing_end
-TIMING_KINDS = ("indexer", "topk", "attention", "indexer_kl")
+TIMING_KINDS = ("indexer", "topk", "attention", "indexer_kl", "dense_kl")
 
 
 def dsa_timing_begin() -> None:
@@ -163,6 +168,21 @@ def dsa_sparse_mla_fwd_paged(q, kv_pool, n_pages, page_table, max_pages, ctx_len
 def dsa_indexer_kl_fwd(q, kv, idx, lse, scores, ld, T, N, H, D_qk, k, scale, kl, stream=None):
     _call("dsa_indexer_kl_fwd", _ptr(q), _ptr(kv), _ptr(idx), _ptr(lse), _ptr(scores), ld, T, N, H, D_qk, k, scale,
           _ptr(kl), _stream(stream))
+
+
+def dsa_indexer_dense_kl_fwd(q, kv, scores, ld, T, N, q_pos0, H, D_qk, scale, kl, lse=None, stream=None):
+    _call("dsa_indexer_dense_kl_fwd", _ptr(q), _ptr(kv), _ptr(scores), ld, T, N, q_pos0, H, D_qk, scale, _ptr(kl),
+          _ptr(lse), _stream(stream))
+
+
+def dsa_dense_warmup_loss_workspace_bytes(T, N) -> int:
+    return load().dsa_dense_warmup_loss_workspace_bytes(T, N)
+
+
+def dsa_dense_warmup_loss(q_idx, w, k_idx, q, kv, T, N, H_I, d_I, H, D_qk, q_pos0, scale, kl, lse, ws, ws_bytes,
+                          stream=None):
+    _call("dsa_dense_warmup_loss", _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(q), _ptr(kv), T, N, H_I, d_I, H, D_qk,
+          q_pos0, scale, _ptr(kl), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def dsa_forward_prefill_workspace_bytes(T, N, H, D_v, k) -> int:

@@ -308,6 +308,25 @@ dsa_status dsa_indexer_kl_fwd(const uint16_t* q, const uint16_t* kv, const int32
                    "indexer KL launch");
 }
 
+dsa_status dsa_indexer_dense_kl_fwd(const uint16_t* q, const uint16_t* kv, const float* scores, int64_t ld,
+                                    int64_t T, int64_t N, int64_t q_pos0, int32_t H, int32_t D_qk, float scale,
+                                    float* kl, float* lse, dsa_stream_t stream) {
+  REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "T must be >= 0 and N >= 1");
+  REQUIRE(q_pos0 >= 0, DSA_ERR_INVALID_ARG, "q_pos0 must be >= 0");
+  if (dsa_status s = check_mla_shape(H, D_qk, 512, 1)) return s;
+  REQUIRE(ld >= N, DSA_ERR_INVALID_ARG, "ld (%lld) must be >= N (%lld)", (long long)ld, (long long)N);
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (T == 0) return ok();
+  REQUIRE_PTR(q); REQUIRE_PTR(kv); REQUIRE_PTR(scores); REQUIRE_PTR(kl);
+  REQUIRE_AL(q); REQUIRE_AL(kv);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_check(timed(DSA_KERNEL_DENSE_KL, st,
+                         [&] {
+                           return dsa::launch_indexer_dense_kl(q, kv, N, scores, ld, T, q_pos0, H, scale, kl, lse, st);
+                         }),
+                   "dense KL launch");
+}
+
 size_t dsa_sparse_mla_fwd_paged_workspace_bytes(int64_t B, int32_t H, int32_t /*D_v*/, int32_t k) {
   return mla_ws(B, H, k);
 }
@@ -398,6 +417,55 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
   }
   return run_mla(q, kv, sel, T, H, k, scale, out, lse, p, ws_bytes - (size_t)(p - (char*)ws), false, N, N,
                  nullptr, nullptr, st);
+}
+
+// ------------------------------------------------------------------ dense warm-up loss
+size_t dsa_dense_warmup_loss_workspace_bytes(int64_t T, int64_t N) {
+  if (T <= 0 || N <= 0) return 0;
+  return round_up(sizeof(float) * (size_t)prefill_tile_rows(T, N) * score_ld(N));
+}
+
+dsa_status dsa_dense_warmup_loss(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
+                                 const uint16_t* kv, int64_t T, int64_t N, int32_t H_I, int32_t d_I, int32_t H,
+                                 int32_t D_qk, int64_t q_pos0, float scale, float* kl, float* lse, void* ws,
+                                 size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "T must be >= 0 and N >= 1");
+  REQUIRE(N <= kMaxCtx, DSA_ERR_UNSUPPORTED, "N must be <= %lld", (long long)kMaxCtx);
+  REQUIRE(q_pos0 >= 0, DSA_ERR_INVALID_ARG, "q_pos0 must be >= 0");
+  if (dsa_status s = check_indexer_shape(H_I, d_I)) return s;
+  if (dsa_status s = check_mla_shape(H, D_qk, 512, 1)) return s;
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (T == 0) return ok();
+  REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(k_idx); REQUIRE_PTR(q); REQUIRE_PTR(kv); REQUIRE_PTR(kl);
+  REQUIRE_AL(q_idx); REQUIRE_AL(w); REQUIRE_AL(k_idx); REQUIRE_AL(q); REQUIRE_AL(kv);
+  const size_t need = dsa_dense_warmup_loss_workspace_bytes(T, N);
+  REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  REQUIRE(ws != nullptr, DSA_ERR_INVALID_ARG, "ws is NULL");
+  REQUIRE_AL(ws);
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t rows = prefill_tile_rows(T, N);
+  const int64_t ld = score_ld(N);
+  float* scores = (float*)ws;
+  for (int64_t r0 = 0; r0 < T; r0 += rows) {
+    const int64_t tr = std::min(rows, T - r0);
+    if (dsa_status s = hip_check(timed(DSA_KERNEL_INDEXER, st,
+                                       [&] {
+                                         return dsa::launch_indexer_prefill(q_idx + r0 * H_I * 128, w + r0 * H_I,
+                                                                            k_idx, tr, N, H_I, q_pos0 + r0, scores,
+                                                                            ld, false, nullptr, st);
+                                       }),
+                                 "indexer launch"))
+      return s;
+    if (dsa_status s = hip_check(timed(DSA_KERNEL_DENSE_KL, st,
+                                       [&] {
+                                         return dsa::launch_indexer_dense_kl(q + r0 * H * 576, kv, N, scores, ld, tr,
+                                                                             q_pos0 + r0, H, scale, kl + r0,
+                                                                             lse ? lse + r0 * H : nullptr, st);
+                                       }),
+                                 "dense KL launch"))
+      return s;
+  }
+  return ok();
 }
 
 // ------------------------------------------------------------------ ragged paged prefill

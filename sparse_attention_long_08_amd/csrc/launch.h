@@ -75,6 +75,13 @@ hipError_t launch_indexer_kl(const uint16_t* q, const uint16_t* kv, int64_t N, c
                              const float* lse, const float* scores, int64_t ld, int64_t T, int32_t H, int32_t k,
                              float scale, float* kl, hipStream_t st);
 
+// Dense warm-up indexer loss per query (one workgroup per query): KL over
+// all keys s < min(q_pos0 + t + 1, N) of the head-averaged dense attention and
+// the softmax of score row t; optionally the dense lse [T, H].
+hipError_t launch_indexer_dense_kl(const uint16_t* q, const uint16_t* kv, int64_t N, const float* scores, int64_t ld,
+                                   int64_t T, int64_t q_pos0, int32_t H, float scale, float* kl, float* lse,
+                                   hipStream_t st);
+
 // Number of key splits used for T queries of H heads with k entries each.
 int32_t sparse_mla_splits(int64_t T, int32_t H, int32_t k);
 

@@ -132,3 +132,25 @@ def test_paged_prefill_validation(q_start, ctx, page_size, status, needle):
                                        128, 8, 576, 512, 32, 0.07, 0, FAKE, FAKE, FAKE, 1 << 30, 0)
     assert st == status
     assert needle in lib.dsa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((FAKE, FAKE, FAKE, 7, 4, 8, 0, 8, 576, 0.07, FAKE, 0, 0), 1, "ld"),
+    ((FAKE, FAKE, FAKE, 8, 4, 8, -1, 8, 576, 0.07, FAKE, 0, 0), 1, "q_pos0"),
+    ((FAKE, FAKE, FAKE, 8, 4, 8, 0, 8, 512, 0.07, FAKE, 0, 0), 2, "D_qk"),
+    ((FAKE, FAKE, FAKE, 8, 4, 8, 0, 129, 576, 0.07, FAKE, 0, 0), 2, "H"),
+    ((FAKE, FAKE, 0, 8, 4, 8, 0, 8, 576, 0.07, FAKE, 0, 0), 1, "scores"),
+])
+def test_dense_kl_validation(args, status, needle):
+    lib = dsa.load()
+    assert lib.dsa_indexer_dense_kl_fwd(*args) == status
+    assert needle in lib.dsa_last_error_message().decode()
+
+
+def test_dense_warmup_workspace_validation():
+    lib = dsa.load()
+    nb = lib.dsa_dense_warmup_loss_workspace_bytes(8, 16)
+    assert nb >= 8 * 64 * 4
+    st = lib.dsa_dense_warmup_loss(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 4, 128, 8, 576, 0, 0.07, FAKE, 0, FAKE,
+                                   nb - 1, 0)
+    assert st == 3 and "workspace" in lib.dsa_last_error_message().decode()

@@ -97,3 +97,65 @@ def test_indexer_kl_chain(dsa, name, rows):
         o = oracle.indexer_kl_row(qh[i], configs.kv_bf16(wl, 0, sel), wl.scale, g_sc[t, sel].astype(np.float64))
         _check_kl(float(g[t]), o, f"row {r0 + t}")
     assert np.all(np.isfinite(g)) and np.all(g >= -1e-5)
+
+
+# ------------------------------------------------------------------ dense warm-up loss (§2.3.1)
+def _dense_warmup(dsa, wl, inp):
+    T, N = wl.T, wl.N
+    nb = dsa.dsa_dense_warmup_loss_workspace_bytes(T, N)
+    ws = ws_tensor(nb)
+    kl = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((T, wl.H), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_dense_warmup_loss(inp["q_idx"], inp["w"], inp["k_idx"], inp["q"], inp["kv"], T, N, wl.H_I, wl.d_I, wl.H,
+                              wl.D_qk, 0, wl.scale, kl, lse, ws, nb)
+    torch.cuda.synchronize()
+    return kl.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny_prefill_L256", "prefill_L32k"])
+def test_dense_warmup_loss_against_oracle(dsa, name):
+    """The fused dense warm-up loss (indexer over row tiles, then the dense KL
+    kernel) against the oracle: every row of the tiny workload, and the first,
+    block-edge, tile-edge, last and seeded-random rows of the 32K prefill."""
+    from oracle import jobs
+    wl = configs.WORKLOADS[name]
+    _case(f"dense warm-up loss {name}")
+    inp = device.make_prefill_inputs(wl)
+    g_kl, g_lse = _dense_warmup(dsa, wl, inp)
+    del inp
+    torch.cuda.empty_cache()
+    if wl.T <= 256:
+        rows = np.arange(wl.T)
+    else:
+        rows = np.unique(np.concatenate([configs.sample_rows(wl, 16), [0, 1, 31, 32, 33, 2047, 2048, 8191, 8192,
+                                                                        wl.T - 1]]))
+    results = jobs.run(jobs.dense_kl_job, [(name, int(t)) for t in rows])
+    for t, r in zip(rows, results):
+        _check_kl(float(g_kl[t]), r["kl"], f"{name} row {t}")
+        assert np.max(np.abs(g_lse[t] - r["lse"])) <= 1e-3, f"{name} row {t} lse"
+    print(f"[{name}] {len(rows)} dense warm-up rows checked", flush=True)
+
+
+def test_dense_kl_equals_sparse_kl_over_all_keys(dsa):
+    """With S_t = every causal key and the dense lse, the sparse-stage kernel
+    computes the same loss as the dense kernel (two kernels, one definition)."""
+    wl = configs.WORKLOADS["tiny_prefill_L256"]
+    _case("dense KL vs sparse KL over all keys")
+    T, N, H = wl.T, wl.N, wl.H
+    inp = device.make_prefill_inputs(wl)
+    ld = N
+    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores(inp["q_idx"], inp["w"], inp["k_idx"], T, N, wl.H_I, wl.d_I, 0, scores, ld)
+    kl_d = torch.empty((T,), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_dense_kl_fwd(inp["q"], inp["kv"], scores, ld, T, N, 0, H, wl.D_qk, wl.scale, kl_d, lse)
+    k = N
+    idx = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        idx[t, : t + 1] = np.arange(t + 1)
+    kl_s = torch.empty((T,), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_kl_fwd(inp["q"], inp["kv"], torch.from_numpy(idx).cuda(), lse, scores, ld, T, N, H, wl.D_qk, k,
+                           wl.scale, kl_s)
+    torch.cuda.synchronize()
+    a, b = kl_d.cpu().numpy(), kl_s.cpu().numpy()
+    assert np.all(np.abs(a - b) <= 1e-6 + 1e-5 * np.abs(b)), np.max(np.abs(a - b))

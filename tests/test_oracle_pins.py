@@ -336,3 +336,29 @@ def test_indexer_kl_matches_torch_kl_div(seed):
     assert got >= 0.0
     # invariant under a shift of every indexer score
     assert oracle.indexer_kl_row(q, kv, scale, iscore + 7.0) == pytest.approx(got, rel=1e-10, abs=1e-13)
+
+
+def test_dense_kl_row_matches_torch_from_raw_inputs():
+    """The dense warm-up loss driver end to end on the tiny workload against an
+    independent torch fp64 route from the generator's raw bytes (float8_e4m3fn and
+    bfloat16 decoding by torch): indexer scores, per-head softmax over all causal
+    keys, the L1-normalised head sum, and kl_div against the indexer softmax."""
+    wl = configs.WORKLOADS["tiny_prefill_L256"]
+    keys = configs.k_idx_bytes(wl, 0, np.arange(wl.N))
+    f8 = lambda b: torch.from_numpy(np.ascontiguousarray(b)).view(torch.float8_e4m3fn).to(torch.float64)
+    bf = lambda u: torch.from_numpy(np.ascontiguousarray(u).astype(np.int16)).view(torch.bfloat16).to(torch.float64)
+    for t in (0, 1, 37, 255):
+        got = oracle.dense_kl_row(wl, t, keys)
+        n = t + 1
+        qi = f8(configs.q_idx_bytes(wl, [t])[0])                   # [H_I, d]
+        w = torch.from_numpy(configs.w_f32(wl, [t])[0]).to(torch.float64)
+        ki = f8(keys[:n])                                            # [n, d]
+        scores = (torch.relu(qi @ ki.T) * w[:, None]).sum(0)         # [n]
+        q = bf(configs.q_bf16(wl, [t])[0])                           # [H, 576]
+        kv = bf(configs.kv_bf16(wl, 0, np.arange(n)))                # [n, 576]
+        z = q @ kv.T * wl.scale                                      # [H, n]
+        target = torch.softmax(z, dim=1).mean(0)
+        want = torch.nn.functional.kl_div(torch.log_softmax(scores, dim=0), target, reduction="sum").item()
+        assert np.allclose(got["scores"], scores.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(got["lse"], torch.logsumexp(z, dim=1).numpy(), rtol=1e-12, atol=1e-12)
+        assert got["kl"] == pytest.approx(want, rel=1e-10, abs=1e-13)
