@@ -48,21 +48,22 @@ PEAK_HBM_GBS = 8000.0
 # on the fused calls alone: bench.py --fused-only), summed over the kernels of the stage,
 # scaled by what the same counters read for a plain 1 GiB device copy (bytes read =
 # FETCH_SIZE KiB x 1024 x 2.0, bytes written = WRITE_SIZE KiB x 1024 x 1.0).  Each entry holds
-# the hash of the kernel sources the counters were taken on; once a source changes, the
-# figure no longer describes the kernel and the roofline reports traffic as null.
+# the hash of the kernel's device sources (its .hip file and common.h) the counters were taken
+# on; once one changes, the figure no longer describes the kernel and the roofline reports
+# traffic as null.
 COUNTER_TRAFFIC = {
-    ("prefill_L128k", "indexer"): ("166d27d41cca3337", ('indexer.hip', 'common.h', 'launch.h'), 792.32e6),
-    ("prefill_L128k", "sparse_mla"): ("21b19605f99cb93b", ('sparse_mla.hip', 'common.h', 'launch.h'), 215668.50e6),
-    ("prefill_L128k", "topk"): ("23036cef194f03a5", ('topk.hip', 'common.h', 'launch.h'), 582.57e6),
-    ("decode_b64_ctx32k", "sparse_mla"): ("21b19605f99cb93b", ('sparse_mla.hip', 'common.h', 'launch.h'), 353.93e6),
-    ("decode_b64_ctx32k", "indexer"): ("166d27d41cca3337", ('indexer.hip', 'common.h', 'launch.h'), 281.34e6),
-    ("decode_b64_ctx32k", "topk"): ("23036cef194f03a5", ('topk.hip', 'common.h', 'launch.h'), 9.24e6),
-    ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("21b19605f99cb93b", ('sparse_mla.hip', 'common.h', 'launch.h'), 270.74e6),
-    ("paged_decode_b32_ctx4k_128k", "indexer"): ("166d27d41cca3337", ('indexer.hip', 'common.h', 'launch.h'), 278.36e6),
-    ("paged_decode_b32_ctx4k_128k", "topk"): ("23036cef194f03a5", ('topk.hip', 'common.h', 'launch.h'), 10.68e6),
-    ("paged_prefill_b4_ctx32k_q8k", "indexer"): ("166d27d41cca3337", ('indexer.hip', 'common.h', 'launch.h'), 1385.15e6),
-    ("paged_prefill_b4_ctx32k_q8k", "sparse_mla"): ("21b19605f99cb93b", ('sparse_mla.hip', 'common.h', 'launch.h'), 10637.14e6),
-    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("23036cef194f03a5", ('topk.hip', 'common.h', 'launch.h'), 1024.03e6),
+    ("prefill_L128k", "indexer"): ("303923c82ceba6ff", ('indexer.hip', 'common.h'), 792.32e6),
+    ("prefill_L128k", "sparse_mla"): ("9bdce1499cc5dd44", ('sparse_mla.hip', 'common.h'), 215668.50e6),
+    ("prefill_L128k", "topk"): ("cc1bee589465a73c", ('topk.hip', 'common.h'), 582.57e6),
+    ("decode_b64_ctx32k", "sparse_mla"): ("9bdce1499cc5dd44", ('sparse_mla.hip', 'common.h'), 353.93e6),
+    ("decode_b64_ctx32k", "indexer"): ("303923c82ceba6ff", ('indexer.hip', 'common.h'), 281.34e6),
+    ("decode_b64_ctx32k", "topk"): ("cc1bee589465a73c", ('topk.hip', 'common.h'), 9.24e6),
+    ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("9bdce1499cc5dd44", ('sparse_mla.hip', 'common.h'), 270.74e6),
+    ("paged_decode_b32_ctx4k_128k", "indexer"): ("303923c82ceba6ff", ('indexer.hip', 'common.h'), 278.36e6),
+    ("paged_decode_b32_ctx4k_128k", "topk"): ("cc1bee589465a73c", ('topk.hip', 'common.h'), 10.68e6),
+    ("paged_prefill_b4_ctx32k_q8k", "indexer"): ("303923c82ceba6ff", ('indexer.hip', 'common.h'), 1385.15e6),
+    ("paged_prefill_b4_ctx32k_q8k", "sparse_mla"): ("9bdce1499cc5dd44", ('sparse_mla.hip', 'common.h'), 10637.14e6),
+    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("cc1bee589465a73c", ('topk.hip', 'common.h'), 1024.03e6),
 }
 
 
