@@ -213,3 +213,38 @@ def test_paged_prefill_mixed(dsa):
     rows = np.unique(np.concatenate([configs.sample_rows(wl, wl.oracle_rows), ends]))
     results = jobs.run(jobs.paged_prefill_job, [(wl.name, int(seq[r]), int(pos[r]), None) for r in rows])
     _check_rows(wl.name, rows, results, g_idx[rows], g_out[rows], g_lse[rows], wl.k)
+
+
+def test_paged_prefill_empty_chunk_and_page_multiple(dsa):
+    """A call whose sequences include an empty chunk and a context that ends on a
+    page boundary: the empty sequence contributes no rows, and every other row
+    equals the same rows of the mixed workload computed alone."""
+    wl = configs.WORKLOADS["paged_prefill_mixed"]
+    _case(f"{wl.name}: empty chunk and a page-multiple context")
+    inp = device.make_paged_prefill_inputs(wl)
+    q_start, seq, pos = configs.chunk_rows(wl)
+    T, k, ctx, pt = wl.T, wl.k, inp["ctx_len"], inp["page_table"]
+
+    def call(qs, cl, rows, table):
+        nbytes = dsa.dsa_forward_prefill_paged_workspace_bytes(len(rows), int(max(cl)), wl.H, wl.D_v, k)
+        ws = ws_tensor(nbytes)
+        idx = torch.empty((len(rows), k), dtype=torch.int32, device="cuda")
+        out = torch.empty((len(rows), wl.H, wl.D_v), dtype=torch.float32, device="cuda")
+        lse = torch.empty((len(rows), wl.H), dtype=torch.float32, device="cuda")
+        r = torch.from_numpy(np.asarray(rows, dtype=np.int64)).cuda()
+        dsa.dsa_forward_prefill_paged(inp["q_idx"][r].contiguous(), inp["w"][r].contiguous(), inp["k_pool"],
+                                      inp["q"].view(torch.int16)[r].contiguous().view(torch.uint16), inp["kv_pool"],
+                                      inp["n_pages"], table, table.shape[1], wl.page, qs, cl, len(cl), wl.H_I, wl.d_I,
+                                      wl.H, wl.D_qk, wl.D_v, k, wl.scale, idx, out, lse, ws, nbytes)
+        torch.cuda.synchronize()
+        return idx, out, lse
+
+    full = call(q_start, ctx, np.arange(T), pt)
+    # sequence 2 (16384 = 256 pages of context) keeps its 256-row chunk; sequence 0 gets an empty chunk
+    rows2 = np.arange(q_start[2], q_start[3])
+    qs = [0, 0, len(rows2)]
+    sub = call(qs, [int(ctx[0]), int(ctx[2])], rows2, pt[[0, 2]].contiguous())
+    for a, b in zip(sub, full):
+        assert torch.equal(a, b[q_start[2]:q_start[3]])
+    del inp
+    _free()

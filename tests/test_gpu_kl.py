@@ -159,3 +159,22 @@ def test_dense_kl_equals_sparse_kl_over_all_keys(dsa):
     torch.cuda.synchronize()
     a, b = kl_d.cpu().numpy(), kl_s.cpu().numpy()
     assert np.all(np.abs(a - b) <= 1e-6 + 1e-5 * np.abs(b)), np.max(np.abs(a - b))
+
+
+def test_dense_warmup_loss_chunk_matches_full_sequence(dsa):
+    """The dense warm-up loss of rows q_pos0 .. T-1 computed as a chunk (queries
+    starting at q_pos0 over the same keys) equals those rows of the full call."""
+    wl = configs.WORKLOADS["tiny_prefill_L256"]
+    _case("dense warm-up loss: chunk at q_pos0 = 100 against the full sequence")
+    inp = device.make_prefill_inputs(wl)
+    g_kl, g_lse = _dense_warmup(dsa, wl, inp)
+    T, N, q0 = wl.T, wl.N, 100
+    nb = dsa.dsa_dense_warmup_loss_workspace_bytes(T - q0, N)
+    ws = ws_tensor(nb)
+    kl = torch.empty((T - q0,), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T - q0, wl.H), dtype=torch.float32, device="cuda")
+    dsa.dsa_dense_warmup_loss(inp["q_idx"][q0:], inp["w"][q0:], inp["k_idx"], inp["q"][q0:], inp["kv"], T - q0, N,
+                              wl.H_I, wl.d_I, wl.H, wl.D_qk, q0, wl.scale, kl, lse, ws, nb)
+    torch.cuda.synchronize()
+    assert np.array_equal(kl.cpu().numpy(), g_kl[q0:])
+    assert np.array_equal(lse.cpu().numpy(), g_lse[q0:])
