@@ -369,7 +369,11 @@ __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __rest
   if (c < (uint32_t)k || c > (uint32_t)kTopkCap) return false;  // uniform across the workgroup
 
   const uint32_t hi = select_in_list(sh, (int)c, sh.list_key, (uint32_t)k, 3);  // theta, the k-th largest
-  for (int i = tid; i < 2 * n_words; i += kTopkThreads) gt_bits[i] = 0;  // gt and eq maps are adjacent
+  const int rw = (int)((n + 31) / 32);  // bitmap words of this row
+  for (int i = tid; i < rw; i += kTopkThreads) {
+    gt_bits[i] = 0;
+    eq_bits[i] = 0;
+  }
   __syncthreads();
   for (int i = tid; i < (int)c; i += kTopkThreads) {
     const uint32_t key = sh.list_key[i];
@@ -380,7 +384,7 @@ __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __rest
       atomicOr(&eq_bits[s >> 5], 1u << (s & 31));
   }
   __syncthreads();
-  emit_selection(sh, gt_bits, eq_bits, n_words, (uint32_t)k, out);
+  emit_selection(sh, gt_bits, eq_bits, rw, (uint32_t)k, out);
   return true;
 }
 
@@ -413,7 +417,11 @@ __device__ __forceinline__ void topk_exact_row(TopkShared& sh, const float* __re
   }
 
   // ------------------------------------------------------------ collect pass
-  for (int i = tid; i < 2 * n_words; i += kTopkThreads) gt_bits[i] = 0;  // gt and eq maps are adjacent
+  const int rw = (int)((n + 31) / 32);  // bitmap words of this row
+  for (int i = tid; i < rw; i += kTopkThreads) {
+    gt_bits[i] = 0;
+    eq_bits[i] = 0;
+  }
   if (tid == 0) sh.list_n = 0;
   __syncthreads();
   const bool exact = (lo == hi);
@@ -448,7 +456,7 @@ __device__ __forceinline__ void topk_exact_row(TopkShared& sh, const float* __re
     __syncthreads();
   }
 
-  emit_selection(sh, gt_bits, eq_bits, n_words, (uint32_t)k, out);
+  emit_selection(sh, gt_bits, eq_bits, rw, (uint32_t)k, out);
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int64_t ld,
@@ -613,8 +621,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_finish_kernel(
     topk_exact_row(sh, row, n, vec, k, gt_bits, eq_bits, n_words_max, out);
     return;
   }
-  const int n_words = (int)((n + 31) / 32);
-  for (int i = tid; i < 2 * n_words_max; i += kTopkThreads) gt_bits[i] = 0u;  // gt and eq maps are adjacent
+  const int n_words = (int)((n + 31) / 32);  // bitmap words of this row
+  for (int i = tid; i < n_words; i += kTopkThreads) {
+    gt_bits[i] = 0u;
+    eq_bits[i] = 0u;
+  }
   for (int i = tid; i < (int)c; i += kTopkThreads) {
     sh.list_key[i] = cand_key[t * kTopkCap + i];
     sh.list_idx[i] = cand_idx[t * kTopkCap + i];
