@@ -16,7 +16,7 @@
 // Mapping.  One workgroup of 4 waves per query.  Wave w owns heads
 // 32w .. 32w+31 as the N side of 32x32x16 bf16 MFMAs and keeps all 36 query
 // k-steps in registers; selected latent rows arrive 32 at a time in a
-// two-stage LDS ring through the global->LDS DMA (the band-major, swizzled
+// three-stage LDS ring, two blocks ahead, through the global->LDS DMA (the band-major, swizzled
 // layout of the attention kernel).  Per block the logit product gives each
 // lane one head over 16 keys; the probabilities go to an LDS tile
 // [32 keys x 128 heads] and eight threads per key sum them over the heads.
@@ -49,13 +49,16 @@ typedef __attribute__((address_space(3))) uint8_t* lds_u8_ptr;
 // conflict-free for the 16-byte key-tile reads of 32 rows)
 __device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (2 * r)) & 7; }
 
-// The two stages arrive restrict-qualified so the compiler sees that the
-// stage being read is not the one a DMA is writing.
+// The three stages arrive restrict-qualified, so the compiler sees that the
+// stage being read is not the one a DMA is writing; step(cur, ahead, blk)
+// reads block blk from cur and fills `ahead` with block blk + 2.
 template <class Step>
-__device__ __forceinline__ void run_pair(uint8_t* __restrict__ sa, uint8_t* __restrict__ sb, int nb, Step& step) {
-  for (int blk = 0; blk < nb; blk += 2) {
-    step(sa, sb, blk);
+__device__ __forceinline__ void run_triple(uint8_t* __restrict__ sa, uint8_t* __restrict__ sb,
+                                           uint8_t* __restrict__ sc, int nb, Step& step) {
+  for (int blk = 0; blk < nb; blk += 3) {
+    step(sa, sc, blk);
     if (blk + 1 < nb) step(sb, sa, blk + 1);
+    if (blk + 2 < nb) step(sc, sb, blk + 2);
   }
 }
 
@@ -90,6 +93,7 @@ template <bool kBufDma>
 __global__ __launch_bounds__(kThreads, 1) void indexer_kl_kernel(KlParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[kBufBytes];
   __shared__ int32_t rows[kMaxK];                          // latent row of every entry (-1: skipped)
   __shared__ float isel[kMaxK];                            // indexer score of every entry
   __shared__ __attribute__((aligned(16))) float pbuf[kBlk * kMaxHeads];  // P of one block, [key][head]
@@ -177,12 +181,16 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_kl_kernel(KlParams p) {
   float ent = 0.f, cross = 0.f, psum = 0.f;  // per key-owning thread, over all blocks
   const int rkey = tid >> 3, rpart = tid & 7;  // head-sum role: key rkey, heads 16*rpart .. +15
 
-  auto step = [&](uint8_t* cur, uint8_t* nxt, int blk) {
-    // this wave's DMA of blk landed; the barrier makes every wave's land and
-    // frees nxt (read in the previous step) and pbuf (read there too)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  auto step = [&](uint8_t* cur, uint8_t* ahead, int blk) {
+    // this wave's DMA of blk landed (the one of blk+1 may still be in
+    // flight); the barrier makes every wave's land and frees `ahead` (read in
+    // the previous step) and pbuf (read there too)
+    if (blk + 1 < nb)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    if (blk + 1 < nb) gather(nxt, blk + 1);
+    if (blk + 2 < nb) gather(ahead, blk + 2);
     const lds_u8_ptr kb = (lds_u8_ptr)cur;
     v16f acc = {};
     v8bf abuf[kPf + 1];
@@ -221,7 +229,8 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_kl_kernel(KlParams p) {
     }
   };
   if (nb > 0) gather(st0, 0);
-  run_pair(st0, st1, nb, step);
+  if (nb > 1) gather(st1, 1);
+  run_triple(st0, st1, st2, nb, step);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   ent = wave_sum(ent);
@@ -286,18 +295,6 @@ __device__ __forceinline__ void lse_merge(float& m, float& l, float m2, float l2
   if (mm == -INFINITY) return;  // both empty
   l = l * expf(m - mm) + l2 * expf(m2 - mm);
   m = mm;
-}
-
-// The three stages arrive restrict-qualified (see run_pair); step(cur, ahead,
-// blk) reads block blk from cur and fills `ahead` with block blk + 2.
-template <class Step>
-__device__ __forceinline__ void run_triple(uint8_t* __restrict__ sa, uint8_t* __restrict__ sb,
-                                           uint8_t* __restrict__ sc, int nb, Step& step) {
-  for (int blk = 0; blk < nb; blk += 3) {
-    step(sa, sc, blk);
-    if (blk + 1 < nb) step(sb, sa, blk + 1);
-    if (blk + 2 < nb) step(sc, sb, blk + 2);
-  }
 }
 
 template <bool kBufDma>
