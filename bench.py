@@ -45,7 +45,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per stage launch read with rocprofv3 (FETCH_SIZE and WRITE_SIZE, one counter per run,
-# on the fused calls alone: bench.py --fused-only), summed over the kernels of the stage,
+# on the fused calls alone: bench.py --fused-only; the loss kernels in the runs of --kl and
+# --dense-kl, restricted to the kernel), summed over the kernels of the stage,
 # scaled by what the same counters read for a plain 1 GiB device copy (bytes read =
 # FETCH_SIZE KiB x 1024 x 2.0, bytes written = WRITE_SIZE KiB x 1024 x 1.0).  Each entry holds
 # the hash of the kernel's device sources (its .hip file and common.h) the counters were taken
@@ -54,16 +55,18 @@ PEAK_HBM_GBS = 8000.0
 COUNTER_TRAFFIC = {
     ("prefill_L128k", "indexer"): ("303923c82ceba6ff", ('indexer.hip', 'common.h'), 792.32e6),
     ("prefill_L128k", "sparse_mla"): ("9bdce1499cc5dd44", ('sparse_mla.hip', 'common.h'), 215668.50e6),
-    ("prefill_L128k", "topk"): ("cc1bee589465a73c", ('topk.hip', 'common.h'), 582.57e6),
+    ("prefill_L128k", "topk"): ("4c830aaaf7a45691", ('topk.hip', 'common.h'), 582.62e6),
     ("decode_b64_ctx32k", "sparse_mla"): ("9bdce1499cc5dd44", ('sparse_mla.hip', 'common.h'), 353.93e6),
     ("decode_b64_ctx32k", "indexer"): ("303923c82ceba6ff", ('indexer.hip', 'common.h'), 281.34e6),
-    ("decode_b64_ctx32k", "topk"): ("cc1bee589465a73c", ('topk.hip', 'common.h'), 9.24e6),
+    ("decode_b64_ctx32k", "topk"): ("4c830aaaf7a45691", ('topk.hip', 'common.h'), 9.24e6),
     ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("9bdce1499cc5dd44", ('sparse_mla.hip', 'common.h'), 270.74e6),
     ("paged_decode_b32_ctx4k_128k", "indexer"): ("303923c82ceba6ff", ('indexer.hip', 'common.h'), 278.36e6),
-    ("paged_decode_b32_ctx4k_128k", "topk"): ("cc1bee589465a73c", ('topk.hip', 'common.h'), 10.68e6),
+    ("paged_decode_b32_ctx4k_128k", "topk"): ("4c830aaaf7a45691", ('topk.hip', 'common.h'), 10.68e6),
     ("paged_prefill_b4_ctx32k_q8k", "indexer"): ("303923c82ceba6ff", ('indexer.hip', 'common.h'), 1385.15e6),
     ("paged_prefill_b4_ctx32k_q8k", "sparse_mla"): ("9bdce1499cc5dd44", ('sparse_mla.hip', 'common.h'), 10637.14e6),
-    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("cc1bee589465a73c", ('topk.hip', 'common.h'), 1024.03e6),
+    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("4c830aaaf7a45691", ('topk.hip', 'common.h'), 1024.61e6),
+    ("prefill_L32k", "indexer_kl"): ("beab70a6d015ce4e", ('indexer_kl.hip', 'common.h'), 6101.45e6),
+    ("prefill_L32k", "dense_kl"): ("beab70a6d015ce4e", ('indexer_kl.hip', 'common.h'), 105785.78e6),
 }
 
 
@@ -534,8 +537,8 @@ def bench_dense_kl(args, wl):
         "config": {"workload": wl.name, "L": T, "H_I": wl.H_I, "H": H, "D_qk": wl.D_qk, "causal": True,
                    "parallelism": "single GPU"},
         "roofline": {"kernel": "dense_kl", "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                     "launches_per_step": launches, "avg_launch_ms": stage_ms["dense_kl"] / max(launches, 1),
+                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                     "traffic": counter_traffic(wl.name, "dense_kl"), "launches_per_step": launches, "avg_launch_ms": stage_ms["dense_kl"] / max(launches, 1),
                      "mfma_issued_tflops": 2 * ach},
         "stages_ms": stage_ms,
     }
