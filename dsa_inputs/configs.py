@@ -218,3 +218,30 @@ def sample_rows(wl: Workload, count: int) -> np.ndarray:
     _, first = np.unique(cand, return_index=True)
     rows = cand[np.sort(first)][:count]
     return np.sort(rows)
+
+
+def dout_bf16(wl: Workload, rows) -> np.ndarray:
+    """Upstream gradient of the attention output for query rows: bf16 bits,
+    standard normal values, [len(rows), H, D_v]."""
+    rows = _rows(rows)
+    idx = (rows[:, None] * (wl.H * wl.D_v) + np.arange(wl.H * wl.D_v)[None, :]).reshape(-1)
+    v = gen.normal_f32(wl.seed, gen.STREAM_DOUT, idx)
+    return gen.f32_to_bf16_bits(v).reshape(len(rows), wl.H, wl.D_v)
+
+
+def random_selection(wl: Workload, positions, k: int | None = None) -> np.ndarray:
+    """A seeded stand-in for a top-k result, for tests that take the selected
+    set as an input: for a query at position p with n = min(p + 1, N)
+    candidates, all of 0..n-1 when n <= k, else k distinct candidates drawn
+    uniformly; ascending, padded with -1.  int32 [len(positions), k]."""
+    k = wl.k if k is None else k
+    pos = _rows(positions)
+    out = np.full((len(pos), k), -1, dtype=np.int32)
+    for i, p_ in enumerate(pos):
+        n = int(min(p_ + 1, wl.N))
+        if n <= k:
+            out[i, :n] = np.arange(n, dtype=np.int32)
+            continue
+        h = gen.draws(wl.seed, gen.STREAM_SEL, int(p_) * wl.N + np.arange(n, dtype=np.int64))
+        out[i] = np.sort(np.argsort(h, kind="stable")[:k]).astype(np.int32)
+    return out

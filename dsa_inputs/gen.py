@@ -49,6 +49,8 @@ STREAM_KV = 5
 STREAM_CTX = 6
 STREAM_PERM = 7
 STREAM_ROWS = 8
+STREAM_DOUT = 9
+STREAM_SEL = 10
 
 
 def mix64(z: np.ndarray) -> np.ndarray:

@@ -59,6 +59,11 @@ def _load():
         lib.oracle_indexer_kl_row.restype = ctypes.c_double
         lib.oracle_indexer_kl_row.argtypes = [_u16p, _u16p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_double, _f64p]
+        _f64p_opt = ctypes.c_void_p
+        lib.oracle_sparse_mla_bwd_row.restype = None
+        lib.oracle_sparse_mla_bwd_row.argtypes = [_u16p, _u16p, _u16p, ctypes.c_int64, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_double, _f64p, _f64p,
+                                                  _f64p_opt, _f64p_opt]
         _lib = lib
     return _lib
 
@@ -124,6 +129,29 @@ def indexer_kl_row(q: np.ndarray, kv_rows: np.ndarray, scale: float, iscore: np.
     assert iscore.shape[0] == kv_rows.shape[0]
     H, D_qk = q.shape
     return float(_load().oracle_indexer_kl_row(q, kv_rows, kv_rows.shape[0], H, D_qk, float(scale), iscore))
+
+
+def sparse_mla_bwd_row(q: np.ndarray, kv_rows: np.ndarray, dO: np.ndarray, scale: float, magnitudes: bool = False):
+    """Gradient of the MQA attention of q [H, D_qk] over gathered latent rows
+    [m, D_qk] for the upstream gradient dO [H, D_v] (bf16 bits): returns
+    (dq [H, D_qk], dkv_rows [m, D_qk]) and, with magnitudes=True, the two
+    absolute-value sums that bound their rounding ("DeepSeek-V3.2" walk-through
+    §2.1.2 attention equation, §2.3.2 sparse training stage)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kv_rows = np.ascontiguousarray(kv_rows, dtype=np.uint16).reshape(-1, q.shape[1])
+    dO = np.ascontiguousarray(dO, dtype=np.uint16)
+    H, D_qk = q.shape
+    D_v = dO.shape[1]
+    assert dO.shape[0] == H and D_v <= D_qk
+    m = kv_rows.shape[0]
+    dq = np.empty((H, D_qk), dtype=np.float64)
+    dkv = np.empty((m, D_qk), dtype=np.float64)
+    mq = np.empty_like(dq) if magnitudes else None
+    mk = np.empty_like(dkv) if magnitudes else None
+    _load().oracle_sparse_mla_bwd_row(q, kv_rows, dO, m, H, D_qk, D_v, float(scale), dq, dkv,
+                                      None if mq is None else mq.ctypes.data,
+                                      None if mk is None else mk.ctypes.data)
+    return (dq, dkv, mq, mk) if magnitudes else (dq, dkv)
 
 
 # ------------------------------------------------------------------ row drivers

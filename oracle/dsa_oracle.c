@@ -258,3 +258,91 @@ double oracle_indexer_kl_row(const uint16_t* q, const uint16_t* kv_rows, int64_t
   free(kvd);
   return kl;
 }
+
+/* Gradient of the sparse MLA-MQA attention of one query (the attention
+ * equation of [P1] §2.1.2 in the MQA form of §2.2), as the sparse training
+ * stage of [P1] §2.3.2 needs it to train the main model through the sparse
+ * attention.  For a loss L with upstream gradient dO[h][D_v] = dL/du_t[h]:
+ *   z_h(s)  = scale * q[h] . kv[s]            (first D_qk dims)
+ *   P_h(s)  = softmax over the m entries of z_h
+ *   dP_h(s) = dO[h] . kv[s][0..D_v)           (dL/dP_h(s), since u = sum_s P V)
+ *   dZ_h(s) = P_h(s) * (dP_h(s) - sum_s' P_h(s') dP_h(s'))   (softmax Jacobian)
+ *   dq[h]   = scale * sum_s dZ_h(s) kv[s]
+ *   dkv[s]  = scale * sum_h dZ_h(s) q[h]  +  sum_h P_h(s) dO[h]  (the second
+ *             term on the first D_v dims only: the values are those dims)
+ * dq is [H][D_qk]; dkv_rows is [m][D_qk], one row per gathered entry (the
+ * caller adds them into the cache rows the entries came from).
+ * mag_dq / mag_dkv (optional, same shapes) receive the same sums taken over
+ * absolute values, with |dP - D| replaced by A(s) + sum_s' P(s') A(s'), where
+ * A(s) = sum_c |dO[h][c]| |kv[s][c]|: the scale against which rounding of the
+ * terms is measured (P, dP and D each carry a relative error of at most a few
+ * units of the format they were formed in, and A bounds |dP| and D's
+ * sensitivity to P).
+ * m == 0 gives zeros. */
+void oracle_sparse_mla_bwd_row(const uint16_t* q, const uint16_t* kv_rows, const uint16_t* dO, int64_t m,
+                               int32_t H, int32_t D_qk, int32_t D_v, double scale, double* dq, double* dkv_rows,
+                               double* mag_dq, double* mag_dkv) {
+  for (int64_t i = 0; i < (int64_t)H * D_qk; ++i) {
+    dq[i] = 0.0;
+    if (mag_dq) mag_dq[i] = 0.0;
+  }
+  for (int64_t i = 0; i < m * D_qk; ++i) {
+    dkv_rows[i] = 0.0;
+    if (mag_dkv) mag_dkv[i] = 0.0;
+  }
+  if (m == 0) return;
+  double* kvd = (double*)malloc(sizeof(double) * (size_t)m * (size_t)D_qk);
+  double* z = (double*)malloc(sizeof(double) * (size_t)m);
+  double* dp = (double*)malloc(sizeof(double) * (size_t)m);
+  double* adp = (double*)malloc(sizeof(double) * (size_t)m);
+  double* qd = (double*)malloc(sizeof(double) * (size_t)D_qk);
+  double* gd = (double*)malloc(sizeof(double) * (size_t)D_v);
+  for (int64_t i = 0; i < m * D_qk; ++i) kvd[i] = oracle_bf16_to_double(kv_rows[i]);
+  for (int h = 0; h < H; ++h) {
+    for (int c = 0; c < D_qk; ++c) qd[c] = oracle_bf16_to_double(q[(int64_t)h * D_qk + c]);
+    for (int c = 0; c < D_v; ++c) gd[c] = oracle_bf16_to_double(dO[(int64_t)h * D_v + c]);
+    double zmax = -INFINITY;
+    for (int64_t s = 0; s < m; ++s) {
+      double dot = 0.0;
+      for (int c = 0; c < D_qk; ++c) dot += qd[c] * kvd[s * D_qk + c];
+      z[s] = scale * dot;
+      if (z[s] > zmax) zmax = z[s];
+    }
+    double denom = 0.0;
+    for (int64_t s = 0; s < m; ++s) denom += exp(z[s] - zmax);
+    double dsum = 0.0, dmag = 0.0; /* sum_s P(s) dP(s), sum_s P(s) A(s) */
+    for (int64_t s = 0; s < m; ++s) {
+      z[s] = exp(z[s] - zmax) / denom; /* z now holds P */
+      double dot = 0.0, adot = 0.0;
+      for (int c = 0; c < D_v; ++c) {
+        dot += gd[c] * kvd[s * D_qk + c];
+        adot += fabs(gd[c]) * fabs(kvd[s * D_qk + c]);
+      }
+      dp[s] = dot;
+      adp[s] = adot;
+      dsum += z[s] * dot;
+      dmag += z[s] * adot;
+    }
+    for (int64_t s = 0; s < m; ++s) {
+      const double p = z[s];
+      const double dz = p * (dp[s] - dsum);
+      const double dz_mag = p * (adp[s] + dmag);
+      for (int c = 0; c < D_qk; ++c) {
+        dq[(int64_t)h * D_qk + c] += scale * dz * kvd[s * D_qk + c];
+        dkv_rows[s * D_qk + c] += scale * dz * qd[c];
+        if (mag_dq) mag_dq[(int64_t)h * D_qk + c] += scale * dz_mag * fabs(kvd[s * D_qk + c]);
+        if (mag_dkv) mag_dkv[s * D_qk + c] += scale * dz_mag * fabs(qd[c]);
+      }
+      for (int c = 0; c < D_v; ++c) {
+        dkv_rows[s * D_qk + c] += p * gd[c];
+        if (mag_dkv) mag_dkv[s * D_qk + c] += p * fabs(gd[c]);
+      }
+    }
+  }
+  free(gd);
+  free(qd);
+  free(adp);
+  free(dp);
+  free(z);
+  free(kvd);
+}

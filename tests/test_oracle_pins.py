@@ -362,3 +362,92 @@ def test_dense_kl_row_matches_torch_from_raw_inputs():
         assert np.allclose(got["scores"], scores.numpy(), rtol=1e-12, atol=1e-12)
         assert np.allclose(got["lse"], torch.logsumexp(z, dim=1).numpy(), rtol=1e-12, atol=1e-12)
         assert got["kl"] == pytest.approx(want, rel=1e-10, abs=1e-13)
+
+
+# --------------------------------------------------------------- sparse attention backward
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float values to bf16 (nearest even) and return the bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _bits_f64(u: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("seed,H,D_qk,D_v,m", [(0, 3, 16, 8, 5), (1, 2, 24, 16, 1), (2, 4, 12, 12, 9)])
+def test_sparse_mla_bwd_matches_autograd(seed, H, D_qk, D_v, m):
+    """dq and dkv against torch autograd (fp64) of the plain forward
+    softmax(scale q K^T) V with V the first D_v dims of each latent row: the
+    gradient is derived by the library, not retyped here."""
+    rng = np.random.default_rng(seed)
+    q = _bf16_bits(rng.standard_normal((H, D_qk)))
+    kv = _bf16_bits(rng.standard_normal((m, D_qk)))
+    dO = _bf16_bits(rng.standard_normal((H, D_v)))
+    scale = 0.37
+    dq, dkv = oracle.sparse_mla_bwd_row(q, kv, dO, scale)
+    qt = torch.tensor(_bits_f64(q), requires_grad=True)
+    kt = torch.tensor(_bits_f64(kv), requires_grad=True)
+    out = torch.softmax(scale * qt @ kt.T, dim=-1) @ kt[:, :D_v]
+    out.backward(torch.tensor(_bits_f64(dO)))
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dkv, kt.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_mla_bwd_matches_finite_differences():
+    """Central differences of the oracle's own forward (fp64) along random
+    directions agree with the directional derivative from dq and dkv."""
+    rng = np.random.default_rng(7)
+    H, D_qk, D_v, m, scale = 2, 8, 4, 4, 0.5
+    q0 = _bits_f64(_bf16_bits(rng.standard_normal((H, D_qk))))
+    kv0 = _bits_f64(_bf16_bits(rng.standard_normal((m, D_qk))))
+    dO = _bf16_bits(rng.standard_normal((H, D_v)))
+    g = _bits_f64(dO)
+    dq, dkv = oracle.sparse_mla_bwd_row(_bf16_bits(q0), _bf16_bits(kv0), dO, scale)
+
+    def loss(q, kv):  # sum dO . out, forward written out in numpy fp64
+        z = scale * q @ kv.T
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        return float((g * (p @ kv[:, :D_v])).sum())
+
+    for _ in range(3):
+        uq, uk = rng.standard_normal(q0.shape), rng.standard_normal(kv0.shape)
+        eps = 1e-5
+        fd = (loss(q0 + eps * uq, kv0 + eps * uk) - loss(q0 - eps * uq, kv0 - eps * uk)) / (2 * eps)
+        an = float((dq * uq).sum() + (dkv * uk).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+def test_sparse_mla_bwd_closed_forms():
+    rng = np.random.default_rng(3)
+    H, D_qk, D_v = 3, 10, 6
+    q = _bf16_bits(rng.standard_normal((H, D_qk)))
+    dO = _bf16_bits(rng.standard_normal((H, D_v)))
+    g = _bits_f64(dO)
+    # one entry: P = 1, so the softmax Jacobian vanishes; the row gets sum_h dO[h]
+    kv1 = _bf16_bits(rng.standard_normal((1, D_qk)))
+    dq, dkv = oracle.sparse_mla_bwd_row(q, kv1, dO, 0.3)
+    assert np.all(dq == 0.0)
+    np.testing.assert_allclose(dkv[0, :D_v], g.sum(axis=0), rtol=1e-15)
+    assert np.all(dkv[0, D_v:] == 0.0)
+    # m copies of one row: P = 1/m, dZ = 0, each row gets sum_h dO[h] / m
+    kv4 = np.repeat(kv1, 4, axis=0)
+    dq, dkv = oracle.sparse_mla_bwd_row(q, kv4, dO, 0.3)
+    assert np.abs(dq).max() < 1e-14
+    np.testing.assert_allclose(dkv[:, :D_v], np.tile(g.sum(axis=0) / 4, (4, 1)), rtol=1e-13, atol=1e-15)
+    # zero upstream gradient, and no entries at all
+    dq, dkv = oracle.sparse_mla_bwd_row(q, kv4, np.zeros_like(dO), 0.3)
+    assert not dq.any() and not dkv.any()
+    dq, dkv = oracle.sparse_mla_bwd_row(q, kv4[:0], dO, 0.3)
+    assert not dq.any() and dkv.shape == (0, D_qk)
+
+
+def test_sparse_mla_bwd_magnitudes_bound_values():
+    rng = np.random.default_rng(4)
+    q = _bf16_bits(rng.standard_normal((3, 16)))
+    kv = _bf16_bits(rng.standard_normal((6, 16)))
+    dO = _bf16_bits(rng.standard_normal((3, 8)))
+    dq, dkv, mq, mk = oracle.sparse_mla_bwd_row(q, kv, dO, 0.25, magnitudes=True)
+    assert np.all(np.abs(dq) <= mq * (1 + 1e-12)) and np.all(np.abs(dkv) <= mk * (1 + 1e-12))
+    assert mq.max() > 0 and mk.max() > 0
