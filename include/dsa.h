@@ -84,7 +84,9 @@ enum {
   DSA_KERNEL_ATTENTION = 2,  /* sparse MLA-MQA attention (+ split combine) */
   DSA_KERNEL_INDEXER_KL = 3, /* indexer KL loss (sparse training stage) */
   DSA_KERNEL_DENSE_KL = 4,   /* indexer KL loss (dense warm-up stage) */
-  DSA_KERNEL_KINDS = 5
+  DSA_KERNEL_MLA_BWD_DQ = 5, /* attention backward: dq, P and dS */
+  DSA_KERNEL_MLA_BWD_DKV = 6,/* attention backward: dkv scatter */
+  DSA_KERNEL_KINDS = 7
 };
 dsa_status dsa_timing_begin(void);
 dsa_status dsa_timing_end(double* ms, int64_t* launches, int32_t n_kinds);
@@ -161,6 +163,33 @@ dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, 
                                     int32_t page_size, const int32_t* idx, int64_t B, int32_t H,
                                     int32_t D_qk, int32_t D_v, int32_t k, float scale, float* out,
                                     float* lse, void* ws, size_t ws_bytes, dsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward of dsa_sparse_mla_fwd, for the sparse training stage of [P1]
+ * §2.3.2 (the main model is trained through the sparse attention of §2.1.2 in
+ * the MQA form of §2.2).  For each query t, head h and valid entry s of idx:
+ *   P  = exp(scale * q[t,h] . kv[s] - lse[t,h]),   dP = dout[t,h] . kv[s][:D_v]
+ *   dS = scale * P * (dP - dout[t,h] . out[t,h])
+ *   dq[t,h] = sum_s dS kv[s]
+ *   dkv[s]  = sum over (t, h) selecting s of  dS q[t,h] + P dout[t,h] (dims < D_v)
+ *   q [T, H, D_qk] bf16, kv [N, D_qk] bf16, idx [T, k] int32 (entries < 0 or
+ *   >= N skip; a row may list an index at most once), out [T, H, D_v] fp32 and
+ *   lse [T, H] fp32 as dsa_sparse_mla_fwd wrote them for the same inputs,
+ *   dout [T, H, D_v] bf16 the upstream gradient.
+ *   dq [T, H, D_qk] fp32 out (overwritten); dkv [N, D_qk] fp32 out (zeroed,
+ *   then accumulated; rows no query selects are 0).
+ * P and dS enter the gradient products as bf16 (relative error ~2^-9 per
+ * term); products are bf16 x bf16 with fp32 accumulation.  dkv is summed with
+ * fp32 atomics, so its rounding depends on the order the workgroups run in.
+ * ws: P and dS of a tile of queries, size from
+ * dsa_sparse_mla_bwd_workspace_bytes(T, H, k) (DSA_ERR_WORKSPACE_TOO_SMALL
+ * below it).  All pointers are device memory owned by the caller.
+ */
+size_t dsa_sparse_mla_bwd_workspace_bytes(int64_t T, int32_t H, int32_t k);
+dsa_status dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* out,
+                              const float* lse, const uint16_t* dout, int64_t T, int64_t N, int32_t H,
+                              int32_t D_qk, int32_t D_v, int32_t k, float scale, float* dq, float* dkv,
+                              void* ws, size_t ws_bytes, dsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Indexer KL loss of the sparse training stage, [P1] §2.3.2 (target built as

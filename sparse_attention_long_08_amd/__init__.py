@@ -31,6 +31,9 @@ SIGNATURES = {
     "dsa_sparse_mla_fwd_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
     "dsa_sparse_mla_fwd": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p,
                                     _c_p, _c_p, _c_sz, _c_p]),
+    "dsa_sparse_mla_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32]),
+    "dsa_sparse_mla_bwd": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
+                                    _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "dsa_sparse_mla_fwd_paged_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
     "dsa_sparse_mla_fwd_paged": (_c_i32, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i64, _c_i32,
                                           _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
@@ -114,7 +117,7 @@ def dsa_abi_version() -> int:
 
 
 # stage kinds of dsa_timing_end
-TIMING_KINDS = ("indexer", "topk", "attention", "indexer_kl", "dense_kl")
+TIMING_KINDS = ("indexer", "topk", "attention", "indexer_kl", "dense_kl", "mla_bwd_dq", "mla_bwd_dkv")
 
 
 def dsa_timing_begin() -> None:
@@ -152,6 +155,16 @@ def dsa_sparse_mla_fwd_workspace_bytes(T, H, D_v, k) -> int:
 def dsa_sparse_mla_fwd(q, kv, idx, T, N, H, D_qk, D_v, k, scale, out, lse, ws, ws_bytes, stream=None):
     _call("dsa_sparse_mla_fwd", _ptr(q), _ptr(kv), _ptr(idx), T, N, H, D_qk, D_v, k, scale, _ptr(out), _ptr(lse),
           _ptr(ws), ws_bytes, _stream(stream))
+
+
+def dsa_sparse_mla_bwd_workspace_bytes(T, H, k) -> int:
+    return load().dsa_sparse_mla_bwd_workspace_bytes(T, H, k)
+
+
+def dsa_sparse_mla_bwd(q, kv, idx, out, lse, dout, T, N, H, D_qk, D_v, k, scale, dq, dkv, ws, ws_bytes,
+                       stream=None):
+    _call("dsa_sparse_mla_bwd", _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse), _ptr(dout), T, N, H, D_qk, D_v,
+          k, scale, _ptr(dq), _ptr(dkv), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def dsa_sparse_mla_fwd_paged_workspace_bytes(B, H, D_v, k) -> int:

@@ -1,4 +1,4 @@
-"""Builds libdsa.so (the HIP/gfx950 DSA forward library) in-tree with hipcc."""
+"""Builds libdsa.so (the HIP/gfx950 DSA library) in-tree with hipcc."""
 from __future__ import annotations
 
 import os
@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "indexer_kl.hip"]
+SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "indexer_kl.hip", "sparse_mla_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -292,6 +292,62 @@ dsa_status dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32
                  (hipStream_t)stream);
 }
 
+// Queries per tile of the attention backward: P and dS of a tile sit in the
+// workspace (2 * tile * k * Hp bf16: 8.6 GB at k = 2048, 128 heads).
+constexpr int64_t kBwdTile = 8192;
+
+size_t dsa_sparse_mla_bwd_workspace_bytes(int64_t T, int32_t H, int32_t k) {
+  if (T <= 0 || H < 1 || k < 1) return 0;
+  const int64_t tile = T < kBwdTile ? T : kBwdTile;
+  return (size_t)(2 * tile * (int64_t)k * dsa::mla_bwd_padded_heads(H) * 2);
+}
+
+dsa_status dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* out,
+                              const float* lse, const uint16_t* dout, int64_t T, int64_t N, int32_t H,
+                              int32_t D_qk, int32_t D_v, int32_t k, float scale, float* dq, float* dkv,
+                              void* ws, size_t ws_bytes, dsa_stream_t stream) {
+  REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "T must be >= 0 and N >= 1");
+  if (dsa_status s = check_mla_shape(H, D_qk, D_v, k)) return s;
+  REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  REQUIRE_PTR(dkv);
+  REQUIRE_AL(dkv);
+  if (T > 0) {
+    REQUIRE_PTR(q); REQUIRE_PTR(kv); REQUIRE_PTR(idx); REQUIRE_PTR(out); REQUIRE_PTR(lse); REQUIRE_PTR(dout);
+    REQUIRE_PTR(dq); REQUIRE_PTR(ws);
+    REQUIRE_AL(q); REQUIRE_AL(kv); REQUIRE_AL(idx); REQUIRE_AL(out); REQUIRE_AL(lse); REQUIRE_AL(dout);
+    REQUIRE_AL(dq); REQUIRE_AL(ws);
+    const size_t need = dsa_sparse_mla_bwd_workspace_bytes(T, H, k);
+    REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "ws_bytes (%zu) below %zu", ws_bytes, need);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (hipError_t e = dsa::launch_zero_f32(dkv, N * (int64_t)D_qk, st)) return hip_check(e, "dkv clear");
+  const int64_t Hp = dsa::mla_bwd_padded_heads(H);
+  for (int64_t t0 = 0; t0 < T; t0 += kBwdTile) {
+    const int64_t tn = T - t0 < kBwdTile ? T - t0 : kBwdTile;
+    dsa::MlaBwdArgs a;
+    a.q = q + t0 * H * (int64_t)D_qk;
+    a.kv = kv;
+    a.idx = idx + t0 * (int64_t)k;
+    a.out = out + t0 * H * (int64_t)D_v;
+    a.lse = lse + t0 * H;
+    a.dout = dout + t0 * H * (int64_t)D_v;
+    a.T = tn;
+    a.N = N;
+    a.H = H;
+    a.k = k;
+    a.scale = scale;
+    a.dq = dq + t0 * H * (int64_t)D_qk;
+    a.pbuf = (uint16_t*)ws;
+    a.dsbuf = (uint16_t*)ws + tn * (int64_t)k * Hp;
+    a.dkv = dkv;
+    hipError_t e = timed(DSA_KERNEL_MLA_BWD_DQ, st, [&] { return dsa::launch_sparse_mla_bwd(a, false, st); });
+    if (e != hipSuccess) return hip_check(e, "attention backward (dq) launch");
+    e = timed(DSA_KERNEL_MLA_BWD_DKV, st, [&] { return dsa::launch_sparse_mla_bwd(a, true, st); });
+    if (e != hipSuccess) return hip_check(e, "attention backward (dkv) launch");
+  }
+  return ok();
+}
+
 dsa_status dsa_indexer_kl_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* lse,
                               const float* scores, int64_t ld, int64_t T, int64_t N, int32_t H, int32_t D_qk,
                               int32_t k, float scale, float* kl, dsa_stream_t stream) {

@@ -82,6 +82,31 @@ hipError_t launch_indexer_dense_kl(const uint16_t* q, const uint16_t* kv, int64_
                                    int64_t T, int64_t q_pos0, int32_t H, float scale, float* kl, float* lse,
                                    hipStream_t st);
 
+// Sparse MLA-MQA backward over one tile of T queries.  Stage 0 (dq kernel):
+// dq, and P / dS of every entry into pbuf / dsbuf ([T, k, Hp] bf16, Hp =
+// mla_bwd_padded_heads(H)); stage 1 (dkv kernel): adds the entries'
+// contributions to dkv (fp32 atomics; dkv must be zeroed beforehand).
+struct MlaBwdArgs {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const int32_t* idx;
+  const float* out;
+  const float* lse;
+  const uint16_t* dout;
+  int64_t T;
+  int64_t N;
+  int32_t H;
+  int32_t k;
+  float scale;
+  float* dq;
+  uint16_t* pbuf;
+  uint16_t* dsbuf;
+  float* dkv;
+};
+int32_t mla_bwd_padded_heads(int32_t H);
+hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, bool dkv_stage, hipStream_t st);
+hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t st);
+
 // Number of key splits used for T queries of H heads with k entries each.
 int32_t sparse_mla_splits(int64_t T, int32_t H, int32_t k);
 

@@ -1,0 +1,481 @@
+// Backward of the sparse MLA-MQA attention on gfx950 bf16 matrix cores.
+//
+// The sparse training stage trains the main model through the sparse
+// attention ("DeepSeek-V3.2" report walk-through, §2.3.2), so the attention
+// over the selected rows (§2.1.2 attention equation, MQA form of §2.2) needs
+// its gradient.  Per query t, head h and selected row s, with dO = dL/dout:
+//   P    = exp(scale * q[t,h] . kv[s] - lse[t,h])        (recomputed)
+//   dP   = dO[t,h] . kv[s][:512]
+//   D    = dO[t,h] . out[t,h]          (= sum_s P dP for the forward's out)
+//   dS   = scale * P * (dP - D)
+//   dq[t,h]  = sum_s dS kv[s]
+//   dkv[s]  += sum_h dS q[t,h]  +  sum_h P dO[t,h]   (second term: dims < 512)
+//
+// Two kernels per tile of queries:
+//
+// mla_bwd_dq_kernel: one workgroup of 4 waves per (query, 64-head half);
+// wave w owns 16 heads.  The selected latent rows are gathered 32 at a time
+// into LDS by DMA (band-major stages with an XOR swizzle, as the forward
+// kernel lays them out), double buffered.  Per block it forms S^T = K Q^T and
+// dP^T = V dO^T on 16x16x32 MFMAs (keys on the rows, heads on the columns,
+// so each lane owns one head and four keys per tile), then P and dS in
+// registers, accumulates dq^T += K^T dS^T (36 tiles of 16 latent dims; the
+// K^T operand is read transposed with ds_read_b64_tr_b16 and dS^T is the
+// lane's own values, with the key order of the two agreeing) and stores P
+// and dS as bf16 to a workspace laid out [query][entry][head].
+//
+// mla_bwd_dkv_kernel: one workgroup of 8 waves per query; each wave owns
+// four or five 16-column tiles of the 576 latent dims.  It holds q and dO of all heads in the
+// B layout of the head contraction (heads on k), streams the P and dS tiles
+// of each 32-entry block through LDS by DMA, forms
+//   dkv_block = dS^T q + P^T dO          (32 entries x 576 dims)
+// and adds it to the cache rows with fp32 atomics.  dkv sums over queries, so
+// this is a scatter; the atomics are the only cross-workgroup traffic.
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kBlk = 32;                    // selected rows per block
+constexpr int kStage = kBlk * kDqk * 2;     // 36864 bytes of gathered rows
+constexpr int kBand = 4096;                 // one 8-chunk band of all 32 rows
+constexpr int kThreads = 256;               // 4 waves
+constexpr int kMaxK = 4096;
+constexpr int kQSteps = kDqk / 32;          // 18 k-steps of the logit product
+constexpr int kVSteps = kDv / 32;           // 16 k-steps of the dP product
+constexpr int kCt = kDqk / 16;              // 36 dq tiles of 16 latent dims
+constexpr int kKvWaves = 8;                 // waves of the dkv kernel (two per SIMD)
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kTilesPerWave = 5;            // dkv column tiles per wave, at most
+
+// Column tile (16 latent dims) of slot ci of dkv wave w, or -1.  Waves 0..3
+// take tiles 5w .. 5w+4; wave 4+i takes 20+3i .. 22+3i and the rope tile
+// 32+i, so the two waves on one SIMD share out 17 tile products (a rope tile
+// has no value term).
+__device__ __forceinline__ int kv_tile(int w, int ci) {
+  if (w < 4) return 5 * w + ci;
+  const int i = w - 4;
+  return ci < 3 ? 20 + 3 * i + ci : (ci == 3 ? 32 + i : -1);
+}
+constexpr int kPRow = 256;                  // LDS bytes per entry row of a P / dS tile (128 heads)
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) uint8_t* lds_u8_ptr;
+typedef __attribute__((address_space(3))) const v8bf* lds_v8bf_cptr;
+
+// XOR swizzle of the 16-byte slot within a 128-byte band row (the forward
+// kernel's layout).
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (2 * r)) & 7; }
+
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+struct BwdParams {
+  const uint16_t* q;     // [T, H, 576]
+  const uint16_t* kv;    // [N, 576]
+  const int32_t* idx;    // [T, k]
+  const float* out;      // [T, H, 512]
+  const float* lse;      // [T, H]
+  const uint16_t* dout;  // [T, H, 512]
+  int64_t T;
+  int64_t N;
+  int32_t H;
+  int32_t Hp;            // heads padded to a multiple of 32 (workspace row)
+  int32_t k;
+  float scale;
+  float scale_log2;      // scale * log2(e)
+  float* dq;             // [T, H, 576]
+  uint16_t* pbuf;        // [T, k, Hp] bf16 P
+  uint16_t* dsbuf;       // [T, k, Hp] bf16 dS (scale folded in)
+  float* dkv;            // [N, 576], accumulated
+};
+
+// Resolves the entries of query t to cache rows (-1: skipped), padded with
+// -1 to whole blocks.
+__device__ __forceinline__ void load_rows(const BwdParams& p, int64_t t, int32_t* rows, int nb) {
+  for (int e = threadIdx.x; e < nb * kBlk; e += blockDim.x) {
+    int32_t r = -1;
+    if (e < p.k) {
+      const int32_t s = p.idx[t * (int64_t)p.k + e];
+      if (s >= 0 && s < p.N) r = s;
+    }
+    rows[e] = r;
+  }
+}
+
+// ---------------------------------------------------------------- dq kernel
+__global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
+  __shared__ int32_t rows[kMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hn = lane & 15, qd = lane >> 4;
+
+  // Workgroups b and b+8 land on the same XCD: with two head halves they
+  // take the two halves of one query, so its gathered rows are shared in L2.
+  const int n_half = (p.Hp + 63) / 64;
+  int64_t t;
+  int half;
+  if (n_half == 2) {
+    const int64_t b = blockIdx.x;
+    half = (int)((b >> 3) & 1);
+    t = (b >> 4) * 8 + (b & 7);
+  } else {
+    half = 0;
+    t = blockIdx.x;
+  }
+  if (t >= p.T) return;
+  const int head = 64 * half + 16 * wave + hn;
+  // a wave whose heads are all padding computes zeros and stores nothing,
+  // but still joins every barrier below
+  const bool wave_on = 64 * half + 16 * wave < p.Hp;
+  const bool hv = head < p.H;
+  const int nb = (p.k + kBlk - 1) / kBlk;
+  load_rows(p, t, rows, nb);
+
+  // q and dO of this lane's head in the B layout of 16x16x32 MFMAs: k-step
+  // ks holds dims 32*ks + 8*qd .. +7.  D = dO . out over the same dims,
+  // summed over the four lanes of the head.
+  const int hc = hv ? head : 0;
+  v8bf qf[kQSteps], df[kVSteps];
+  float dsum = 0.f;
+  {
+    const uint16_t* qrow = p.q + (t * p.H + hc) * (int64_t)kDqk + 8 * qd;
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      const v8bf v = *(const v8bf*)(qrow + 32 * ks);
+      qf[ks] = hv ? v : (v8bf){};
+    }
+    const uint16_t* drow = p.dout + (t * p.H + hc) * (int64_t)kDv + 8 * qd;
+    const float* orow = p.out + (t * p.H + hc) * (int64_t)kDv + 8 * qd;
+#pragma unroll
+    for (int ks = 0; ks < kVSteps; ++ks) {
+      const v8bf v = *(const v8bf*)(drow + 32 * ks);
+      const float4 o0 = *(const float4*)(orow + 32 * ks);
+      const float4 o1 = *(const float4*)(orow + 32 * ks + 4);
+      df[ks] = hv ? v : (v8bf){};
+      dsum += (float)v[0] * o0.x + (float)v[1] * o0.y + (float)v[2] * o0.z + (float)v[3] * o0.w +
+              (float)v[4] * o1.x + (float)v[5] * o1.y + (float)v[6] * o1.z + (float)v[7] * o1.w;
+    }
+    dsum += shfl_xor_f(dsum, 16);
+    dsum += shfl_xor_f(dsum, 32);
+  }
+  const float lse_l2 = hv ? p.lse[t * p.H + hc] * 1.4426950408889634f : 0.f;
+  __syncthreads();  // rows[]
+
+  // Gather of one block: wave w moves rows 8w .. 8w+7, one DMA per band;
+  // lane L carries row 8w + L/8 into slot L%8 of the band.
+  const int g_row = 8 * wave + (lane >> 3);
+  const int g_chunk = (lane & 7) ^ swz(g_row);
+  auto gather = [&](uint8_t* base, int blk) {
+    int32_t row = rows[blk * kBlk + g_row];
+    row = row < 0 ? 0 : row;  // skipped entries read row 0; P = 0 masks them
+    const uint16_t* src = p.kv + ((uint64_t)(uint32_t)row * kDqk + 8 * g_chunk);
+#pragma unroll
+    for (int bd = 0; bd < 9; ++bd)
+      __builtin_amdgcn_global_load_lds((const void*)(src + 64 * bd), (lds_ptr)(base + bd * kBand + wave * 1024), 16,
+                                       0, 0);
+  };
+
+  // Operand offsets.  Key tile kt, k-step ks (A of S^T and dP^T): lane (row
+  // 16kt + hn, qd) reads chunk 4ks + qd = band ks/2, slot (4(ks%2) + qd) ^
+  // swz(row).
+  uint32_t k_off[2][2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int r = 16 * kt + hn;
+      k_off[kt][par] = (uint32_t)(r * 128 + (((4 * par + qd) ^ swz(r)) << 4));
+    }
+  // K^T tile ct (A of dq^T): the B operand dS^T of lane (head, qd) holds, at
+  // k-slot 8qd + i, key 4qd + i (i < 4, tile 0) or 16 + 4qd + i - 4 (tile 1),
+  // i.e. its own accumulator values.  ds_read_b64_tr_b16 gives lane i of a
+  // 16-lane group column i of the 4 x 16 block whose rows lane 4*rho + c
+  // addresses at columns 4c .. 4c+3, so group qd reads rows (keys) 4qd + rho
+  // (and 16 + 4qd + rho) at dims 16ct + 4c: chunk 2ct + c/2, byte 8(c%2).
+  uint32_t t_off[2][4];
+  {
+    const int rho = hn >> 2, c = hn & 3;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 16 * hi + 4 * qd + rho;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+        t_off[hi][c4] = (uint32_t)(r * 128 + (((2 * c4 + (c >> 1)) ^ swz(r)) << 4) + 8 * (c & 1));
+    }
+  }
+
+  v4f dqa[kCt];
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) dqa[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  uint16_t* const pdst = p.pbuf + (t * (int64_t)p.k) * p.Hp + (wave_on ? head : 0);
+  uint16_t* const sdst = p.dsbuf + (t * (int64_t)p.k) * p.Hp + (wave_on ? head : 0);
+
+  auto step = [&](const uint8_t* __restrict__ cur, int blk) {
+    const lds_u8_ptr base = (lds_u8_ptr)cur;
+    // logits and dP of the block
+    v4f sacc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
+    v4f pacc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const v8bf a = *(lds_v8bf_cptr)(base + (ks >> 1) * kBand + k_off[kt][ks & 1]);
+        sacc[kt] = mfma_bf16_16x16x32(a, qf[ks], sacc[kt]);
+        if (ks < kVSteps) pacc[kt] = mfma_bf16_16x16x32(a, df[ks < kVSteps ? ks : 0], pacc[kt]);
+      }
+    }
+    // P and dS; lane holds keys 16kt + 4qd + r of its head
+    float pv[2][4], dv[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = blk * kBlk + 16 * kt + 4 * qd + r;
+        const bool valid = hv && rows[e] >= 0;
+        const float pr = valid ? __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], p.scale_log2, -lse_l2)) : 0.f;
+        pv[kt][r] = pr;
+        dv[kt][r] = p.scale * pr * (pacc[kt][r] - dsum);
+      }
+    const v8bf bop = (v8bf){to_bf16(dv[0][0]), to_bf16(dv[0][1]), to_bf16(dv[0][2]), to_bf16(dv[0][3]),
+                            to_bf16(dv[1][0]), to_bf16(dv[1][1]), to_bf16(dv[1][2]), to_bf16(dv[1][3])};
+    if (wave_on) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = blk * kBlk + 16 * kt + 4 * qd + r;
+          if (e < p.k) {
+            pdst[(int64_t)e * p.Hp] = __builtin_bit_cast(uint16_t, to_bf16(pv[kt][r]));
+            sdst[(int64_t)e * p.Hp] = __builtin_bit_cast(uint16_t, to_bf16(dv[kt][r]));
+          }
+        }
+    }
+    // dq^T += K^T dS^T
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) {
+      const uint32_t off = (ct >> 2) * kBand;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + off + t_off[0][ct & 3]));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + off + t_off[1][ct & 3]));
+      const v8bf a = __builtin_bit_cast(v8bf, (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      dqa[ct] = mfma_bf16_16x16x32(a, bop, dqa[ct]);
+    }
+  };
+
+  if (nb > 0) gather(stage0, 0);
+  for (int blk = 0; blk < nb; ++blk) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // block blk landed everywhere; block blk-1's stage is free
+    uint8_t* cur = (blk & 1) ? stage1 : stage0;
+    uint8_t* nxt = (blk & 1) ? stage0 : stage1;
+    if (blk + 1 < nb) gather(nxt, blk + 1);
+    step(cur, blk);
+  }
+
+  if (hv) {
+    float* drow = p.dq + (t * p.H + head) * (int64_t)kDqk + 4 * qd;
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) *(float4*)(drow + 16 * ct) = make_float4(dqa[ct][0], dqa[ct][1], dqa[ct][2], dqa[ct][3]);
+  }
+}
+
+// ---------------------------------------------------------------- dkv kernel
+__global__ __launch_bounds__(kKvThreads, 1) void mla_bwd_dkv_kernel(BwdParams p) {
+  // [stage][P, dS][32 entries x 128 heads] bf16, slot of chunk c in row j at c ^ (j % 16)
+  __shared__ __attribute__((aligned(16))) uint8_t pst[2][2][kBlk * kPRow];
+  __shared__ __attribute__((aligned(16))) uint8_t stg[32 * 2 * kDqk];  // one 32-head chunk of q or dO
+  __shared__ int32_t rows[kMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hn = lane & 15, qd = lane >> 4;
+  const int64_t t = blockIdx.x;
+  if (t >= p.T) return;
+  const int nb = (p.k + kBlk - 1) / kBlk;
+  load_rows(p, t, rows, nb);
+  // Head chunks past Hp are never loaded: zero them once in both stages so
+  // that the k-steps over them multiply zeros (q and dO are zero there too).
+  if (p.Hp < 128) {
+    for (int i = tid; i < 2 * 2 * kBlk * 16; i += kKvThreads) {
+      const int c = i & 15, j = (i >> 4) & 31, arr = (i >> 9) & 1, sidx = i >> 10;
+      const int chunk = c ^ (j & 15);
+      if (8 * chunk >= p.Hp) *(v4i*)&pst[sidx][arr][j * kPRow + 16 * c] = (v4i){0, 0, 0, 0};
+    }
+  }
+
+  // q and dO in the B layout of the head contraction: slot ci covers dims
+  // 16 kv_tile(w, ci) + hn; k-step kh holds heads 32kh + 8qd .. +7.  Each
+  // 32-head chunk of q (then of dO) is staged row-major in LDS and read back
+  // transposed with ds_read_b64_tr_b16 (lane i of a 16-lane group receives
+  // column i of the 4 x 16 block whose rows lane 4*rho + c addresses at
+  // columns 4c .. 4c+3): group qd reads heads 8qd + rho and 8qd + 4 + rho.
+  v8bf qc[kTilesPerWave][4], dc[kTilesPerWave][4];
+  {
+    const int rho = hn >> 2, c = hn & 3;
+#pragma unroll
+    for (int kh = 0; kh < 4; ++kh) {
+#pragma unroll
+      for (int arr = 0; arr < 2; ++arr) {
+        const int width = arr ? kDv : kDqk;
+        const int cpr = width / 8;  // 16-byte chunks per head row
+        const uint16_t* src = arr ? p.dout : p.q;
+        for (int i = tid; i < 32 * cpr; i += kKvThreads) {
+          const int r = i / cpr, ch = i - r * cpr, h = 32 * kh + r;
+          v4i v = (v4i){0, 0, 0, 0};
+          if (h < p.H) v = *(const v4i*)(src + (t * p.H + h) * (int64_t)width + 8 * ch);
+          *(v4i*)&stg[r * (2 * kDqk) + 16 * ch] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ci = 0; ci < kTilesPerWave; ++ci) {
+          const int tile = kv_tile(wave, ci);
+          v8bf val = (v8bf){};
+          if (tile >= 0 && (!arr || tile < kDv / 16)) {
+            const uint32_t col_b = (uint32_t)(2 * (16 * tile + 4 * c));
+            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4s_ptr)((lds_u8_ptr)stg + (8 * qd + rho) * (2 * kDqk) + col_b));
+            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4s_ptr)((lds_u8_ptr)stg + (8 * qd + 4 + rho) * (2 * kDqk) + col_b));
+            val = __builtin_bit_cast(v8bf, (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          }
+          if (arr) dc[ci][kh] = val;
+          else qc[ci][kh] = val;
+        }
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();  // rows[]
+
+  // DMA of the P and dS rows of one block: 16 instructions of 4 entry rows
+  // each (instruction ii: array ii/8, rows 4(ii%8) .. +3), wave w issuing ii =
+  // w and w + 8; lane L fills row 4(ii%8) + L/16, slot L%16 with chunk
+  // (L%16) ^ row%16 (chunks past Hp/8 are not loaded and stay zero).
+  auto gather = [&](int sidx, int blk) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ii = wave + kKvWaves * i;
+      const int arr = ii >> 3, j0 = 4 * (ii & 7);
+      const int j = j0 + (lane >> 4);
+      const int c = (lane & 15) ^ (j & 15);
+      int e = blk * kBlk + j;
+      e = e < p.k ? e : p.k - 1;
+      if (8 * c < p.Hp) {
+        const int64_t off = (t * (int64_t)p.k + e) * p.Hp + 8 * c;
+        const uint16_t* src = arr ? p.dsbuf : p.pbuf;
+        __builtin_amdgcn_global_load_lds((const void*)(src + off), (lds_ptr)(&pst[sidx][arr][0] + j0 * kPRow), 16,
+                                         0, 0);
+      }
+    }
+  };
+
+  auto step = [&](int sidx, int blk) {
+    const lds_u8_ptr pb = (lds_u8_ptr)&pst[sidx][0][0];
+    const lds_u8_ptr sb = (lds_u8_ptr)&pst[sidx][1][0];
+    v4f acc[2][kTilesPerWave];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ci = 0; ci < kTilesPerWave; ++ci) acc[kt][ci] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kh = 0; kh < 4; ++kh) {
+      v8bf ap[2], as[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint32_t off = (uint32_t)((16 * kt + hn) * kPRow + (((4 * kh + qd) ^ hn) << 4));
+        ap[kt] = *(lds_v8bf_cptr)(pb + off);
+        as[kt] = *(lds_v8bf_cptr)(sb + off);
+      }
+#pragma unroll
+      for (int ci = 0; ci < kTilesPerWave; ++ci) {
+        const int tile = kv_tile(wave, ci);
+        if (tile < 0) continue;
+        const bool has_v = tile < kDv / 16;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          acc[kt][ci] = mfma_bf16_16x16x32(as[kt], qc[ci][kh], acc[kt][ci]);
+          if (has_v) acc[kt][ci] = mfma_bf16_16x16x32(ap[kt], dc[ci][kh], acc[kt][ci]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one k-step of operands live at a time
+    }
+    // scatter: lane (dim 16 tile + hn, qd) holds entries 16kt + 4qd + r
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int32_t row = rows[blk * kBlk + 16 * kt + 4 * qd + r];
+        if (row >= 0) {
+          float* dst = p.dkv + (int64_t)row * kDqk + hn;
+#pragma unroll
+          for (int ci = 0; ci < kTilesPerWave; ++ci) {
+            const int tile = kv_tile(wave, ci);
+            if (tile >= 0) unsafeAtomicAdd(dst + 16 * tile, acc[kt][ci][r]);
+          }
+        }
+      }
+  };
+
+  if (nb > 0) gather(0, 0);
+  for (int blk = 0; blk < nb; ++blk) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (blk + 1 < nb) gather((blk + 1) & 1, blk + 1);
+    step(blk & 1, blk);
+  }
+}
+
+__global__ void zero_f32_kernel(float* __restrict__ x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t j = i; j < n; j += stride) x[j] = 0.f;
+}
+
+}  // namespace
+
+int32_t mla_bwd_padded_heads(int32_t H) { return (H + 31) / 32 * 32; }
+
+hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, bool dkv_stage, hipStream_t st) {
+  if (a.T <= 0) return hipSuccess;
+  BwdParams p;
+  p.q = a.q;
+  p.kv = a.kv;
+  p.idx = a.idx;
+  p.out = a.out;
+  p.lse = a.lse;
+  p.dout = a.dout;
+  p.T = a.T;
+  p.N = a.N;
+  p.H = a.H;
+  p.Hp = mla_bwd_padded_heads(a.H);
+  p.k = a.k;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.dq = a.dq;
+  p.pbuf = a.pbuf;
+  p.dsbuf = a.dsbuf;
+  p.dkv = a.dkv;
+  if (!dkv_stage) {
+    const int n_half = (p.Hp + 63) / 64;
+    const int64_t grid = n_half == 2 ? (a.T + 7) / 8 * 16 : a.T;
+    hipLaunchKernelGGL(mla_bwd_dq_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3((unsigned)a.T), dim3(kKvThreads), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -154,3 +154,31 @@ def test_dense_warmup_workspace_validation():
     st = lib.dsa_dense_warmup_loss(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16, 4, 128, 8, 576, 0, 0.07, FAKE, 0, FAKE,
                                    nb - 1, 0)
     assert st == 3 and "workspace" in lib.dsa_last_error_message().decode()
+
+
+# dsa_sparse_mla_bwd(q, kv, idx, out, lse, dout, T, N, H, D_qk, D_v, k, scale, dq, dkv, ws, ws_bytes, stream)
+@pytest.mark.parametrize("args,status,needle", [
+    ((FAKE,) * 6 + (4, 0, 8, 576, 512, 16, 0.07, FAKE, FAKE, FAKE, 1 << 30, 0), 1, "N"),
+    ((FAKE,) * 6 + (4, 64, 8, 576, 256, 16, 0.07, FAKE, FAKE, FAKE, 1 << 30, 0), 2, "D_v"),
+    ((FAKE,) * 6 + (4, 64, 0, 576, 512, 16, 0.07, FAKE, FAKE, FAKE, 1 << 30, 0), 2, "H"),
+    ((FAKE,) * 6 + (4, 64, 8, 576, 512, 5000, 0.07, FAKE, FAKE, FAKE, 1 << 30, 0), 2, "k"),
+    ((FAKE,) * 6 + (4, 64, 8, 576, 512, 16, -1.0, FAKE, FAKE, FAKE, 1 << 30, 0), 1, "scale"),
+    ((FAKE,) * 6 + (4, 64, 8, 576, 512, 16, 0.07, FAKE, 0, FAKE, 1 << 30, 0), 1, "dkv"),
+    ((FAKE,) * 5 + (0,) + (4, 64, 8, 576, 512, 16, 0.07, FAKE, FAKE, FAKE, 1 << 30, 0), 1, "dout"),
+    ((FAKE,) * 6 + (4, 64, 8, 576, 512, 16, 0.07, FAKE + 4, FAKE, FAKE, 1 << 30, 0), 1, "aligned"),
+])
+def test_sparse_mla_bwd_validation(args, status, needle):
+    lib = dsa.load()
+    assert lib.dsa_sparse_mla_bwd(*args) == status
+    assert needle in lib.dsa_last_error_message().decode()
+
+
+def test_sparse_mla_bwd_workspace():
+    lib = dsa.load()
+    # P and dS of a tile of at most 8192 queries, heads padded to a multiple of 32
+    assert lib.dsa_sparse_mla_bwd_workspace_bytes(4, 8, 16) == 2 * 4 * 16 * 32 * 2
+    assert lib.dsa_sparse_mla_bwd_workspace_bytes(32768, 128, 2048) == 2 * 8192 * 2048 * 128 * 2
+    assert lib.dsa_sparse_mla_bwd_workspace_bytes(0, 128, 2048) == 0
+    nb = lib.dsa_sparse_mla_bwd_workspace_bytes(4, 8, 16)
+    st = lib.dsa_sparse_mla_bwd(*((FAKE,) * 6), 4, 64, 8, 576, 512, 16, 0.07, FAKE, FAKE, FAKE, nb - 1, 0)
+    assert st == 3 and "ws_bytes" in lib.dsa_last_error_message().decode()
