@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--dense-kl", action="store_true",
                     help="time the dense warm-up indexer KL loss (prefill_L32k unless --workload names another "
                          "prefill workload)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the sparse attention backward (prefill_L32k unless --workload names another "
+                         "prefill workload)")
     ap.add_argument("--kl", action="store_true",
                     help="time the sparse-stage indexer KL loss instead of the forward path (prefill_L32k unless "
                          "--workload names another prefill workload)")
@@ -147,7 +150,7 @@ def main():
 
     from dsa_inputs import configs
 
-    if (args.kl or args.dense_kl) and args.workload == ap.get_default("workload"):
+    if (args.kl or args.dense_kl or args.bwd) and args.workload == ap.get_default("workload"):
         args.workload = "prefill_L32k"
     wl = configs.WORKLOADS[args.workload]
     if wl.kind == "paged_prefill":
@@ -162,6 +165,13 @@ def main():
         args.steps = 3 if args.steps is None else args.steps
         args.warmup = 1 if args.warmup is None else args.warmup
         return bench_dense_kl(args, wl)
+    if args.bwd:
+        if decode:
+            print("--bwd needs a prefill workload", file=sys.stderr)
+            sys.exit(2)
+        args.steps = 3 if args.steps is None else args.steps
+        args.warmup = 1 if args.warmup is None else args.warmup
+        return bench_bwd(args, wl)
     if args.kl:
         if decode:
             print("--kl needs a prefill workload", file=sys.stderr)
@@ -559,6 +569,116 @@ def bench_dense_kl(args, wl):
                                          f"lse + KL over all causal keys, single-threaded C oracle in fp64, "
                                          f"{dt:.1f} s"}
     print(json.dumps(rec))
+
+
+def bench_bwd(args, wl):
+    """Sparse MLA-MQA attention backward (the gradient the sparse training stage,
+    "DeepSeek-V3.2" walk-through §2.3.2, takes through the attention of §2.1.2)
+    over every query row of a prefill workload.  The selected sets, out and lse
+    come from one fused forward call (untimed); each timed step is one
+    dsa_sparse_mla_bwd call (dq kernel, then dkv kernel, per 8192-query tile),
+    timed in the two phases of the prefill bench."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_long_08_amd as dsa
+    from dsa_inputs import device, gen
+
+    dsa.load()
+    T, N, k, H = wl.T, wl.N, wl.k, wl.H
+    print(f"[bench] generating {wl.name} inputs on the GPU", file=sys.stderr, flush=True)
+    inp = device.make_prefill_inputs(wl)
+    stream = torch.cuda.current_stream()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H, wl.D_v), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    nbf = dsa.dsa_forward_prefill_workspace_bytes(T, N, H, wl.D_v, k)
+    wsf = torch.empty(max(nbf, 256), dtype=torch.uint8, device="cuda")
+    dsa.dsa_forward_prefill(inp["q_idx"], inp["w"], inp["k_idx"], inp["q"], inp["kv"], T, N, wl.H_I, wl.d_I, H,
+                            wl.D_qk, wl.D_v, k, 0, wl.scale, idx, out, lse, wsf, nbf)
+    del wsf
+    dout = torch.empty((T, H, wl.D_v), dtype=torch.uint16, device="cuda")
+    device.fill(dout, T, H * wl.D_v, device.BF16_NORMAL, wl.seed, gen.STREAM_DOUT)
+    dq = torch.empty((T, H, wl.D_qk), dtype=torch.float32, device="cuda")
+    dkv = torch.empty((N, wl.D_qk), dtype=torch.float32, device="cuda")
+    nb = dsa.dsa_sparse_mla_bwd_workspace_bytes(T, H, k)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+
+    def fused():
+        dsa.dsa_sparse_mla_bwd(inp["q"], inp["kv"], idx, out, lse, dout, T, N, H, wl.D_qk, wl.D_v, k, wl.scale, dq,
+                               dkv, ws, nb)
+
+    for _ in range(args.warmup):
+        fused()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        fused()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(f"[bench] {args.steps} backward steps done: {ms_per_step:.1f} ms per step", file=sys.stderr, flush=True)
+    rec_t, ev_ms_per_step = launch_times(dsa, torch, stream, fused, args.steps)
+    stage_ms = {kind: rec_t[kind][0] / args.steps for kind in ("mla_bwd_dq", "mla_bwd_dkv")}
+    w = algorithmic_work(wl, T)
+    # per selected (query, entry) pair and head: dq kernel forms the logits
+    # (576), dP (512) and dq (576); dkv kernel dS^T q (576) and P^T dO (512)
+    flops = {"mla_bwd_dq": w["selected"] * 2 * H * (wl.D_qk + wl.D_v + wl.D_qk),
+             "mla_bwd_dkv": w["selected"] * 2 * H * (wl.D_qk + wl.D_v)}
+    dom = max(stage_ms, key=stage_ms.get)
+    launches = rec_t[dom][1] // args.steps
+    ach = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    total_tf = sum(flops.values()) / (ms_per_step * 1e-3) / 1e12
+    rec = {
+        "metric": "DSA sparse MLA-MQA attention backward query-tokens/s",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "gpu_ms_per_step": e0.elapsed_time(e1) / args.steps,
+        "ms_per_step_with_launch_events": ev_ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator, device-resident; selection from the fused forward)",
+        "config": {"workload": wl.name, "L": T, "k": k, "H": H, "D_qk": wl.D_qk, "D_v": wl.D_v, "causal": True,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": counter_traffic(wl.name, dom),
+                     "launches_per_step": launches, "avg_launch_ms": stage_ms[dom] / max(launches, 1)},
+        "stages_ms": stage_ms,
+        "step_tflops": total_tf,
+    }
+    del inp, ws, dq, dkv, out, lse, dout, idx
+    rec["cpu_baseline"] = None if (args.no_cpu or args.fused_only) else bwd_cpu_baseline(wl, 50)
+    print(json.dumps(rec))
+
+
+def bwd_cpu_baseline(wl, rows: int):
+    """The oracle (single thread) on `rows` seeded-random query rows of the
+    backward: one query's gradient over its selected rows."""
+    import numpy as np
+    import oracle
+    from dsa_inputs import configs
+    pos = configs.sample_rows(wl, rows)
+    q = configs.q_bf16(wl, pos)
+    dO = configs.dout_bf16(wl, pos)
+    sel = configs.random_selection(wl, pos)
+    kvs = [configs.kv_bf16(wl, 0, s[s >= 0]) for s in sel]
+    print(f"[bench] CPU oracle baseline on {len(pos)} rows", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(len(pos)):
+        oracle.sparse_mla_bwd_row(q[i], kvs[i], dO[i], wl.scale)
+    dt = time.perf_counter() - t0
+    return {"value": len(pos) / dt, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(pos)} seeded-random query rows of {wl.name} (positions {int(pos.min())}.."
+                      f"{int(pos.max())}), gradient of one query over its selected rows (k = {wl.k}, H = {wl.H}), "
+                      f"single-threaded C oracle in fp64, {dt:.1f} s"}
 
 
 def bench_kl(args, wl):
