@@ -578,7 +578,6 @@ def bench_bwd(args, wl):
     come from one fused forward call (untimed); each timed step is one
     dsa_sparse_mla_bwd call (dq kernel, then dkv kernel, per 8192-query tile),
     timed in the two phases of the prefill bench."""
-    import numpy as np
     import torch
 
     import sparse_attention_long_08_amd as dsa
@@ -601,7 +600,7 @@ def bench_bwd(args, wl):
     device.fill(dout, T, H * wl.D_v, device.BF16_NORMAL, wl.seed, gen.STREAM_DOUT)
     dq = torch.empty((T, H, wl.D_qk), dtype=torch.float32, device="cuda")
     dkv = torch.empty((N, wl.D_qk), dtype=torch.float32, device="cuda")
-    nb = dsa.dsa_sparse_mla_bwd_workspace_bytes(T, H, k)
+    nb = dsa.dsa_sparse_mla_bwd_workspace_bytes(T, N, H, k)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
 
     def fused():
@@ -621,15 +620,23 @@ def bench_bwd(args, wl):
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     print(f"[bench] {args.steps} backward steps done: {ms_per_step:.1f} ms per step", file=sys.stderr, flush=True)
     rec_t, ev_ms_per_step = launch_times(dsa, torch, stream, fused, args.steps)
-    stage_ms = {kind: rec_t[kind][0] / args.steps for kind in ("mla_bwd_dq", "mla_bwd_dkv")}
+    kinds = ("mla_bwd_dq", "mla_bwd_dkv", "mla_bwd_reduce")
+    stage_ms = {kind: rec_t[kind][0] / args.steps for kind in kinds}
     w = algorithmic_work(wl, T)
-    # per selected (query, entry) pair and head: dq kernel forms the logits
-    # (576), dP (512) and dq (576); dkv kernel dS^T q (576) and P^T dO (512)
+    # per selected (query, entry) pair and head: the dq kernel forms the logits
+    # (576), dP (512) and dq (576); the dkv kernel dS^T q (576) and P^T dO (512).
+    # The row sums read each pair's fp32 addend row once and update dkv.
     flops = {"mla_bwd_dq": w["selected"] * 2 * H * (wl.D_qk + wl.D_v + wl.D_qk),
              "mla_bwd_dkv": w["selected"] * 2 * H * (wl.D_qk + wl.D_v)}
+    red_bytes = w["selected"] * (wl.D_qk * 4 + 2 * 4 + 4)
     dom = max(stage_ms, key=stage_ms.get)
     launches = rec_t[dom][1] // args.steps
-    ach = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    if dom == "mla_bwd_reduce":
+        bound, unit, peak = "hbm", "GB/s", PEAK_HBM_GBS
+        ach = red_bytes / (stage_ms[dom] * 1e-3) / 1e9
+    else:
+        bound, unit, peak = "mfma", "TFLOP/s", PEAK_BF16_TFLOPS
+        ach = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
     total_tf = sum(flops.values()) / (ms_per_step * 1e-3) / 1e12
     rec = {
         "metric": "DSA sparse MLA-MQA attention backward query-tokens/s",
@@ -648,8 +655,8 @@ def bench_bwd(args, wl):
         "data": "synthetic (seeded counter-based generator, device-resident; selection from the fused forward)",
         "config": {"workload": wl.name, "L": T, "k": k, "H": H, "D_qk": wl.D_qk, "D_v": wl.D_v, "causal": True,
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": counter_traffic(wl.name, dom),
+        "roofline": {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+                     "frac": ach / peak, "traffic": counter_traffic(wl.name, dom),
                      "launches_per_step": launches, "avg_launch_ms": stage_ms[dom] / max(launches, 1)},
         "stages_ms": stage_ms,
         "step_tflops": total_tf,

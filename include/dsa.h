@@ -85,8 +85,9 @@ enum {
   DSA_KERNEL_INDEXER_KL = 3, /* indexer KL loss (sparse training stage) */
   DSA_KERNEL_DENSE_KL = 4,   /* indexer KL loss (dense warm-up stage) */
   DSA_KERNEL_MLA_BWD_DQ = 5, /* attention backward: dq, P and dS */
-  DSA_KERNEL_MLA_BWD_DKV = 6,/* attention backward: dkv scatter */
-  DSA_KERNEL_KINDS = 7
+  DSA_KERNEL_MLA_BWD_DKV = 6,/* attention backward: per-entry dkv addends */
+  DSA_KERNEL_MLA_BWD_REDUCE = 7, /* attention backward: addends summed per cache row */
+  DSA_KERNEL_KINDS = 8
 };
 dsa_status dsa_timing_begin(void);
 dsa_status dsa_timing_end(double* ms, int64_t* launches, int32_t n_kinds);
@@ -179,13 +180,16 @@ dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, 
  *   dq [T, H, D_qk] fp32 out (overwritten); dkv [N, D_qk] fp32 out (zeroed,
  *   then accumulated; rows no query selects are 0).
  * P and dS enter the gradient products as bf16 (relative error ~2^-9 per
- * term); products are bf16 x bf16 with fp32 accumulation.  dkv is summed with
- * fp32 atomics, so its rounding depends on the order the workgroups run in.
- * ws: P and dS of a tile of queries, size from
- * dsa_sparse_mla_bwd_workspace_bytes(T, H, k) (DSA_ERR_WORKSPACE_TOO_SMALL
- * below it).  All pointers are device memory owned by the caller.
+ * term); products are bf16 x bf16 with fp32 accumulation.  Each (query,
+ * entry) contribution to dkv is formed as an fp32 row; the rows of one cache
+ * row are summed in fp32 in an order that may vary from call to call.
+ * ws: P, dS and the contribution rows of a tile of up to 2048 queries plus
+ * their grouping by cache row; size from
+ * dsa_sparse_mla_bwd_workspace_bytes(T, N, H, k) (about 12 GB at k = 2048,
+ * H = 128; DSA_ERR_WORKSPACE_TOO_SMALL below it).  N <= 2^30.  All pointers
+ * are device memory owned by the caller.
  */
-size_t dsa_sparse_mla_bwd_workspace_bytes(int64_t T, int32_t H, int32_t k);
+size_t dsa_sparse_mla_bwd_workspace_bytes(int64_t T, int64_t N, int32_t H, int32_t k);
 dsa_status dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* out,
                               const float* lse, const uint16_t* dout, int64_t T, int64_t N, int32_t H,
                               int32_t D_qk, int32_t D_v, int32_t k, float scale, float* dq, float* dkv,

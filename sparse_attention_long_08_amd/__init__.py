@@ -31,7 +31,7 @@ SIGNATURES = {
     "dsa_sparse_mla_fwd_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
     "dsa_sparse_mla_fwd": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p,
                                     _c_p, _c_p, _c_sz, _c_p]),
-    "dsa_sparse_mla_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32]),
+    "dsa_sparse_mla_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32, _c_i32]),
     "dsa_sparse_mla_bwd": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "dsa_sparse_mla_fwd_paged_workspace_bytes": (_c_sz, [_c_i64, _c_i32, _c_i32, _c_i32]),
@@ -117,7 +117,8 @@ def dsa_abi_version() -> int:
 
 
 # stage kinds of dsa_timing_end
-TIMING_KINDS = ("indexer", "topk", "attention", "indexer_kl", "dense_kl", "mla_bwd_dq", "mla_bwd_dkv")
+TIMING_KINDS = ("indexer", "topk", "attention", "indexer_kl", "dense_kl", "mla_bwd_dq", "mla_bwd_dkv",
+                "mla_bwd_reduce")
 
 
 def dsa_timing_begin() -> None:
@@ -157,8 +158,8 @@ def dsa_sparse_mla_fwd(q, kv, idx, T, N, H, D_qk, D_v, k, scale, out, lse, ws, w
           _ptr(ws), ws_bytes, _stream(stream))
 
 
-def dsa_sparse_mla_bwd_workspace_bytes(T, H, k) -> int:
-    return load().dsa_sparse_mla_bwd_workspace_bytes(T, H, k)
+def dsa_sparse_mla_bwd_workspace_bytes(T, N, H, k) -> int:
+    return load().dsa_sparse_mla_bwd_workspace_bytes(T, N, H, k)
 
 
 def dsa_sparse_mla_bwd(q, kv, idx, out, lse, dout, T, N, H, D_qk, D_v, k, scale, dq, dkv, ws, ws_bytes,

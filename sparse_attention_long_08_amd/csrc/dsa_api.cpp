@@ -292,14 +292,41 @@ dsa_status dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32
                  (hipStream_t)stream);
 }
 
-// Queries per tile of the attention backward: P and dS of a tile sit in the
-// workspace (2 * tile * k * Hp bf16: 8.6 GB at k = 2048, 128 heads).
-constexpr int64_t kBwdTile = 8192;
+// Queries per tile of the attention backward.  A tile's workspace holds P
+// and dS (bf16 [tile, k, Hp]), the fp32 addend rows [tile, k, 576] (9.7 GB at
+// k = 2048) and the inverted index of its entries.
+constexpr int64_t kBwdTile = 2048;
 
-size_t dsa_sparse_mla_bwd_workspace_bytes(int64_t T, int32_t H, int32_t k) {
-  if (T <= 0 || H < 1 || k < 1) return 0;
+namespace {
+struct BwdWs {
+  size_t p, ds, addend, count, offsets, list, total;
+};
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+BwdWs bwd_ws(int64_t T, int64_t N, int32_t H, int32_t k) {
   const int64_t tile = T < kBwdTile ? T : kBwdTile;
-  return (size_t)(2 * tile * (int64_t)k * dsa::mla_bwd_padded_heads(H) * 2);
+  const size_t ent = (size_t)tile * (size_t)k;
+  BwdWs w;
+  size_t o = 0;
+  w.p = o;
+  o += al256(ent * dsa::mla_bwd_padded_heads(H) * 2);
+  w.ds = o;
+  o += al256(ent * dsa::mla_bwd_padded_heads(H) * 2);
+  w.addend = o;
+  o += al256(ent * 576 * 4);
+  w.count = o;
+  o += al256((size_t)N * 4);
+  w.offsets = o;
+  o += al256((size_t)(N + 1) * 4);
+  w.list = o;
+  o += al256(ent * 4);
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+size_t dsa_sparse_mla_bwd_workspace_bytes(int64_t T, int64_t N, int32_t H, int32_t k) {
+  if (T <= 0 || N < 1 || H < 1 || k < 1) return 0;
+  return bwd_ws(T, N, H, k).total;
 }
 
 dsa_status dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* out,
@@ -307,6 +334,7 @@ dsa_status dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32
                               int32_t D_qk, int32_t D_v, int32_t k, float scale, float* dq, float* dkv,
                               void* ws, size_t ws_bytes, dsa_stream_t stream) {
   REQUIRE(T >= 0 && N >= 1, DSA_ERR_INVALID_ARG, "T must be >= 0 and N >= 1");
+  REQUIRE(N <= (int64_t)1 << 30, DSA_ERR_UNSUPPORTED, "N must be <= 2^30 (got %lld)", (long long)N);
   if (dsa_status s = check_mla_shape(H, D_qk, D_v, k)) return s;
   REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
   REQUIRE_PTR(dkv);
@@ -316,12 +344,13 @@ dsa_status dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32
     REQUIRE_PTR(dq); REQUIRE_PTR(ws);
     REQUIRE_AL(q); REQUIRE_AL(kv); REQUIRE_AL(idx); REQUIRE_AL(out); REQUIRE_AL(lse); REQUIRE_AL(dout);
     REQUIRE_AL(dq); REQUIRE_AL(ws);
-    const size_t need = dsa_sparse_mla_bwd_workspace_bytes(T, H, k);
+    const size_t need = dsa_sparse_mla_bwd_workspace_bytes(T, N, H, k);
     REQUIRE(ws_bytes >= need, DSA_ERR_WORKSPACE_TOO_SMALL, "ws_bytes (%zu) below %zu", ws_bytes, need);
   }
   hipStream_t st = (hipStream_t)stream;
   if (hipError_t e = dsa::launch_zero_f32(dkv, N * (int64_t)D_qk, st)) return hip_check(e, "dkv clear");
-  const int64_t Hp = dsa::mla_bwd_padded_heads(H);
+  const BwdWs w = bwd_ws(T, N, H, k);
+  uint8_t* const base = (uint8_t*)ws;
   for (int64_t t0 = 0; t0 < T; t0 += kBwdTile) {
     const int64_t tn = T - t0 < kBwdTile ? T - t0 : kBwdTile;
     dsa::MlaBwdArgs a;
@@ -337,13 +366,19 @@ dsa_status dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32
     a.k = k;
     a.scale = scale;
     a.dq = dq + t0 * H * (int64_t)D_qk;
-    a.pbuf = (uint16_t*)ws;
-    a.dsbuf = (uint16_t*)ws + tn * (int64_t)k * Hp;
+    a.pbuf = (uint16_t*)(base + w.p);
+    a.dsbuf = (uint16_t*)(base + w.ds);
+    a.addend = (float*)(base + w.addend);
+    a.row_count = (int32_t*)(base + w.count);
+    a.row_offsets = (int32_t*)(base + w.offsets);
+    a.row_list = (int32_t*)(base + w.list);
     a.dkv = dkv;
-    hipError_t e = timed(DSA_KERNEL_MLA_BWD_DQ, st, [&] { return dsa::launch_sparse_mla_bwd(a, false, st); });
+    hipError_t e = timed(DSA_KERNEL_MLA_BWD_DQ, st, [&] { return dsa::launch_sparse_mla_bwd(a, 0, st); });
     if (e != hipSuccess) return hip_check(e, "attention backward (dq) launch");
-    e = timed(DSA_KERNEL_MLA_BWD_DKV, st, [&] { return dsa::launch_sparse_mla_bwd(a, true, st); });
+    e = timed(DSA_KERNEL_MLA_BWD_DKV, st, [&] { return dsa::launch_sparse_mla_bwd(a, 1, st); });
     if (e != hipSuccess) return hip_check(e, "attention backward (dkv) launch");
+    e = timed(DSA_KERNEL_MLA_BWD_REDUCE, st, [&] { return dsa::launch_sparse_mla_bwd(a, 2, st); });
+    if (e != hipSuccess) return hip_check(e, "attention backward (row sums) launch");
   }
   return ok();
 }

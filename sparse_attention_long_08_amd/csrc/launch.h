@@ -84,8 +84,10 @@ hipError_t launch_indexer_dense_kl(const uint16_t* q, const uint16_t* kv, int64_
 
 // Sparse MLA-MQA backward over one tile of T queries.  Stage 0 (dq kernel):
 // dq, and P / dS of every entry into pbuf / dsbuf ([T, k, Hp] bf16, Hp =
-// mla_bwd_padded_heads(H)); stage 1 (dkv kernel): adds the entries'
-// contributions to dkv (fp32 atomics; dkv must be zeroed beforehand).
+// mla_bwd_padded_heads(H)); stage 1 (dkv kernel): each entry's contribution
+// to its cache row into addend ([T, k, 576] fp32); stage 2: groups the
+// entries by cache row (row_count [N], row_offsets [N+1], row_list [T*k]
+// int32) and adds each row's sum to dkv (dkv cleared beforehand).
 struct MlaBwdArgs {
   const uint16_t* q;
   const uint16_t* kv;
@@ -101,10 +103,14 @@ struct MlaBwdArgs {
   float* dq;
   uint16_t* pbuf;
   uint16_t* dsbuf;
+  float* addend;
+  int32_t* row_count;
+  int32_t* row_offsets;
+  int32_t* row_list;
   float* dkv;
 };
 int32_t mla_bwd_padded_heads(int32_t H);
-hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, bool dkv_stage, hipStream_t st);
+hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int stage, hipStream_t st);
 hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t st);
 
 // Number of key splits used for T queries of H heads with k entries each.

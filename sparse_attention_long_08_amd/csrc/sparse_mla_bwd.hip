@@ -25,12 +25,17 @@
 // and dS as bf16 to a workspace laid out [query][entry][head].
 //
 // mla_bwd_dkv_kernel: one workgroup of 8 waves per query; each wave owns
-// four or five 16-column tiles of the 576 latent dims.  It holds q and dO of all heads in the
-// B layout of the head contraction (heads on k), streams the P and dS tiles
-// of each 32-entry block through LDS by DMA, forms
-//   dkv_block = dS^T q + P^T dO          (32 entries x 576 dims)
-// and adds it to the cache rows with fp32 atomics.  dkv sums over queries, so
-// this is a scatter; the atomics are the only cross-workgroup traffic.
+// four or five 16-column tiles of the 576 latent dims.  It holds q and dO of
+// all heads in the B layout of the head contraction (heads on k), streams
+// the P and dS tiles of each 32-entry block through LDS by DMA, forms
+//   addend_block = dS^T q + P^T dO          (32 entries x 576 dims)
+// and stores it, one fp32 row per (query, entry).
+//
+// dkv sums the addends over every (query, entry) that selected a row, so it
+// is a scatter.  Instead of atomics (whose adds all travel to the memory
+// side, since 75 MB of dkv rows fit no L2), the tile's entries are grouped by
+// cache row through an inverted index (count, scan, fill) and
+// dkv_reduce_kernel sums each row's addends with one wave per row.
 #include "common.h"
 #include "launch.h"
 
@@ -92,7 +97,7 @@ struct BwdParams {
   float* dq;             // [T, H, 576]
   uint16_t* pbuf;        // [T, k, Hp] bf16 P
   uint16_t* dsbuf;       // [T, k, Hp] bf16 dS (scale folded in)
-  float* dkv;            // [N, 576], accumulated
+  float* addend;         // [T, k, 576] fp32: each entry's contribution to its cache row
 };
 
 // Resolves the entries of query t to cache rows (-1: skipped), padded with
@@ -404,18 +409,18 @@ __global__ __launch_bounds__(kKvThreads, 1) void mla_bwd_dkv_kernel(BwdParams p)
       }
       __builtin_amdgcn_sched_barrier(0);  // one k-step of operands live at a time
     }
-    // scatter: lane (dim 16 tile + hn, qd) holds entries 16kt + 4qd + r
+    // addend rows: lane (dim 16 tile + hn, qd) holds entries 16kt + 4qd + r
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int32_t row = rows[blk * kBlk + 16 * kt + 4 * qd + r];
-        if (row >= 0) {
-          float* dst = p.dkv + (int64_t)row * kDqk + hn;
+        const int e = blk * kBlk + 16 * kt + 4 * qd + r;
+        if (e < p.k) {
+          float* dst = p.addend + (t * (int64_t)p.k + e) * kDqk + hn;
 #pragma unroll
           for (int ci = 0; ci < kTilesPerWave; ++ci) {
             const int tile = kv_tile(wave, ci);
-            if (tile >= 0) unsafeAtomicAdd(dst + 16 * tile, acc[kt][ci][r]);
+            if (tile >= 0) dst[16 * tile] = acc[kt][ci][r];
           }
         }
       }
@@ -428,6 +433,96 @@ __global__ __launch_bounds__(kKvThreads, 1) void mla_bwd_dkv_kernel(BwdParams p)
     if (blk + 1 < nb) gather((blk + 1) & 1, blk + 1);
     step(blk & 1, blk);
   }
+}
+
+// ---------------------------------------------------------------- inverted index
+// Entries of the tile (e = t*k + j) grouped by cache row: count per row,
+// exclusive scan into offsets (cursor starts as a copy), fill the list.
+__global__ void csr_count_kernel(const int32_t* __restrict__ idx, int64_t n_ent, int64_t N,
+                                 int32_t* __restrict__ count) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n_ent; e += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t s = idx[e];
+    if (s >= 0 && s < N) atomicAdd(count + s, 1);
+  }
+}
+
+// One workgroup of 1024 threads: thread i scans a contiguous chunk.
+__global__ __launch_bounds__(1024) void csr_scan_kernel(int32_t* __restrict__ count, int32_t* __restrict__ offsets,
+                                                        int64_t N) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t chunk = (N + 1023) / 1024;
+  const int64_t b = tid * chunk, e = b + chunk < N ? b + chunk : N;
+  int32_t sum = 0;
+  for (int64_t i = b; i < e; ++i) sum += count[i];
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int32_t v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    offsets[N] = run;
+  }
+  __syncthreads();
+  int32_t run = part[tid];
+  for (int64_t i = b; i < e; ++i) {
+    const int32_t c = count[i];
+    offsets[i] = run;
+    count[i] = run;  // becomes the fill cursor
+    run += c;
+  }
+}
+
+__global__ void csr_fill_kernel(const int32_t* __restrict__ idx, int64_t n_ent, int64_t N,
+                                int32_t* __restrict__ cursor, int32_t* __restrict__ list) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n_ent; e += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t s = idx[e];
+    if (s >= 0 && s < N) list[atomicAdd(cursor + s, 1)] = (int32_t)e;
+  }
+}
+
+// dkv[s] += sum of the addend rows listed for s: one wave per cache row, lane
+// l holding dims l + 64c (c < 9); list entries are fetched 64 at a time.
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ list,
+                                                         const float* __restrict__ addend, float* __restrict__ dkv,
+                                                         int64_t N) {
+  const int lane = threadIdx.x & 63;
+  const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= N) return;
+  const int32_t b = offsets[s], e = offsets[s + 1];
+  if (b == e) return;
+  float acc[9];
+#pragma unroll
+  for (int c = 0; c < 9; ++c) acc[c] = 0.f;
+  for (int32_t i0 = b; i0 < e; i0 += 64) {
+    const int32_t n = e - i0 < 64 ? e - i0 : 64;
+    const int32_t mine = lane < n ? list[i0 + lane] : 0;
+    int32_t j = 0;
+    for (; j + 2 <= n; j += 2) {
+      const float* r0 = addend + (int64_t)__shfl(mine, j, 64) * kDqk + lane;
+      const float* r1 = addend + (int64_t)__shfl(mine, j + 1, 64) * kDqk + lane;
+      float v0[9], v1[9];
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        v0[c] = r0[64 * c];
+        v1[c] = r1[64 * c];
+      }
+#pragma unroll
+      for (int c = 0; c < 9; ++c) acc[c] += v0[c] + v1[c];
+    }
+    if (j < n) {
+      const float* r0 = addend + (int64_t)__shfl(mine, j, 64) * kDqk + lane;
+#pragma unroll
+      for (int c = 0; c < 9; ++c) acc[c] += r0[64 * c];
+    }
+  }
+  float* d = dkv + s * kDqk + lane;
+#pragma unroll
+  for (int c = 0; c < 9; ++c) d[64 * c] += acc[c];
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ x, int64_t n) {
@@ -448,8 +543,22 @@ hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, bool dkv_stage, hipStream_t st) {
+hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int stage, hipStream_t st) {
   if (a.T <= 0) return hipSuccess;
+  if (stage == 2) {  // inverted index of the tile's entries, then the per-row sums
+    const int64_t n_ent = a.T * (int64_t)a.k;
+    hipError_t e = launch_zero_f32((float*)a.row_count, a.N, st);  // int32 zeros
+    if (e != hipSuccess) return e;
+    int64_t g = (n_ent + 255) / 256;
+    g = g > 16384 ? 16384 : g;
+    hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)g), dim3(256), 0, st, a.idx, n_ent, a.N, a.row_count);
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, st, a.row_count, a.row_offsets, a.N);
+    hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)g), dim3(256), 0, st, a.idx, n_ent, a.N, a.row_count,
+                       a.row_list);
+    hipLaunchKernelGGL(dkv_reduce_kernel, dim3((unsigned)((a.N + 3) / 4)), dim3(256), 0, st, a.row_offsets,
+                       a.row_list, a.addend, a.dkv, a.N);
+    return hipGetLastError();
+  }
   BwdParams p;
   p.q = a.q;
   p.kv = a.kv;
@@ -467,8 +576,8 @@ hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, bool dkv_stage, hipStream_
   p.dq = a.dq;
   p.pbuf = a.pbuf;
   p.dsbuf = a.dsbuf;
-  p.dkv = a.dkv;
-  if (!dkv_stage) {
+  p.addend = a.addend;
+  if (stage == 0) {
     const int n_half = (p.Hp + 63) / 64;
     const int64_t grid = n_half == 2 ? (a.T + 7) / 8 * 16 : a.T;
     hipLaunchKernelGGL(mla_bwd_dq_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, p);

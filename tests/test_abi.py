@@ -173,12 +173,22 @@ def test_sparse_mla_bwd_validation(args, status, needle):
     assert needle in lib.dsa_last_error_message().decode()
 
 
+def _bwd_ws_bytes(T, N, H, k):
+    """The documented layout: P and dS (bf16 [tile, k, Hp]), fp32 addend rows
+    [tile, k, 576], row counts [N], row offsets [N+1] and the entry list
+    [tile * k] (int32), each region 256-byte aligned; tile = min(T, 2048)."""
+    al = lambda x: (x + 255) // 256 * 256
+    ent = min(T, 2048) * k
+    hp = (H + 31) // 32 * 32
+    return 2 * al(ent * hp * 2) + al(ent * 576 * 4) + al(N * 4) + al((N + 1) * 4) + al(ent * 4)
+
+
 def test_sparse_mla_bwd_workspace():
     lib = dsa.load()
-    # P and dS of a tile of at most 8192 queries, heads padded to a multiple of 32
-    assert lib.dsa_sparse_mla_bwd_workspace_bytes(4, 8, 16) == 2 * 4 * 16 * 32 * 2
-    assert lib.dsa_sparse_mla_bwd_workspace_bytes(32768, 128, 2048) == 2 * 8192 * 2048 * 128 * 2
-    assert lib.dsa_sparse_mla_bwd_workspace_bytes(0, 128, 2048) == 0
-    nb = lib.dsa_sparse_mla_bwd_workspace_bytes(4, 8, 16)
+    for T, N, H, k in [(4, 64, 8, 16), (32768, 32768, 128, 2048), (3000, 5000, 96, 100)]:
+        assert lib.dsa_sparse_mla_bwd_workspace_bytes(T, N, H, k) == _bwd_ws_bytes(T, N, H, k)
+    assert lib.dsa_sparse_mla_bwd_workspace_bytes(32768, 32768, 128, 2048) < 12 * 2 ** 30
+    assert lib.dsa_sparse_mla_bwd_workspace_bytes(0, 64, 128, 2048) == 0
+    nb = lib.dsa_sparse_mla_bwd_workspace_bytes(4, 64, 8, 16)
     st = lib.dsa_sparse_mla_bwd(*((FAKE,) * 6), 4, 64, 8, 576, 512, 16, 0.07, FAKE, FAKE, FAKE, nb - 1, 0)
     assert st == 3 and "ws_bytes" in lib.dsa_last_error_message().decode()

@@ -46,7 +46,7 @@ def _bwd_on_gpu(dsa, q, kv, idx, dO, T, N, H, k, scale):
         dsa.dsa_sparse_mla_fwd(q_d, kv_d, idx_d, T, N, H, 576, 512, k, scale, out, lse, ws, nb)
     dq = torch.full((max(T, 1), H, 576), float("nan"), dtype=torch.float32, device="cuda")
     dkv = torch.full((N, 576), float("nan"), dtype=torch.float32, device="cuda")
-    nbb = dsa.dsa_sparse_mla_bwd_workspace_bytes(T, H, k)
+    nbb = dsa.dsa_sparse_mla_bwd_workspace_bytes(T, N, H, k)
     wsb = ws_tensor(nbb)
     dsa.dsa_sparse_mla_bwd(q_d, kv_d, idx_d, out, lse, do_d, T, N, H, 576, 512, k, scale, dq, dkv, wsb, nbb)
     torch.cuda.synchronize()
