@@ -293,7 +293,7 @@ dsa_status dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32
 }
 
 // Queries per tile of the attention backward.  A tile's workspace holds P
-// and dS (bf16 [tile, k, Hp]), the fp32 addend rows [tile, k, 576] (9.7 GB at
+// and dS (bf16 [tile, k rounded up to 32, H rounded up to 64]), the fp32 addend rows [tile, k, 576] (9.7 GB at
 // k = 2048) and the inverted index of its entries.
 constexpr int64_t kBwdTile = 2048;
 
@@ -305,12 +305,13 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 BwdWs bwd_ws(int64_t T, int64_t N, int32_t H, int32_t k) {
   const int64_t tile = T < kBwdTile ? T : kBwdTile;
   const size_t ent = (size_t)tile * (size_t)k;
+  const size_t ent_p = (size_t)tile * (size_t)((k + 31) / 32 * 32);
   BwdWs w;
   size_t o = 0;
   w.p = o;
-  o += al256(ent * dsa::mla_bwd_padded_heads(H) * 2);
+  o += al256(ent_p * dsa::mla_bwd_slot_heads(H) * 2);
   w.ds = o;
-  o += al256(ent * dsa::mla_bwd_padded_heads(H) * 2);
+  o += al256(ent_p * dsa::mla_bwd_slot_heads(H) * 2);
   w.addend = o;
   o += al256(ent * 576 * 4);
   w.count = o;

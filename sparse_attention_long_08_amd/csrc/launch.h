@@ -83,8 +83,8 @@ hipError_t launch_indexer_dense_kl(const uint16_t* q, const uint16_t* kv, int64_
                                    hipStream_t st);
 
 // Sparse MLA-MQA backward over one tile of T queries.  Stage 0 (dq kernel):
-// dq, and P / dS of every entry into pbuf / dsbuf ([T, k, Hp] bf16, Hp =
-// mla_bwd_padded_heads(H)); stage 1 (dkv kernel): each entry's contribution
+// dq, and P / dS of every entry into pbuf / dsbuf ([T, kp, Hs] bf16, kp = k
+// rounded up to 32, Hs = mla_bwd_slot_heads(H)); stage 1 (dkv kernel): each entry's contribution
 // to its cache row into addend ([T, k, 576] fp32); stage 2: groups the
 // entries by cache row (row_count [N], row_offsets [N+1], row_list [T*k]
 // int32) and adds each row's sum to dkv (dkv cleared beforehand).
@@ -110,6 +110,7 @@ struct MlaBwdArgs {
   float* dkv;
 };
 int32_t mla_bwd_padded_heads(int32_t H);
+int32_t mla_bwd_slot_heads(int32_t H);
 hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int stage, hipStream_t st);
 hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t st);
 

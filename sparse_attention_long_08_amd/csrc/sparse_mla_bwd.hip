@@ -90,13 +90,16 @@ struct BwdParams {
   int64_t T;
   int64_t N;
   int32_t H;
-  int32_t Hp;            // heads padded to a multiple of 32 (workspace row)
+  int32_t Hp;            // heads padded to a multiple of 32 (k-steps of the head contraction)
+  int32_t Hs;            // heads padded to a multiple of 64: the workspace row (one slot per dq-kernel lane)
   int32_t k;
+  int32_t kp;            // k rounded up to whole blocks: entry stride of pbuf / dsbuf
+  uint32_t kv_bytes;     // extent of kv when below 4 GiB (buffer-form DMA), else 0
   float scale;
   float scale_log2;      // scale * log2(e)
   float* dq;             // [T, H, 576]
-  uint16_t* pbuf;        // [T, k, Hp] bf16 P
-  uint16_t* dsbuf;       // [T, k, Hp] bf16 dS (scale folded in)
+  uint16_t* pbuf;        // [T, kp, Hs] bf16 P (entries k .. kp-1 and heads H .. Hs-1 are padding)
+  uint16_t* dsbuf;       // [T, kp, Hs] bf16 dS (scale folded in)
   float* addend;         // [T, k, 576] fp32: each entry's contribution to its cache row
 };
 
@@ -113,10 +116,24 @@ __device__ __forceinline__ void load_rows(const BwdParams& p, int64_t t, int32_t
   }
 }
 
+// Drives a three-stage ring; the stages arrive restrict-qualified so that
+// the compiler sees the stage being read is not the one a DMA is filling.
+template <class Step>
+__device__ __forceinline__ void run_ring3(uint8_t* __restrict__ sa, uint8_t* __restrict__ sb,
+                                          uint8_t* __restrict__ sc, int nb, Step& step) {
+  for (int blk = 0; blk < nb; blk += 3) {
+    step(sa, sc, blk);
+    if (blk + 1 < nb) step(sb, sa, blk + 1);
+    if (blk + 2 < nb) step(sc, sb, blk + 2);
+  }
+}
+
 // ---------------------------------------------------------------- dq kernel
+template <bool kBufDma>
 __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage2[kStage];
   __shared__ int32_t rows[kMaxK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hn = lane & 15, qd = lane >> 4;
@@ -136,9 +153,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
   }
   if (t >= p.T) return;
   const int head = 64 * half + 16 * wave + hn;
-  // a wave whose heads are all padding computes zeros and stores nothing,
-  // but still joins every barrier below
-  const bool wave_on = 64 * half + 16 * wave < p.Hp;
+  // a wave whose heads are all padding computes zeros, stores them to its
+  // own padding slots and joins every barrier
   const bool hv = head < p.H;
   const int nb = (p.k + kBlk - 1) / kBlk;
   load_rows(p, t, rows, nb);
@@ -177,14 +193,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
   // lane L carries row 8w + L/8 into slot L%8 of the band.
   const int g_row = 8 * wave + (lane >> 3);
   const int g_chunk = (lane & 7) ^ swz(g_row);
+  // the buffer form of the DMA leaves the compiler's LDS wait counting exact
+  const __amdgpu_buffer_rsrc_t kv_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)0, (int)p.kv_bytes, 0x00020000);
   auto gather = [&](uint8_t* base, int blk) {
     int32_t row = rows[blk * kBlk + g_row];
     row = row < 0 ? 0 : row;  // skipped entries read row 0; P = 0 masks them
-    const uint16_t* src = p.kv + ((uint64_t)(uint32_t)row * kDqk + 8 * g_chunk);
+    if constexpr (kBufDma) {
+      const uint32_t voff = (uint32_t)row * (kDqk * 2) + 16 * g_chunk;
 #pragma unroll
-    for (int bd = 0; bd < 9; ++bd)
-      __builtin_amdgcn_global_load_lds((const void*)(src + 64 * bd), (lds_ptr)(base + bd * kBand + wave * 1024), 16,
-                                       0, 0);
+      for (int bd = 0; bd < 9; ++bd)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (lds_ptr)(base + bd * kBand + wave * 1024), 16,
+                                                 voff + 128 * bd, 0, 0, 0);
+    } else {
+      const uint16_t* src = p.kv + ((uint64_t)(uint32_t)row * kDqk + 8 * g_chunk);
+#pragma unroll
+      for (int bd = 0; bd < 9; ++bd)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 64 * bd), (lds_ptr)(base + bd * kBand + wave * 1024),
+                                         16, 0, 0);
+    }
   };
 
   // Operand offsets.  Key tile kt, k-step ks (A of S^T and dP^T): lane (row
@@ -220,10 +247,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) dqa[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* const pdst = p.pbuf + (t * (int64_t)p.k) * p.Hp + (wave_on ? head : 0);
-  uint16_t* const sdst = p.dsbuf + (t * (int64_t)p.k) * p.Hp + (wave_on ? head : 0);
+  uint16_t* const pdst = p.pbuf + (t * (int64_t)p.kp) * p.Hs + head;
+  uint16_t* const sdst = p.dsbuf + (t * (int64_t)p.kp) * p.Hs + head;
 
-  auto step = [&](const uint8_t* __restrict__ cur, int blk) {
+  // Wait for this wave's DMA of block blk.  Vector memory operations retire
+  // in issue order; after that DMA each earlier step issued its 16 P / dS
+  // stores and the DMA two blocks ahead of it (9 operations).
+  auto wait_block = [&](int blk) {
+    if (blk == 0) {
+      if (nb > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if (blk == 1) {
+      if (nb > 2) asm volatile("s_waitcnt vmcnt(25)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      if (blk + 1 < nb) asm volatile("s_waitcnt vmcnt(41)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+  };
+
+  auto step = [&](uint8_t* __restrict__ cur, uint8_t* __restrict__ ahead, int blk) {
+    wait_block(blk);  // block blk landed everywhere; block blk-1's stage is free
+    if (blk + 2 < nb) gather(ahead, blk + 2);
     const lds_u8_ptr base = (lds_u8_ptr)cur;
     // logits and dP of the block
     v4f sacc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
@@ -251,18 +297,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
       }
     const v8bf bop = (v8bf){to_bf16(dv[0][0]), to_bf16(dv[0][1]), to_bf16(dv[0][2]), to_bf16(dv[0][3]),
                             to_bf16(dv[1][0]), to_bf16(dv[1][1]), to_bf16(dv[1][2]), to_bf16(dv[1][3])};
-    if (wave_on) {
+    // 16 stores per lane and block, issued by every wave (a wave of padding
+    // heads writes the zeros of its own padded columns), so the wait counts
+    // above are exact; entries k .. kp-1 are padding rows
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = blk * kBlk + 16 * kt + 4 * qd + r;
-          if (e < p.k) {
-            pdst[(int64_t)e * p.Hp] = __builtin_bit_cast(uint16_t, to_bf16(pv[kt][r]));
-            sdst[(int64_t)e * p.Hp] = __builtin_bit_cast(uint16_t, to_bf16(dv[kt][r]));
-          }
-        }
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int e = blk * kBlk + 16 * kt + 4 * qd + r;
+        pdst[(int64_t)e * p.Hs] = __builtin_bit_cast(uint16_t, to_bf16(pv[kt][r]));
+        sdst[(int64_t)e * p.Hs] = __builtin_bit_cast(uint16_t, to_bf16(dv[kt][r]));
+      }
     // dq^T += K^T dS^T
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
@@ -275,14 +320,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
   };
 
   if (nb > 0) gather(stage0, 0);
-  for (int blk = 0; blk < nb; ++blk) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // block blk landed everywhere; block blk-1's stage is free
-    uint8_t* cur = (blk & 1) ? stage1 : stage0;
-    uint8_t* nxt = (blk & 1) ? stage0 : stage1;
-    if (blk + 1 < nb) gather(nxt, blk + 1);
-    step(cur, blk);
-  }
+  if (nb > 1) gather(stage1, 1);
+  run_ring3(stage0, stage1, stage2, nb, step);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (hv) {
     float* drow = p.dq + (t * p.H + head) * (int64_t)kDqk + 4 * qd;
@@ -371,7 +411,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void mla_bwd_dkv_kernel(BwdParams p)
       int e = blk * kBlk + j;
       e = e < p.k ? e : p.k - 1;
       if (8 * c < p.Hp) {
-        const int64_t off = (t * (int64_t)p.k + e) * p.Hp + 8 * c;
+        const int64_t off = (t * (int64_t)p.kp + e) * p.Hs + 8 * c;
         const uint16_t* src = arr ? p.dsbuf : p.pbuf;
         __builtin_amdgcn_global_load_lds((const void*)(src + off), (lds_ptr)(&pst[sidx][arr][0] + j0 * kPRow), 16,
                                          0, 0);
@@ -534,6 +574,7 @@ __global__ void zero_f32_kernel(float* __restrict__ x, int64_t n) {
 }  // namespace
 
 int32_t mla_bwd_padded_heads(int32_t H) { return (H + 31) / 32 * 32; }
+int32_t mla_bwd_slot_heads(int32_t H) { return (H + 63) / 64 * 64; }
 
 hipError_t launch_zero_f32(float* x, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
@@ -570,7 +611,10 @@ hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int stage, hipStream_t st)
   p.N = a.N;
   p.H = a.H;
   p.Hp = mla_bwd_padded_heads(a.H);
+  p.Hs = mla_bwd_slot_heads(a.H);
   p.k = a.k;
+  p.kp = (a.k + kBlk - 1) / kBlk * kBlk;
+  p.kv_bytes = a.N * (int64_t)kDqk * 2 < ((int64_t)1 << 32) ? (uint32_t)(a.N * (int64_t)kDqk * 2) : 0u;
   p.scale = a.scale;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.dq = a.dq;
@@ -580,7 +624,10 @@ hipError_t launch_sparse_mla_bwd(const MlaBwdArgs& a, int stage, hipStream_t st)
   if (stage == 0) {
     const int n_half = (p.Hp + 63) / 64;
     const int64_t grid = n_half == 2 ? (a.T + 7) / 8 * 16 : a.T;
-    hipLaunchKernelGGL(mla_bwd_dq_kernel, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+    if (p.kv_bytes)
+      hipLaunchKernelGGL(mla_bwd_dq_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL(mla_bwd_dq_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, st, p);
   } else {
     hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3((unsigned)a.T), dim3(kKvThreads), 0, st, p);
   }

@@ -174,13 +174,15 @@ def test_sparse_mla_bwd_validation(args, status, needle):
 
 
 def _bwd_ws_bytes(T, N, H, k):
-    """The documented layout: P and dS (bf16 [tile, k, Hp]), fp32 addend rows
-    [tile, k, 576], row counts [N], row offsets [N+1] and the entry list
-    [tile * k] (int32), each region 256-byte aligned; tile = min(T, 2048)."""
+    """The documented layout: P and dS (bf16 [tile, k rounded up to 32, H
+    rounded up to 64]), fp32 addend rows [tile, k, 576], row counts [N], row
+    offsets [N+1] and the entry list [tile * k] (int32), each region 256-byte
+    aligned; tile = min(T, 2048)."""
     al = lambda x: (x + 255) // 256 * 256
     ent = min(T, 2048) * k
-    hp = (H + 31) // 32 * 32
-    return 2 * al(ent * hp * 2) + al(ent * 576 * 4) + al(N * 4) + al((N + 1) * 4) + al(ent * 4)
+    ent_p = min(T, 2048) * ((k + 31) // 32 * 32)
+    hs = (H + 63) // 64 * 64
+    return 2 * al(ent_p * hs * 2) + al(ent * 576 * 4) + al(N * 4) + al((N + 1) * 4) + al(ent * 4)
 
 
 def test_sparse_mla_bwd_workspace():
