@@ -247,8 +247,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) dqa[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* const pdst = p.pbuf + (t * (int64_t)p.kp) * p.Hs + head;
-  uint16_t* const sdst = p.dsbuf + (t * (int64_t)p.kp) * p.Hs + head;
+  // workspace rows of this query (uniform base, 32-bit per-lane offsets)
+  uint16_t* const pdst = p.pbuf + (t * (int64_t)p.kp) * p.Hs;
+  uint16_t* const sdst = p.dsbuf + (t * (int64_t)p.kp) * p.Hs;
+  uint32_t st_off[2][4];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st_off[kt][r] = (uint32_t)((16 * kt + 4 * qd + r) * p.Hs + head);
 
   // Wait for this wave's DMA of block blk.  Vector memory operations retire
   // in issue order; after that DMA each earlier step issued its 16 P / dS
@@ -271,18 +277,41 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
     wait_block(blk);  // block blk landed everywhere; block blk-1's stage is free
     if (blk + 2 < nb) gather(ahead, blk + 2);
     const lds_u8_ptr base = (lds_u8_ptr)cur;
-    // logits and dP of the block
+    // logits and dP of the block; key tiles are read kPf k-steps ahead
+    constexpr int kPf = 3;
+    auto rd_k = [&](int kt, int ks) { return *(lds_v8bf_cptr)(base + (ks >> 1) * kBand + k_off[kt][ks & 1]); };
+    auto rd_t = [&](int ct) {
+      const uint32_t off = (ct >> 2) * kBand;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + off + t_off[0][ct & 3]));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + off + t_off[1][ct & 3]));
+      return __builtin_bit_cast(v8bf, (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
     v4f sacc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
     v4f pacc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
+    v8bf ab[kPf + 1][2];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) {
+      ab[i][0] = rd_k(0, i);
+      ab[i][1] = rd_k(1, i);
+    }
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
+      if (ks + kPf < kQSteps) {
+        ab[(ks + kPf) % (kPf + 1)][0] = rd_k(0, ks + kPf);
+        ab[(ks + kPf) % (kPf + 1)][1] = rd_k(1, ks + kPf);
+      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const v8bf a = *(lds_v8bf_cptr)(base + (ks >> 1) * kBand + k_off[kt][ks & 1]);
+        const v8bf a = ab[ks % (kPf + 1)][kt];
         sacc[kt] = mfma_bf16_16x16x32(a, qf[ks], sacc[kt]);
         if (ks < kVSteps) pacc[kt] = mfma_bf16_16x16x32(a, df[ks < kVSteps ? ks : 0], pacc[kt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first transposed key tiles of the dq product do not depend on dS
+    v8bf tb[kPf + 1];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) tb[i] = rd_t(i);
     // P and dS; lane holds keys 16kt + 4qd + r of its head
     float pv[2][4], dv[2][4];
 #pragma unroll
@@ -298,24 +327,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
     const v8bf bop = (v8bf){to_bf16(dv[0][0]), to_bf16(dv[0][1]), to_bf16(dv[0][2]), to_bf16(dv[0][3]),
                             to_bf16(dv[1][0]), to_bf16(dv[1][1]), to_bf16(dv[1][2]), to_bf16(dv[1][3])};
     // 16 stores per lane and block, issued by every wave (a wave of padding
-    // heads writes the zeros of its own padded columns), so the wait counts
+    // heads writes the zeros of its own padding slots), so the wait counts
     // above are exact; entries k .. kp-1 are padding rows
+    uint16_t* const pb = pdst + (int64_t)blk * kBlk * p.Hs;
+    uint16_t* const sb = sdst + (int64_t)blk * kBlk * p.Hs;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int e = blk * kBlk + 16 * kt + 4 * qd + r;
-        pdst[(int64_t)e * p.Hs] = __builtin_bit_cast(uint16_t, to_bf16(pv[kt][r]));
-        sdst[(int64_t)e * p.Hs] = __builtin_bit_cast(uint16_t, to_bf16(dv[kt][r]));
+        pb[st_off[kt][r]] = __builtin_bit_cast(uint16_t, to_bf16(pv[kt][r]));
+        sb[st_off[kt][r]] = __builtin_bit_cast(uint16_t, to_bf16(dv[kt][r]));
       }
     // dq^T += K^T dS^T
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
-      const uint32_t off = (ct >> 2) * kBand;
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + off + t_off[0][ct & 3]));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(base + off + t_off[1][ct & 3]));
-      const v8bf a = __builtin_bit_cast(v8bf, (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      dqa[ct] = mfma_bf16_16x16x32(a, bop, dqa[ct]);
+      if (ct + kPf < kCt) tb[(ct + kPf) % (kPf + 1)] = rd_t(ct + kPf);
+      dqa[ct] = mfma_bf16_16x16x32(tb[ct % (kPf + 1)], bop, dqa[ct]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
