@@ -174,7 +174,7 @@ dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, 
  *   dq[t,h] = sum_s dS kv[s]
  *   dkv[s]  = sum over (t, h) selecting s of  dS q[t,h] + P dout[t,h] (dims < D_v)
  *   q [T, H, D_qk] bf16, kv [N, D_qk] bf16, idx [T, k] int32 (entries < 0 or
- *   >= N skip; a row may list an index at most once), out [T, H, D_v] fp32 and
+ *   >= N skip; an index listed twice counts twice, as in the forward), out [T, H, D_v] fp32 and
  *   lse [T, H] fp32 as dsa_sparse_mla_fwd wrote them for the same inputs,
  *   dout [T, H, D_v] bf16 the upstream gradient.
  *   dq [T, H, D_qk] fp32 out (overwritten); dkv [N, D_qk] fp32 out (zeroed,

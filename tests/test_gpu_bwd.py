@@ -97,7 +97,8 @@ def _rand_idx(rng, T, k, n):
                                      (5, 2048, 128, 4096)])
 def test_sparse_mla_bwd_against_oracle(dsa, T, k, H, N):
     """Several 32-entry blocks with a ragged tail, padded rows, an all-padding
-    row, an out-of-range entry, head counts below 128 (padded heads)."""
+    row, an out-of-range entry, a repeated index, head counts below 128
+    (padded heads)."""
     _case(f"sparse_mla_bwd T={T} k={k} H={H} N={N}")
     wl = configs.Workload(**{**configs.WORKLOADS["prefill_L32k"].__dict__, "H": H, "N": N})
     rng = np.random.default_rng(T * 31 + k + H)
@@ -107,6 +108,8 @@ def test_sparse_mla_bwd_against_oracle(dsa, T, k, H, N):
     idx = _rand_idx(rng, T, k, N)
     idx[0, :] = -1          # no valid entry: dq = 0, nothing scattered
     idx[1, -1] = N + 5      # out-of-range entries are skipped
+    if T > 2 and k >= 3:
+        idx[2, 1:3] = idx[2, 0]  # a repeated index counts once per occurrence, as in the forward
     dq, dkv = _bwd_on_gpu(dsa, q, kv, idx, dO, T, N, H, k, wl.scale)
     rdq, mq, rdkv, mk = _oracle(q, lambda sel: kv[sel], idx, dO, N, wl.scale)
     assert np.all(dq[0] == 0.0)
