@@ -214,29 +214,38 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
     }
   };
 
+  // Key order.  Row m of a 16-key tile of S^T holds key 16kt + kperm(m):
+  // the groups of four rows are placed in the order 0, 3, 1, 2.  With it the
+  // lanes that the LDS serves together (for the 16-byte key-tile reads and
+  // the 8-byte transposed reads, whether it serves 8 or 16 of the first and
+  // 16 or 32 of the second per cycle) reach distinct banks under the stage
+  // swizzle; in plain order the transposed reads of rows r and r+4 collide.
+  auto kperm = [](int m) { return (m & 3) | (((0x2130 >> (4 * (m >> 2))) & 0xF) << 2); };
+
   // Operand offsets.  Key tile kt, k-step ks (A of S^T and dP^T): lane (row
-  // 16kt + hn, qd) reads chunk 4ks + qd = band ks/2, slot (4(ks%2) + qd) ^
-  // swz(row).
+  // hn, qd) reads key 16kt + kperm(hn), chunk 4ks + qd = band ks/2, slot
+  // (4(ks%2) + qd) ^ swz(key).
   uint32_t k_off[2][2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      const int r = 16 * kt + hn;
+      const int r = 16 * kt + kperm(hn);
       k_off[kt][par] = (uint32_t)(r * 128 + (((4 * par + qd) ^ swz(r)) << 4));
     }
   // K^T tile ct (A of dq^T): the B operand dS^T of lane (head, qd) holds, at
-  // k-slot 8qd + i, key 4qd + i (i < 4, tile 0) or 16 + 4qd + i - 4 (tile 1),
-  // i.e. its own accumulator values.  ds_read_b64_tr_b16 gives lane i of a
-  // 16-lane group column i of the 4 x 16 block whose rows lane 4*rho + c
-  // addresses at columns 4c .. 4c+3, so group qd reads rows (keys) 4qd + rho
-  // (and 16 + 4qd + rho) at dims 16ct + 4c: chunk 2ct + c/2, byte 8(c%2).
+  // k-slot 8qd + i, accumulator row 4qd + i of tile 0 (i < 4) or 4qd + i - 4
+  // of tile 1, i.e. its own accumulator values.  ds_read_b64_tr_b16 gives
+  // lane i of a 16-lane group column i of the 4 x 16 block whose rows lane
+  // 4*rho + c addresses at columns 4c .. 4c+3, so group qd reads keys
+  // kperm(4qd + rho) (and 16 + kperm(4qd + rho)) at dims 16ct + 4c: chunk
+  // 2ct + c/2, byte 8(c%2).
   uint32_t t_off[2][4];
   {
     const int rho = hn >> 2, c = hn & 3;
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
-      const int r = 16 * hi + 4 * qd + rho;
+      const int r = 16 * hi + kperm(4 * qd + rho);
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4)
         t_off[hi][c4] = (uint32_t)(r * 128 + (((2 * c4 + (c >> 1)) ^ swz(r)) << 4) + 8 * (c & 1));
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st_off[kt][r] = (uint32_t)((16 * kt + 4 * qd + r) * p.Hs + head);
+    for (int r = 0; r < 4; ++r) st_off[kt][r] = (uint32_t)((16 * kt + kperm(4 * qd + r)) * p.Hs + head);
 
   // Wait for this wave's DMA of block blk.  Vector memory operations retire
   // in issue order; after that DMA each earlier step issued its 16 P / dS
@@ -312,13 +321,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
     v8bf tb[kPf + 1];
 #pragma unroll
     for (int i = 0; i < kPf; ++i) tb[i] = rd_t(i);
-    // P and dS; lane holds keys 16kt + 4qd + r of its head
+    // P and dS; lane holds keys 16kt + kperm(4qd + r) of its head
     float pv[2][4], dv[2][4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int e = blk * kBlk + 16 * kt + 4 * qd + r;
+        const int e = blk * kBlk + 16 * kt + kperm(4 * qd + r);
         const bool valid = hv && rows[e] >= 0;
         const float pr = valid ? __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], p.scale_log2, -lse_l2)) : 0.f;
         pv[kt][r] = pr;
