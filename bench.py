@@ -67,9 +67,9 @@ COUNTER_TRAFFIC = {
     ("paged_prefill_b4_ctx32k_q8k", "topk"): ("4c830aaaf7a45691", ('topk.hip', 'common.h'), 1024.61e6),
     ("prefill_L32k", "indexer_kl"): ("beab70a6d015ce4e", ('indexer_kl.hip', 'common.h'), 6101.45e6),
     ("prefill_L32k", "dense_kl"): ("beab70a6d015ce4e", ('indexer_kl.hip', 'common.h'), 105785.78e6),
-    ("prefill_L32k", "mla_bwd_dq"): ("e5f27a614ab54893", ('sparse_mla_bwd.hip', 'common.h'), 5635e6),
-    ("prefill_L32k", "mla_bwd_dkv"): ("e5f27a614ab54893", ('sparse_mla_bwd.hip', 'common.h'), 12732e6),
-    ("prefill_L32k", "mla_bwd_reduce"): ("e5f27a614ab54893", ('sparse_mla_bwd.hip', 'common.h'), 9691e6),
+    ("prefill_L32k", "mla_bwd_dq"): ("2346475007df154d", ('sparse_mla_bwd.hip', 'common.h'), 5635e6),
+    ("prefill_L32k", "mla_bwd_dkv"): ("2346475007df154d", ('sparse_mla_bwd.hip', 'common.h'), 12732e6),
+    ("prefill_L32k", "mla_bwd_reduce"): ("2346475007df154d", ('sparse_mla_bwd.hip', 'common.h'), 9691e6),
 }
 
 

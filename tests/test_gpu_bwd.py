@@ -117,6 +117,24 @@ def test_sparse_mla_bwd_against_oracle(dsa, T, k, H, N):
     _check(dkv, rdkv, mk, "dkv")
 
 
+def test_sparse_mla_bwd_several_query_tiles(dsa):
+    """4100 queries: the call works through query tiles of 2048 (the last one
+    ragged), so dq is written per tile and dkv sums contributions across
+    tiles; every element is compared."""
+    T, k, H, N = 4100, 40, 8, 300
+    _case(f"sparse_mla_bwd T={T} k={k} H={H} N={N} (three query tiles)")
+    wl = configs.Workload(**{**configs.WORKLOADS["tiny_prefill_L256"].__dict__, "H": H, "N": N})
+    rng = np.random.default_rng(4100)
+    q = configs.q_bf16(wl, np.arange(T))
+    kv = configs.kv_bf16(wl, 0, np.arange(N))
+    dO = gen.f32_to_bf16_bits(rng.standard_normal((T, H, 512)).astype(np.float32))
+    idx = _rand_idx(rng, T, k, N)
+    dq, dkv = _bwd_on_gpu(dsa, q, kv, idx, dO, T, N, H, k, wl.scale)
+    rdq, mq, rdkv, mk = _oracle(q, lambda sel: kv[sel], idx, dO, N, wl.scale)
+    _check(dq, rdq, mq, "dq")
+    _check(dkv, rdkv, mk, "dkv")
+
+
 def test_sparse_mla_bwd_full_size_sampled_rows(dsa):
     """The 32K-token workload's shapes (N = 32768 cached rows, k = 2048, 128
     heads) in the launch configuration of a full run, on 12 seeded-random query
