@@ -68,7 +68,7 @@ COUNTER_TRAFFIC = {
     ("prefill_L32k", "indexer_kl"): ("beab70a6d015ce4e", ('indexer_kl.hip', 'common.h'), 6101.45e6),
     ("prefill_L32k", "dense_kl"): ("beab70a6d015ce4e", ('indexer_kl.hip', 'common.h'), 105785.78e6),
     ("prefill_L32k", "mla_bwd_dq"): ("2346475007df154d", ('sparse_mla_bwd.hip', 'common.h'), 5635e6),
-    ("prefill_L32k", "mla_bwd_dkv"): ("2346475007df154d", ('sparse_mla_bwd.hip', 'common.h'), 12732e6),
+    ("prefill_L32k", "mla_bwd_dkv"): ("2346475007df154d", ('sparse_mla_bwd.hip', 'common.h'), 12730e6),
     ("prefill_L32k", "mla_bwd_reduce"): ("2346475007df154d", ('sparse_mla_bwd.hip', 'common.h'), 9691e6),
 }
 
