@@ -41,6 +41,29 @@ def prefill_job(args):
     return oracle.prefill_row(wl, int(t), keys)
 
 
+def indexer_row_job(args):
+    """args = (prefill workload name, row t) -> the oracle's index scores of row t
+    over keys 0..t (float64 [t + 1])."""
+    import oracle
+    from dsa_inputs import configs
+    name, t = args
+    wl = _workload(name, None)
+    keys = _prefill_keys(wl, t + 1)
+    return oracle.indexer_row(configs.q_idx_bytes(wl, [t])[0], configs.w_f32(wl, [t])[0], keys[: t + 1])
+
+
+def decode_indexer_row_job(args):
+    """args = (decode workload name, sequence b) -> the oracle's index scores of
+    the decode query of sequence b over its ctx_len[b] keys."""
+    import oracle
+    from dsa_inputs import configs
+    name, b = args
+    wl = _workload(name, None)
+    n = int(configs.ctx_lens(wl)[b])
+    keys = configs.k_idx_bytes(wl, int(b), np.arange(n))
+    return oracle.indexer_row(configs.q_idx_bytes(wl, [b])[0], configs.w_f32(wl, [b])[0], keys)
+
+
 def decode_job(args):
     """args = (workload name, sequence b, k or None) -> oracle chain dict."""
     import oracle

@@ -40,16 +40,51 @@ def test_tiny_prefill_exact(dsa, k):
             check_attention(g_out[t], g_lse[t], o_d, l_d)
 
 
-def _check_rows(name, rows, results, g_idx, g_out, g_lse, k):
+def _check_rows(name, rows, results, g_idx, g_out, g_lse, k, attn_on):
+    """Selection rule per row; attention against the oracle's chain when the sets
+    are equal, else against the oracle's attention on the GPU's own index set
+    (attn_on(i, idx) -> (out, lse)), with every attention rule in both cases."""
     swapped = 0
     for i, r in enumerate(results):
         d = check_selection(g_idx[i], r["idx"], r["scores"], k, exact=False)
         swapped += d > 0
-        # rows whose selection differs only by near-ties: the outputs still
-        # obey the absolute rules; the relative-RMS rule is for equal sets
-        check_attention(g_out[i], g_lse[i], r["out"], r["lse"], rel_rms=None if d else 1e-2)
+        if d:
+            o_out, o_lse = attn_on(i, g_idx[i])
+            check_attention(g_out[i], g_lse[i], o_out, o_lse)
+        else:
+            check_attention(g_out[i], g_lse[i], r["out"], r["lse"])
     print(f"[{name}] {len(rows)} rows checked, {swapped} with near-tie swaps", flush=True)
     assert swapped <= max(2, len(rows) // 20)
+
+
+def _attn_on(wl, q_rows, seqs):
+    """Oracle attention of query row i (generator row q_rows[i], sequence
+    seqs[i]) over a given index set (-1 entries dropped)."""
+    def f(i, idx):
+        sel = idx[idx >= 0]
+        return oracle.sparse_mla_row(configs.q_bf16(wl, [int(q_rows[i])])[0],
+                                     configs.kv_bf16(wl, int(seqs[i]), sel), wl.scale, wl.D_v)
+    return f
+
+
+def _stage_isolation(name, g_idx, score_rows, ns, k):
+    """The oracle's top-k run on the GPU's own fp32 score rows reproduces the
+    fused call's selection bit for bit."""
+    for i in range(len(g_idx)):
+        o = oracle.topk_row(score_rows[i, : ns[i]].astype(np.float64), k)
+        assert np.array_equal(g_idx[i], o), f"{name}: row {i}: selection differs from top-k of its own GPU scores"
+    print(f"[{name}] stage isolation: {len(g_idx)} rows bit-exact", flush=True)
+
+
+def _decode_score_rows(dsa, wl, q_idx, w, k_pool, n_pages, page_table, ctx):
+    """The GPU's own score rows of a decode batch (dsa_indexer_scores_paged)."""
+    B, max_pages = page_table.shape
+    max_ctx = int(ctx.max().item())
+    scores = torch.empty((B, max_ctx), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores_paged(q_idx, w, k_pool, n_pages, page_table, max_pages, ctx, wl.page, B, wl.H_I,
+                                 wl.d_I, max_ctx, scores, max_ctx)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy()
 
 
 def test_decode_b64_ctx32k(dsa):
@@ -58,11 +93,18 @@ def test_decode_b64_ctx32k(dsa):
     inp = device.make_decode_inputs(wl)
     idx, out, lse = decode(wl, inp)
     g_idx, g_out, g_lse = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    # the GPU's own score rows: the contiguous keys as a pool through an identity page table
+    _case("decode B=64: GPU score rows for stage isolation")
+    B, N, pages = wl.B, wl.N, wl.N // wl.page
+    pt = torch.arange(B * pages, dtype=torch.int32, device="cuda").view(B, pages)
+    srows = _decode_score_rows(dsa, wl, inp["q_idx"], inp["w"], inp["k_idx"].view(B * pages, wl.page, wl.d_I),
+                               B * pages, pt, inp["ctx_len"])
     del inp, idx, out, lse
     _free()
+    _stage_isolation(wl.name, g_idx, srows, configs.ctx_lens(wl), wl.k)
     rows = list(range(wl.B))
     results = jobs.run(jobs.decode_job, [(wl.name, b, None) for b in rows])
-    _check_rows(wl.name, rows, results, g_idx, g_out, g_lse, wl.k)
+    _check_rows(wl.name, rows, results, g_idx, g_out, g_lse, wl.k, _attn_on(wl, rows, rows))
 
 
 def test_paged_decode_b32(dsa):
@@ -71,14 +113,18 @@ def test_paged_decode_b32(dsa):
     inp = device.make_paged_inputs(wl)
     idx, out, lse = paged_decode(wl, inp)
     g_idx, g_out, g_lse = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    _case("paged decode B=32: GPU score rows for stage isolation")
+    srows = _decode_score_rows(dsa, wl, inp["q_idx"], inp["w"], inp["k_pool"], inp["n_pages"], inp["page_table"],
+                               inp["ctx_len"])
     del inp, idx, out, lse
     _free()
+    _stage_isolation(wl.name, g_idx, srows, configs.ctx_lens(wl), wl.k)
     rows = list(range(wl.B))
     results = jobs.run(jobs.decode_job, [(wl.name, b, None) for b in rows])
-    _check_rows(wl.name, rows, results, g_idx, g_out, g_lse, wl.k)
+    _check_rows(wl.name, rows, results, g_idx, g_out, g_lse, wl.k, _attn_on(wl, rows, rows))
 
 
-def _prefill_sampled(name, rows):
+def _prefill_sampled(dsa, name, rows):
     wl = configs.WORKLOADS[name]
     _case(f"forward_prefill {name} T={wl.T}")
     inp = device.make_prefill_inputs(wl)
@@ -87,24 +133,37 @@ def _prefill_sampled(name, rows):
     g_idx = idx[ridx].cpu().numpy()
     g_out = out[ridx].cpu().numpy()
     g_lse = lse[ridx].cpu().numpy()
-    del inp, idx, out, lse
+    del idx, out, lse
+    # the GPU's own fp32 score rows of the sampled rows (one dsa_indexer_scores call each)
+    _case(f"{name}: GPU score rows of {len(rows)} sampled rows for stage isolation")
+    N = wl.N
+    scores = torch.empty((len(rows), N), dtype=torch.float32, device="cuda")
+    for i, t in enumerate(rows):
+        t = int(t)
+        dsa.dsa_indexer_scores(inp["q_idx"][t:t + 1], inp["w"][t:t + 1], inp["k_idx"], 1, N, wl.H_I, wl.d_I, t,
+                               scores[i:i + 1], N)
+    torch.cuda.synchronize()
+    srows = scores.cpu().numpy()
+    del inp, scores
     _free()
+    _stage_isolation(name, g_idx, srows, np.minimum(np.asarray(rows) + 1, N), wl.k)
+    del srows
     results = jobs.run(jobs.prefill_job, [(wl.name, int(t), None) for t in rows])
-    _check_rows(name, rows, results, g_idx, g_out, g_lse, wl.k)
+    _check_rows(name, rows, results, g_idx, g_out, g_lse, wl.k, _attn_on(wl, rows, np.zeros(len(rows), int)))
 
 
 def test_prefill_32k_sampled(dsa):
     wl = configs.WORKLOADS["prefill_L32k"]
     rows = np.unique(np.concatenate([configs.sample_rows(wl, wl.oracle_rows), np.arange(64),
                                      np.arange(wl.T - 64, wl.T), [2046, 2047, 2048, 2049]]))
-    _prefill_sampled(wl.name, rows)
+    _prefill_sampled(dsa, wl.name, rows)
 
 
 def test_prefill_128k_sampled(dsa):
     wl = configs.WORKLOADS["prefill_L128k"]
     rows = np.unique(np.concatenate([configs.sample_rows(wl, wl.oracle_rows), np.arange(8), [2047, 2048],
                                      [wl.T - 1]]))
-    _prefill_sampled(wl.name, rows)
+    _prefill_sampled(dsa, wl.name, rows)
 
 
 def test_decode_heavy_ties_and_mixed_lengths(dsa):
@@ -212,7 +271,8 @@ def test_paged_prefill_mixed(dsa):
     ends = np.concatenate([q_start[:-1], q_start[1:] - 1])
     rows = np.unique(np.concatenate([configs.sample_rows(wl, wl.oracle_rows), ends]))
     results = jobs.run(jobs.paged_prefill_job, [(wl.name, int(seq[r]), int(pos[r]), None) for r in rows])
-    _check_rows(wl.name, rows, results, g_idx[rows], g_out[rows], g_lse[rows], wl.k)
+    _check_rows(wl.name, rows, results, g_idx[rows], g_out[rows], g_lse[rows], wl.k,
+                _attn_on(wl, seq[rows] * wl.S + pos[rows], seq[rows]))
 
 
 def test_paged_prefill_empty_chunk_and_page_multiple(dsa):

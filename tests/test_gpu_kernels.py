@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import jobs
 from dsa_inputs import configs, device, gen
 from dsa_run import check_attention, check_scores, ws_tensor
 
@@ -130,6 +131,60 @@ def test_indexer_paged(dsa):
         o = oracle.indexer_row(configs.q_idx_bytes(wl, [b])[0], configs.w_f32(wl, [b])[0], keys)
         check_scores(s[b, : ctx[b]], o)
         assert np.all(np.isneginf(s[b, ctx[b]: max_ctx]))
+
+
+def test_indexer_full_rows_128k(dsa):
+    """The last 8 rows of the 128K prefill (q_pos0 = 131064) over all 131072
+    keys: every one of the 16 key chunks, every candidate within 1e-5 |o| + 1e-6."""
+    wl = configs.WORKLOADS["prefill_L128k"]
+    T, N = 8, wl.N
+    q_pos0 = N - T
+    _case(f"indexer full rows q_pos0={q_pos0} T={T} N={N}")
+    rows = torch.arange(q_pos0, q_pos0 + T, dtype=torch.int64, device="cuda")
+    q_idx = torch.empty((T, wl.H_I, wl.d_I), dtype=torch.uint8, device="cuda")
+    w = torch.empty((T, wl.H_I), dtype=torch.float32, device="cuda")
+    k_idx = torch.empty((N, wl.d_I), dtype=torch.uint8, device="cuda")
+    device.fill(q_idx, T, wl.H_I * wl.d_I, device.E4M3_NORMAL, wl.seed, gen.STREAM_Q_IDX, rowmap=rows)
+    device.fill(w, T, wl.H_I, device.F32_UNIFORM, wl.seed, gen.STREAM_W, rowmap=rows)
+    device.fill(k_idx, N, wl.d_I, device.E4M3_NORMAL, wl.seed, gen.STREAM_K_IDX)
+    scores = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores(q_idx, w, k_idx, T, N, wl.H_I, wl.d_I, q_pos0, scores, N)
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()
+    ref = jobs.run(jobs.indexer_row_job, [(wl.name, q_pos0 + i) for i in range(T)])
+    for i in range(T):
+        n = q_pos0 + i + 1
+        assert ref[i].shape[0] == n
+        check_scores(s[i, :n], ref[i])
+        assert np.all(np.isneginf(s[i, n:]))
+
+
+def test_indexer_paged_identity_table_decode_rows(dsa):
+    """The contiguous 64 x 32K decode keys addressed as a paged pool through an
+    identity page table (sequence b's page p is pool page 512 b + p): whole
+    score rows of three sequences within 1e-5 |o| + 1e-6 of the oracle."""
+    wl = configs.WORKLOADS["decode_b64_ctx32k"]
+    B, N = wl.B, wl.N
+    _case(f"indexer paged identity table B={B} N={N}")
+    q_idx = torch.empty((B, wl.H_I, wl.d_I), dtype=torch.uint8, device="cuda")
+    w = torch.empty((B, wl.H_I), dtype=torch.float32, device="cuda")
+    k_idx = torch.empty((B, N, wl.d_I), dtype=torch.uint8, device="cuda")
+    device.fill(q_idx, B, wl.H_I * wl.d_I, device.E4M3_NORMAL, wl.seed, gen.STREAM_Q_IDX)
+    device.fill(w, B, wl.H_I, device.F32_UNIFORM, wl.seed, gen.STREAM_W)
+    device.fill(k_idx, B * N, wl.d_I, device.E4M3_NORMAL, wl.seed, gen.STREAM_K_IDX)
+    pages = N // wl.page
+    pt = torch.arange(B * pages, dtype=torch.int32, device="cuda").view(B, pages)
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    scores = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores_paged(q_idx, w, k_idx.view(B * pages, wl.page, wl.d_I), B * pages, pt, pages, ctx,
+                                 wl.page, B, wl.H_I, wl.d_I, N, scores, N)
+    torch.cuda.synchronize()
+    seqs = [0, 37, B - 1]
+    s = scores[seqs].cpu().numpy()
+    ref = jobs.run(jobs.decode_indexer_row_job, [(wl.name, b) for b in seqs])
+    for i in range(len(seqs)):
+        assert ref[i].shape[0] == N
+        check_scores(s[i], ref[i])
 
 
 # ------------------------------------------------------------------ top-k

@@ -451,3 +451,53 @@ def test_sparse_mla_bwd_magnitudes_bound_values():
     dq, dkv, mq, mk = oracle.sparse_mla_bwd_row(q, kv, dO, 0.25, magnitudes=True)
     assert np.all(np.abs(dq) <= mq * (1 + 1e-12)) and np.all(np.abs(dkv) <= mk * (1 + 1e-12))
     assert mq.max() > 0 and mk.max() > 0
+
+
+def test_sparse_mla_bwd_magnitude_scale_hand_values():
+    """The magnitude scale that sets the backward's per-element tolerance, at a
+    hand-computed case (pinned from both sides, so a scale that is too large
+    fails as well as one that is too small).  H = 1, two rows, D_qk = 2, D_v = 1,
+    scale 1/2: q = (1, 0), kv = (1, 2) and (1, -4), dO = (2).  Both logits are
+    1/2, so P = (1/2, 1/2); A(s) = |dO|.|kv_s[:1]| = 2 for both rows and
+    sum_s P A = 2, so each row's |dP - D| stand-in is P (A + sum P A) = 2.
+    mag_dq[c] = sum_s scale * 2 * |kv_s,c| = (1 + 1, 2 + 4) = (2, 6);
+    mag_dkv[s] = scale * 2 * |q| + P |dO| on the value dim = (1 + 1, 0) = (2, 0).
+    The gradient itself: dP = 2 = D for both rows, so dq = 0 and each row
+    gets P dO = 1 on its value dim."""
+    q = _bf16_bits(np.array([[1.0, 0.0]]))
+    kv = _bf16_bits(np.array([[1.0, 2.0], [1.0, -4.0]]))
+    dO = _bf16_bits(np.array([[2.0]]))
+    dq, dkv, mq, mk = oracle.sparse_mla_bwd_row(q, kv, dO, 0.5, magnitudes=True)
+    np.testing.assert_allclose(mq, [[2.0, 6.0]], rtol=1e-15)
+    np.testing.assert_allclose(mk, [[2.0, 0.0], [2.0, 0.0]], rtol=1e-15)
+    np.testing.assert_allclose(dq, [[0.0, 0.0]], atol=1e-15)
+    np.testing.assert_allclose(dkv, [[1.0, 0.0], [1.0, 0.0]], rtol=1e-15, atol=1e-15)
+    # one row: P = 1, A = sum P A = |dO| |kv[:1]| = 2 * 3 = 6, stand-in 12;
+    # mag_dq = scale * 12 * |kv| = (18, 3), mag_dkv = scale * 12 * |q| + (2, 0) = (8, 0)
+    kv1 = _bf16_bits(np.array([[-3.0, 0.5]]))
+    dq, dkv, mq, mk = oracle.sparse_mla_bwd_row(q, kv1, dO, 0.5, magnitudes=True)
+    np.testing.assert_allclose(mq, [[18.0, 3.0]], rtol=1e-15)
+    np.testing.assert_allclose(mk, [[8.0, 0.0]], rtol=1e-15)
+
+
+@pytest.mark.parametrize("kind", ["decode", "paged_decode"])
+def test_decode_row_candidates_are_the_whole_context(kind):
+    """A decode query sits at position ctx_len - 1 and its own key is already in
+    the cache, so it has exactly ctx_len candidates, 0 .. ctx_len - 1.  With
+    k >= ctx_len the oracle therefore selects every one of them (its own
+    position included) and pads the rest; with k = ctx_len - 1 it drops exactly
+    one candidate, the lowest-scoring one (lowest position among equals)."""
+    if kind == "decode":
+        wl = configs.Workload("pin_decode", "decode", 2, B=3, N=37, H_I=4, H=8, k=40)
+    else:
+        wl = configs.Workload("pin_paged", "paged_decode", 5, B=3, N=128, H_I=4, H=8, k=200, ctx_lo=20, ctx_hi=70)
+    ctx = configs.ctx_lens(wl)
+    for b in range(wl.B):
+        n = int(ctx[b])
+        r = oracle.decode_row(wl, b)
+        assert r["scores"].shape == (n,)
+        assert np.array_equal(r["idx"][:n], np.arange(n)) and np.all(r["idx"][n:] == -1)
+        r1 = oracle.decode_row(wl, b, k=n - 1)
+        s = r["scores"]
+        drop = int(np.flatnonzero(s == s.min())[-1])  # ties keep the lowest positions
+        assert np.array_equal(r1["idx"], np.delete(np.arange(n), drop))
