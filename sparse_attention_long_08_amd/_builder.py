@@ -21,10 +21,12 @@ HIPCC_FLAGS = [
 
 # Per-source extra flags: VGPR-form MFMAs.  The attention kernel keeps its
 # logit accumulators in VGPRs so that its 256 output accumulators alone fill
-# the accumulation registers; the indexer's epilogue reads every accumulator
-# with VALU instructions, which cannot read accumulation registers directly.
+# the accumulation registers; the indexer's epilogue (also run by the fused
+# prefill's top-k when it rescores keys) reads every accumulator with VALU
+# instructions, which cannot read accumulation registers directly.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-SOURCE_FLAGS = {"sparse_mla.hip": _VGPR_FORM, "indexer.hip": _VGPR_FORM, "indexer_kl.hip": _VGPR_FORM}
+SOURCE_FLAGS = {"sparse_mla.hip": _VGPR_FORM, "indexer.hip": _VGPR_FORM, "indexer_kl.hip": _VGPR_FORM,
+                "topk.hip": _VGPR_FORM}
 
 
 def _run(cmd):

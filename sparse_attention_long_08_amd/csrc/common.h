@@ -13,13 +13,17 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef short v2s __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-// D = A(16x128 fp8 e4m3) * B(128x16 fp8 e4m3) + C, fp32 accumulate, unit scales.
-// Lane l supplies A row (l % 16) / B column (l % 16), 32 consecutive k values
-// starting at 32 * (l / 16) (the same k set for A and B, so the contraction
-// covers all 128 k).  C/D: lane l holds column l % 16, rows 4*(l/16) + i.
+// D = A(16x128 fp8 e4m3) * B(128x16 fp8 e4m3) + C, unit scales.  Lane l
+// supplies A row (l % 16) / B column (l % 16), 32 consecutive k values starting
+// at 32 * (l / 16) (the same k set for A and B, so the contraction covers all
+// 128 k).  C/D: lane l holds column l % 16, rows 4*(l/16) + i.  The sums are
+// not fp32-accurate: products are truncated in groups of 8 k (see the FP8
+// scoring pass in indexer.hip).
 __device__ __forceinline__ v4f mfma_f8_16x16x128(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }

@@ -444,11 +444,40 @@ dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, 
 }
 
 // ------------------------------------------------------------------ fused prefill
+// Workspace of the fused prefill: the score tile, the selection (when the
+// caller passes no idx), the FP8 scoring pass's bound inputs (per key, two
+// globals, per row) and the attention's split partials.
+namespace {
+struct PrefillWs {
+  size_t scores, idx, key_s, glob, row_fac, row_eps, row_flag, mla, total;
+};
+PrefillWs prefill_ws(int64_t T, int64_t N, int32_t H, int32_t k) {
+  PrefillWs w{};
+  size_t o = 0;
+  w.scores = o;
+  o += round_up(sizeof(float) * (size_t)prefill_tile_rows(T, N) * score_ld(N));
+  w.idx = o;
+  o += round_up(sizeof(int32_t) * (size_t)T * k);
+  w.key_s = o;
+  o += round_up(sizeof(float) * (size_t)N);
+  w.glob = o;
+  o += round_up(2 * sizeof(uint32_t));
+  w.row_fac = o;
+  o += round_up(sizeof(float) * (size_t)T);
+  w.row_eps = o;
+  o += round_up(sizeof(float) * (size_t)T);
+  w.row_flag = o;
+  o += round_up(sizeof(int32_t) * (size_t)T);
+  w.mla = o;
+  o += mla_ws(T, H, k);
+  w.total = o;
+  return w;
+}
+}  // namespace
+
 size_t dsa_forward_prefill_workspace_bytes(int64_t T, int64_t N, int32_t H, int32_t /*D_v*/, int32_t k) {
   if (T <= 0 || N <= 0 || k <= 0) return 0;
-  const int64_t rows = prefill_tile_rows(T, N);
-  return round_up(sizeof(float) * (size_t)rows * score_ld(N)) + round_up(sizeof(int32_t) * (size_t)T * k) +
-         mla_ws(T, H, k);
+  return prefill_ws(T, N, H, k).total;
 }
 
 dsa_status dsa_forward_prefill_plan(int64_t T, int64_t N, int64_t* tile_rows, int64_t* score_ld_out) {
@@ -483,32 +512,45 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
   hipStream_t st = (hipStream_t)stream;
   const int64_t rows = prefill_tile_rows(T, N);
   const int64_t ld = score_ld(N);
-  char* p = (char*)ws;
-  float* scores = (float*)p;
-  p += round_up(sizeof(float) * (size_t)rows * ld);
-  int32_t* idx_ws = (int32_t*)p;
-  p += round_up(sizeof(int32_t) * (size_t)T * k);
-  int32_t* sel = idx ? idx : idx_ws;
+  const PrefillWs wl = prefill_ws(T, N, H, k);
+  char* base = (char*)ws;
+  float* scores = (float*)(base + wl.scores);
+  int32_t* sel = idx ? idx : (int32_t*)(base + wl.idx);
+  float* key_s = (float*)(base + wl.key_s);
+  uint32_t* glob = (uint32_t*)(base + wl.glob);
+  float* row_fac = (float*)(base + wl.row_fac);
+  float* row_eps = (float*)(base + wl.row_eps);
+  int32_t* row_flag = (int32_t*)(base + wl.row_flag);
+  // Per row tile: the FP8 scoring pass, then the band top-k, which rescores
+  // the keys near each row's threshold exactly (the selection is that of the
+  // exact scores).  The bound inputs are computed once, with the first tile.
   for (int64_t r0 = 0; r0 < T; r0 += rows) {
     const int64_t tr = std::min(rows, T - r0);
     if (dsa_status s = hip_check(timed(DSA_KERNEL_INDEXER, st,
                                        [&] {
-                                         return dsa::launch_indexer_prefill(q_idx + r0 * H_I * 128, w + r0 * H_I,
-                                                                            k_idx, tr, N, H_I, q_pos0 + r0, scores,
-                                                                            ld, false, nullptr, st);
+                                         if (r0 == 0) {
+                                           hipError_t e = dsa::launch_fp8_bounds(q_idx, w, k_idx, T, N, H_I, key_s,
+                                                                                 glob, row_fac, row_eps, row_flag, st);
+                                           if (e != hipSuccess) return e;
+                                         }
+                                         return dsa::launch_indexer_fp8_prefill(q_idx + r0 * H_I * 128, w + r0 * H_I,
+                                                                                k_idx, tr, N, H_I, q_pos0 + r0, scores,
+                                                                                ld, st);
                                        }),
                                  "indexer launch"))
       return s;
     if (dsa_status s = hip_check(timed(DSA_KERNEL_TOPK, st,
                                        [&] {
-                                         return dsa::launch_topk(scores, ld, tr, N, q_pos0 + r0, nullptr, k,
-                                                                 sel + r0 * k, st);
+                                         return dsa::launch_topk_band(scores, ld, tr, N, q_pos0 + r0, k, sel + r0 * k,
+                                                                      q_idx + r0 * H_I * 128, w + r0 * H_I, k_idx, H_I,
+                                                                      key_s, glob, row_fac + r0, row_eps + r0,
+                                                                      row_flag + r0, st);
                                        }),
                                  "top-k launch"))
       return s;
   }
-  return run_mla(q, kv, sel, T, H, k, scale, out, lse, p, ws_bytes - (size_t)(p - (char*)ws), false, N, N,
-                 nullptr, nullptr, st);
+  return run_mla(q, kv, sel, T, H, k, scale, out, lse, base + wl.mla, ws_bytes - wl.mla, false, N, N, nullptr,
+                 nullptr, st);
 }
 
 // ------------------------------------------------------------------ dense warm-up loss

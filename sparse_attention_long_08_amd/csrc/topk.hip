@@ -25,6 +25,7 @@
 // selected position its output slot (the lowest-position ties are the first r
 // "== theta" bits), so the output is ascending with no sort.
 #include "common.h"
+#include "indexer_exact.h"
 #include "launch.h"
 
 namespace dsa {
@@ -44,7 +45,7 @@ struct TopkShared {
   uint32_t sel_bin;
   uint32_t sel_above;
   uint32_t list_n;
-  uint32_t pad;
+  uint32_t n_sure;  // band selection: keys selected on their approximate score alone
 };
 
 // Inclusive block scan of two counters (one workgroup).  Returns inclusive
@@ -314,10 +315,10 @@ __device__ __forceinline__ uint32_t select_in_list(TopkShared& sh, int nl, const
 // The sampled threshold estimate: 1/16 of the row (64-key chunks spread
 // over the whole row) is read into `sample` (at least n/4 + 240 bytes of
 // LDS) and its exact r-th largest key returned, with r chosen so that about
-// 1.37k keys of the full row are expected at or above it.  Needs a 16-byte
-// aligned row with n >= kSampleMinN.
+// target_eighths / 8 of k keys of the full row are expected at or above it.
+// Needs a 16-byte aligned row with n >= kSampleMinN.
 __device__ __forceinline__ uint32_t sample_estimate(TopkShared& sh, const float* __restrict__ row, int64_t n,
-                                                    int32_t k, uint32_t* sample) {
+                                                    int32_t k, uint32_t* sample, int32_t target_eighths = 11) {
   const int tid = threadIdx.x;
   // sampled chunk j: keys 64*(16*j + (5*j % 16)) .. +63, whole chunks inside the row
   const int64_t n_chunks = n / 64;
@@ -339,8 +340,9 @@ __device__ __forceinline__ uint32_t sample_estimate(TopkShared& sh, const float*
     }
   }
   __syncthreads();
-  // rank of the estimate within the sample: about 1.37k of the row lie above it
-  const int64_t target = (int64_t)k + (int64_t)k * 3 / 8;
+  // rank of the estimate within the sample: about target_eighths / 8 of k keys
+  // of the row lie above it (1.375 k unless the caller asks for more)
+  const int64_t target = (int64_t)k * target_eighths / 8;
   int64_t rs = (target * m + n - 1) / n;
   if (rs < 1) rs = 1;
   if (rs > m) rs = m;
@@ -687,6 +689,331 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int64_t T, int64_t 
   hipLaunchKernelGGL(topk_rows_finish_kernel, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, N,
                      n_valid, k, meta, cand_key, cand_idx, idx, n_words);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------ fused prefill: band selection
+// The fused prefill scores every causal pair with the FP8 scoring pass
+// (indexer.hip) and selects on those approximate scores I~ as follows, which
+// gives exactly the selection the exact scores I (those of
+// dsa_indexer_scores, bit for bit) give.  With |I~[s] - I[s]| <= E[s] =
+// fac S[s] + 2^-9 I~[s] + eps (the bound of the scoring pass; I~ >= 0 on
+// rows that are not flagged) and theta~ the k-th largest I~ of the row, the
+// k-th largest exact score theta lies in [L, U] = theta~ -+ H with
+// H = fac max(S) + 2^-9 theta~ + eps.  A key with I~ - E > U is above theta,
+// so it is selected whatever the ties; one with I~ + E < L is below theta and
+// is not.  Every other key (the band, a few hundred per row) is rescored with
+// the exact arithmetic, and the band's (k - #sure) largest exact scores, ties
+// to the lower position, complete the selection: every key whose exact score
+// equals theta is in the band, so the tie rule sees all of them.  Rows that
+// are flagged, or whose candidate list would overflow, are rescored whole and
+// take the plain selection.
+struct BandArgs {
+  const uint8_t* q_idx;     // the tile's query rows [T, H_I, 128]
+  const float* w;           // [T, H_I]
+  const uint8_t* k_idx;     // [N, 128]
+  int32_t H_I;
+  const float* key_s;       // [N] S of each key
+  const uint32_t* glob;     // [0]: largest S (float bits)
+  const float* row_fac;     // [T]
+  const float* row_eps;     // [T]
+  const int32_t* row_flag;  // [T] nonzero: exact route
+};
+
+// inverse of order_key
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// The k-th largest key of the row (theta) by radix refinement over the row,
+// then over the threshold bin gathered into the LDS list.
+__device__ __forceinline__ uint32_t row_theta_exact(TopkShared& sh, const float* __restrict__ row, int64_t n,
+                                                    bool vec, int32_t k) {
+  const int tid = threadIdx.x;
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu, above = 0u, in_range = (uint32_t)n;
+  int level = 0;
+  for (; level < 3; ++level) {
+    if (level > 0 && in_range <= (uint32_t)kTopkCap) break;
+    const int sh_ = level_shift(level), nb = 1 << level_bits(level);
+    for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    scan_row(row, n, vec, [&](int64_t, uint32_t key) {
+      if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key >> sh_) & (nb - 1)], 1u);
+    });
+    __syncthreads();
+    find_bin(sh, nb, above, (uint32_t)k);
+    const uint32_t bin = sh.sel_bin;
+    above = sh.sel_above;
+    in_range = sh.hist[bin];
+    const uint32_t span = (sh_ == 0) ? 0u : ((1u << sh_) - 1u);
+    lo = (lo & ~(((uint32_t)(nb - 1)) << sh_)) | (bin << sh_);
+    hi = lo | span;
+    __syncthreads();
+  }
+  if (lo == hi) return lo;
+  if (tid == 0) sh.list_n = 0;
+  __syncthreads();
+  scan_row(row, n, vec, [&](int64_t s, uint32_t key) {
+    if (key >= lo && key <= hi) {
+      const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+      sh.list_key[slot] = key;
+      sh.list_idx[slot] = (int32_t)s;
+    }
+  });
+  __syncthreads();
+  refine_list(sh, (int)sh.list_n, lo, hi, above, level, (uint32_t)k, sh.list_key);
+  return lo;
+}
+
+// Exact scores of nk keys of one query row, each wave taking 64 keys at a
+// time through the score kernels' own arithmetic (indexer_exact.h): entry e
+// is key pos(e); out(e, score) runs on the lane that holds entry e.
+template <int NT, class PosFn, class OutFn>
+__device__ __forceinline__ void rescore_exact(const uint8_t* __restrict__ q_row, const float* __restrict__ w_row,
+                                              int32_t H_I, const uint8_t* __restrict__ k_idx, int nk, PosFn pos,
+                                              OutFn out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int n_chunks = (nk + 63) / 64;
+  if (wave >= n_chunks) return;
+  Frag a[NT];
+  float wr[NT][4];
+  load_query<NT>(q_row, w_row, 0, true, H_I, col, grp, a, wr);
+  for (int ch = wave; ch < n_chunks; ch += kTopkWaves) {
+    float part[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int e = min(64 * ch + 16 * blk + col, nk - 1);
+      const v4i* p = (const v4i*)(k_idx + pos(e) * kIdxD + 32 * grp);
+      part[blk] = head_sum<NT>(a, wr, widen32(p[0], p[1]));
+    }
+    const float v = group_transpose_reduce(part[0], part[1], part[2], part[3], grp);
+    const int e = 64 * ch + lane;
+    if (e < nk) out(e, v);
+  }
+}
+
+// The band selection of one row (see above).  Returns false, having written
+// no output, when the row must take the exact route instead.
+template <int NT>
+__device__ __forceinline__ bool band_select(TopkShared& sh, const float* __restrict__ row, int64_t n, bool vec,
+                                            int32_t k, int64_t t, const BandArgs& ba, uint32_t* gt_bits,
+                                            uint32_t* eq_bits, int32_t* __restrict__ out) {
+  constexpr int kPer = (kTopkCap + kTopkThreads - 1) / kTopkThreads;  // list entries per thread
+  const int tid = threadIdx.x;
+  // theta~: from the sampled candidate list when it brackets rank k, else by
+  // radix refinement over the row
+  uint32_t th_key = 0u, t_low = 0xFFFFFFFFu;
+  bool have_list = false;
+  if (vec && n >= kSampleMinN) {
+    // 1.5 k keys expected above the estimate: the band reaches about 1.2 k
+    // to 1.3 k below the top on these workloads, so the list gathered here
+    // usually holds every band key and no second pass over the row is needed
+    const uint32_t t_est = sample_estimate(sh, row, n, k, gt_bits, 12);
+    if (tid == 0) sh.list_n = 0;
+    __syncthreads();
+    scan_row(row, n, true, [&](int64_t s, uint32_t key) {
+      if (key >= t_est) {
+        const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+        if (slot < (uint32_t)kTopkCap) {
+          sh.list_key[slot] = key;
+          sh.list_idx[slot] = (int32_t)s;
+        }
+      }
+    });
+    __syncthreads();
+    const uint32_t c = sh.list_n;
+    if (c >= (uint32_t)k && c <= (uint32_t)kTopkCap) {
+      th_key = select_in_list(sh, (int)c, sh.list_key, (uint32_t)k, 3);
+      have_list = true;
+      t_low = t_est;
+    }
+  }
+  if (!have_list) th_key = row_theta_exact(sh, row, n, vec, k);
+
+  // the bracket [L, U] of theta and the lowest approximate score a band key
+  // can have; the 2^-18 terms cover the fp32 rounding of these sums
+  const float theta = key_float(th_key);
+  const float fac = ba.row_fac[t], eps = ba.row_eps[t];
+  const float base = fmaf(fac, __uint_as_float(ba.glob[0]), eps);
+  float H = fmaf(0x1p-9f, fabsf(theta), base);
+  H += 0x1p-18f * (fabsf(theta) + H);
+  const float U = theta + H, L = theta - H;
+  const float lcut = L - base - 0x1p-8f * fabsf(L) - 0x1p-18f * (fabsf(L) + base);
+  const uint32_t key_lcut = order_key(lcut);
+
+  // candidate list: every key with I~ >= lcut
+  if (have_list && key_lcut >= t_low) {
+    const int c = (int)sh.list_n;
+    uint32_t kk[kPer];
+    int32_t ii[kPer];
+    bool keep[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + kTopkThreads * j;
+      keep[j] = false;
+      kk[j] = 0u;
+      ii[j] = 0;
+      if (i < c) {
+        kk[j] = sh.list_key[i];
+        ii[j] = sh.list_idx[i];
+        keep[j] = kk[j] >= key_lcut;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) sh.list_n = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (keep[j]) {
+        const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+        sh.list_key[slot] = kk[j];
+        sh.list_idx[slot] = ii[j];
+      }
+    __syncthreads();
+  } else {
+    if (tid == 0) sh.list_n = 0;
+    __syncthreads();
+    scan_row(row, n, vec, [&](int64_t s, uint32_t key) {
+      if (key >= key_lcut) {
+        const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+        if (slot < (uint32_t)kTopkCap) {
+          sh.list_key[slot] = key;
+          sh.list_idx[slot] = (int32_t)s;
+        }
+      }
+    });
+    __syncthreads();
+    if (sh.list_n > (uint32_t)kTopkCap) return false;  // uniform across the workgroup
+  }
+
+  // classify the list: sure keys into the "> theta" bitmap, band keys
+  // compacted into the front of the list (positions only)
+  const int nl = (int)sh.list_n;
+  const int rw = (int)((n + 31) / 32);  // bitmap words of this row
+  for (int i = tid; i < rw; i += kTopkThreads) {
+    gt_bits[i] = 0u;
+    eq_bits[i] = 0u;
+  }
+  int32_t pos[kPer];
+  int cls[kPer];  // 0 out, 1 sure, 2 band
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + kTopkThreads * j;
+    cls[j] = 0;
+    pos[j] = 0;
+    if (i < nl) {
+      const float x = key_float(sh.list_key[i]);
+      pos[j] = sh.list_idx[i];
+      float E = fmaf(fac, ba.key_s[pos[j]], fmaf(0x1p-9f, fabsf(x), eps));
+      E += 0x1p-18f * (fabsf(x) + E);
+      cls[j] = (x - E > U) ? 1 : ((x + E >= L) ? 2 : 0);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    sh.list_n = 0;
+    sh.n_sure = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (cls[j] == 1) {
+      atomicOr(&gt_bits[pos[j] >> 5], 1u << (pos[j] & 31));
+      atomicAdd(&sh.n_sure, 1u);
+    } else if (cls[j] == 2) {
+      sh.list_idx[atomicAdd(&sh.list_n, 1u)] = pos[j];
+    }
+  }
+  __syncthreads();
+  const int nb = (int)sh.list_n;
+  const uint32_t n_sure = sh.n_sure;
+  // the bound guarantees n_sure < k <= n_sure + nb; were it ever violated the
+  // row takes the exact route (uniform)
+  if (n_sure >= (uint32_t)k || (uint32_t)nb < (uint32_t)k - n_sure) return false;
+
+  // exact scores of the band keys, as order keys in the list
+  rescore_exact<NT>(ba.q_idx + t * ba.H_I * kIdxD, ba.w + t * ba.H_I, ba.H_I, ba.k_idx, nb,
+                    [&](int e) { return (int64_t)sh.list_idx[e]; },
+                    [&](int e, float v) { sh.list_key[e] = order_key(v); });
+  __syncthreads();
+  const uint32_t hi = select_in_list(sh, nb, sh.list_key, (uint32_t)k - n_sure, 3);  // theta itself
+  for (int i = tid; i < nb; i += kTopkThreads) {
+    const uint32_t key = sh.list_key[i];
+    const int32_t s = sh.list_idx[i];
+    if (key > hi)
+      atomicOr(&gt_bits[s >> 5], 1u << (s & 31));
+    else if (key == hi)
+      atomicOr(&eq_bits[s >> 5], 1u << (s & 31));
+  }
+  __syncthreads();
+  emit_selection(sh, gt_bits, eq_bits, rw, (uint32_t)k, out);
+  return true;
+}
+
+// One workgroup per row of the fused prefill's score tile (approximate
+// scores of the candidates).  Rows without a band selection are rescored in
+// place with the exact arithmetic and take the plain selection.
+template <int NT>
+__global__ __launch_bounds__(kTopkThreads) void topk_band_kernel(float* __restrict__ scores, int64_t ld, int64_t T,
+                                                                  int64_t N, int64_t q_pos0, int32_t k,
+                                                                  int32_t* __restrict__ idx, int32_t n_words,
+                                                                  BandArgs ba) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
+  uint32_t* gt_bits = reinterpret_cast<uint32_t*>(smem + sizeof(TopkShared));
+  uint32_t* eq_bits = gt_bits + n_words;
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  int64_t n = q_pos0 + t + 1;
+  n = n > N ? N : n;
+  int32_t* out = idx + t * (int64_t)k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  float* row = scores + t * ld;
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
+  if (ba.row_flag[t] == 0 && band_select<NT>(sh, row, n, vec, k, t, ba, gt_bits, eq_bits, out)) return;
+  // exact route: the whole row rescored in place, then the plain selection
+  rescore_exact<NT>(ba.q_idx + t * ba.H_I * kIdxD, ba.w + t * ba.H_I, ba.H_I, ba.k_idx, (int)n,
+                    [](int e) { return (int64_t)e; }, [&](int e, float v) { row[e] = v; });
+  __threadfence();
+  __syncthreads();
+  if (vec && n >= kSampleMinN && topk_sampled(sh, row, n, k, gt_bits, eq_bits, n_words, out)) return;
+  topk_exact_row(sh, row, n, vec, k, gt_bits, eq_bits, n_words, out);
+}
+
+namespace {
+template <int NT>
+hipError_t topk_band_nt(float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0, int32_t k, int32_t* idx,
+                        const BandArgs& ba, hipStream_t st) {
+  const int32_t n_words = (int32_t)((N + 31) / 32);
+  const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words + 256;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)topk_band_kernel<NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192 + 256));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(topk_band_kernel<NT>, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, T, N, q_pos0,
+                     k, idx, n_words, ba);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_topk_band(float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0, int32_t k,
+                            int32_t* idx, const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int32_t H_I,
+                            const float* key_s, const uint32_t* glob, const float* row_fac, const float* row_eps,
+                            const int32_t* row_flag, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  const BandArgs ba{q_idx, w, k_idx, H_I, key_s, glob, row_fac, row_eps, row_flag};
+  switch ((H_I + 15) / 16) {
+    case 1: return topk_band_nt<1>(scores, ld, T, N, q_pos0, k, idx, ba, st);
+    case 2: return topk_band_nt<2>(scores, ld, T, N, q_pos0, k, idx, ba, st);
+    case 3: return topk_band_nt<3>(scores, ld, T, N, q_pos0, k, idx, ba, st);
+    default: return topk_band_nt<4>(scores, ld, T, N, q_pos0, k, idx, ba, st);
+  }
 }
 
 }  // namespace dsa
