@@ -841,36 +841,10 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const float* __restr
   const float lcut = L - base - 0x1p-8f * fabsf(L) - 0x1p-18f * (fabsf(L) + base);
   const uint32_t key_lcut = order_key(lcut);
 
-  // candidate list: every key with I~ >= lcut
-  if (have_list && key_lcut >= t_low) {
-    const int c = (int)sh.list_n;
-    uint32_t kk[kPer];
-    int32_t ii[kPer];
-    bool keep[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = tid + kTopkThreads * j;
-      keep[j] = false;
-      kk[j] = 0u;
-      ii[j] = 0;
-      if (i < c) {
-        kk[j] = sh.list_key[i];
-        ii[j] = sh.list_idx[i];
-        keep[j] = kk[j] >= key_lcut;
-      }
-    }
-    __syncthreads();
-    if (tid == 0) sh.list_n = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (keep[j]) {
-        const uint32_t slot = atomicAdd(&sh.list_n, 1u);
-        sh.list_key[slot] = kk[j];
-        sh.list_idx[slot] = ii[j];
-      }
-    __syncthreads();
-  } else {
+  // candidate list: every key with I~ >= lcut (the sampled list already holds
+  // them when its threshold is at or below lcut; its other entries classify
+  // as out below)
+  if (!(have_list && key_lcut >= t_low)) {
     if (tid == 0) sh.list_n = 0;
     __syncthreads();
     scan_row(row, n, vec, [&](int64_t s, uint32_t key) {
@@ -887,7 +861,7 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const float* __restr
   }
 
   // classify the list: sure keys into the "> theta" bitmap, band keys
-  // compacted into the front of the list (positions only)
+  // compacted into the front of the list (positions only), the rest out
   const int nl = (int)sh.list_n;
   const int rw = (int)((n + 31) / 32);  // bitmap words of this row
   for (int i = tid; i < rw; i += kTopkThreads) {
