@@ -324,6 +324,28 @@ dsa_status dsa_forward_decode_paged(const uint8_t* q_idx, const float* w, const 
                                     int32_t* idx, float* out, float* lse, void* ws, size_t ws_bytes,
                                     dsa_stream_t stream);
 
+/* dsa_forward_decode_paged without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments (less ws and
+ * ws_bytes), validation and results, bit for bit.  Its scratch is one
+ * 96 MiB array per GPU inside the library, held by each GPU the library runs
+ * on until the process ends: a call needing more
+ * (dsa_forward_decode_paged_workspace_bytes above 100663296 bytes; 32
+ * sequences of up to 131072 tokens with H = 128 and k = 2048 need about
+ * 85 MB) returns DSA_ERR_UNSUPPORTED before any launch.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams
+ * or threads) race and give undefined results; calls ordered on one stream
+ * are safe, and no part of the array needs clearing between them.
+ */
+dsa_status dsa_forward_decode_paged_noalloc(const uint8_t* q_idx, const float* w, const uint8_t* k_pool,
+                                            const uint16_t* q, const uint16_t* kv_pool, int64_t n_pages,
+                                            const int32_t* page_table, int32_t max_pages, const int32_t* ctx_len,
+                                            int32_t page_size, int64_t B, int64_t max_ctx, int32_t H_I,
+                                            int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v, int32_t k,
+                                            float scale, int32_t* idx, float* out, float* lse,
+                                            dsa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

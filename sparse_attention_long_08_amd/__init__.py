@@ -59,6 +59,9 @@ SIGNATURES = {
     "dsa_forward_decode_paged": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32,
                                           _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                           _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "dsa_forward_decode_paged_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32,
+                                                  _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                  _c_f32, _c_p, _c_p, _c_p, _c_p]),
 }
 
 
@@ -250,3 +253,10 @@ def dsa_forward_decode_paged(q_idx, w, k_pool, q, kv_pool, n_pages, page_table, 
     _call("dsa_forward_decode_paged", _ptr(q_idx), _ptr(w), _ptr(k_pool), _ptr(q), _ptr(kv_pool), n_pages,
           _ptr(page_table), max_pages, _ptr(ctx_len), page_size, B, max_ctx, H_I, d_I, H, D_qk, D_v, k, scale,
           _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def dsa_forward_decode_paged_noalloc(q_idx, w, k_pool, q, kv_pool, n_pages, page_table, max_pages, ctx_len, page_size,
+                                     B, max_ctx, H_I, d_I, H, D_qk, D_v, k, scale, idx, out, lse, stream=None):
+    _call("dsa_forward_decode_paged_noalloc", _ptr(q_idx), _ptr(w), _ptr(k_pool), _ptr(q), _ptr(kv_pool), n_pages,
+          _ptr(page_table), max_pages, _ptr(ctx_len), page_size, B, max_ctx, H_I, d_I, H, D_qk, D_v, k, scale,
+          _ptr(idx), _ptr(out), _ptr(lse), _stream(stream))

@@ -7,6 +7,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "../../include/dsa.h"
@@ -773,12 +775,12 @@ dsa_status dsa_forward_decode(const uint8_t* q_idx, const float* w, const uint8_
                     nullptr, (hipStream_t)stream);
 }
 
-dsa_status dsa_forward_decode_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool, const uint16_t* q,
-                                    const uint16_t* kv_pool, int64_t n_pages, const int32_t* page_table,
-                                    int32_t max_pages, const int32_t* ctx_len, int32_t page_size, int64_t B,
-                                    int64_t max_ctx, int32_t H_I, int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v,
-                                    int32_t k, float scale, int32_t* idx, float* out, float* lse, void* ws,
-                                    size_t ws_bytes, dsa_stream_t stream) {
+// Validation shared by the two paged decode entry points.
+static dsa_status check_decode_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool, const uint16_t* q,
+                                     const uint16_t* kv_pool, int64_t n_pages, const int32_t* page_table,
+                                     int32_t max_pages, const int32_t* ctx_len, int32_t page_size, int64_t B,
+                                     int64_t max_ctx, int32_t H_I, int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v,
+                                     int32_t k, float scale, int32_t* idx, float* out, float* lse) {
   REQUIRE(B >= 0, DSA_ERR_INVALID_ARG, "B must be >= 0");
   REQUIRE(max_ctx <= kMaxCtx, DSA_ERR_UNSUPPORTED, "max_ctx must be <= %lld", (long long)kMaxCtx);
   if (dsa_status s = check_indexer_shape(H_I, d_I)) return s;
@@ -787,13 +789,80 @@ dsa_status dsa_forward_decode_paged(const uint8_t* q_idx, const float* w, const 
   REQUIRE_PTR(kv_pool);
   REQUIRE_AL(kv_pool);
   REQUIRE(scale > 0.f && scale < 1e30f, DSA_ERR_INVALID_ARG, "scale must be positive and finite");
-  if (B == 0) return ok();
+  if (B == 0) return DSA_OK;
   REQUIRE_PTR(q_idx); REQUIRE_PTR(w); REQUIRE_PTR(q); REQUIRE_PTR(out); REQUIRE_PTR(lse);
   REQUIRE_AL(q_idx); REQUIRE_AL(w); REQUIRE_AL(q); REQUIRE_AL(out); REQUIRE_AL(lse);
   if (idx) REQUIRE_AL(idx);
+  return DSA_OK;
+}
+
+dsa_status dsa_forward_decode_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool, const uint16_t* q,
+                                    const uint16_t* kv_pool, int64_t n_pages, const int32_t* page_table,
+                                    int32_t max_pages, const int32_t* ctx_len, int32_t page_size, int64_t B,
+                                    int64_t max_ctx, int32_t H_I, int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v,
+                                    int32_t k, float scale, int32_t* idx, float* out, float* lse, void* ws,
+                                    size_t ws_bytes, dsa_stream_t stream) {
+  if (dsa_status s = check_decode_paged(q_idx, w, k_pool, q, kv_pool, n_pages, page_table, max_pages, ctx_len,
+                                        page_size, B, max_ctx, H_I, d_I, H, D_qk, D_v, k, scale, idx, out, lse))
+    return s;
+  if (B == 0) return ok();
   dsa::PagedArgs pa{page_table, max_pages, page_size, n_pages};
   return run_decode(q_idx, w, k_pool, q, kv_pool, ctx_len, B, max_ctx, H_I, H, k, scale, idx, out, lse, ws,
                     ws_bytes, 0, &pa, (hipStream_t)stream);
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free paged decode
+// Scratch of dsa_forward_decode_paged_noalloc: one array per GPU, part of the
+// library's code object (so held by each GPU the library runs on until the
+// process ends) and shared by every call on that GPU.  In host code the
+// array's name is only a stand-in; kernels get its device address, looked up
+// once per device.
+constexpr size_t kNoallocScratchBytes = (size_t)96 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+hipError_t scratch_ptr(void** out) {
+  static std::mutex m;
+  static std::map<int, void*> by_dev;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(m);
+  const auto it = by_dev.find(dev);
+  if (it != by_dev.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  by_dev[dev] = ptr;
+  *out = ptr;
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" dsa_status dsa_forward_decode_paged_noalloc(
+    const uint8_t* q_idx, const float* w, const uint8_t* k_pool, const uint16_t* q, const uint16_t* kv_pool,
+    int64_t n_pages, const int32_t* page_table, int32_t max_pages, const int32_t* ctx_len, int32_t page_size,
+    int64_t B, int64_t max_ctx, int32_t H_I, int32_t d_I, int32_t H, int32_t D_qk, int32_t D_v, int32_t k,
+    float scale, int32_t* idx, float* out, float* lse, dsa_stream_t stream) {
+  if (dsa_status s = check_decode_paged(q_idx, w, k_pool, q, kv_pool, n_pages, page_table, max_pages, ctx_len,
+                                        page_size, B, max_ctx, H_I, d_I, H, D_qk, D_v, k, scale, idx, out, lse))
+    return s;
+  if (B == 0) return ok();
+  // the kernels write every scratch byte they later read (score rows, the
+  // selection, the top-k candidate lists with their counters, the split
+  // partials), so nothing has to be cleared between calls
+  const size_t need = decode_ws(B, max_ctx, H, k);
+  REQUIRE(need <= kNoallocScratchBytes, DSA_ERR_UNSUPPORTED,
+          "this decode needs %zu bytes of scratch, above the %zu-byte maximum of the allocation-free call", need,
+          kNoallocScratchBytes);
+  void* ptr = nullptr;
+  if (dsa_status s = hip_check(scratch_ptr(&ptr), "scratch address")) return s;
+  dsa::PagedArgs pa{page_table, max_pages, page_size, n_pages};
+  return run_decode(q_idx, w, k_pool, q, kv_pool, ctx_len, B, max_ctx, H_I, H, k, scale, idx, out, lse, ptr,
+                    kNoallocScratchBytes, 0, &pa, (hipStream_t)stream);
+}

@@ -194,3 +194,24 @@ def test_sparse_mla_bwd_workspace():
     nb = lib.dsa_sparse_mla_bwd_workspace_bytes(4, 64, 8, 16)
     st = lib.dsa_sparse_mla_bwd(*((FAKE,) * 6), 4, 64, 8, 576, 512, 16, 0.07, FAKE, FAKE, FAKE, nb - 1, 0)
     assert st == 3 and "ws_bytes" in lib.dsa_last_error_message().decode()
+
+
+def test_noalloc_decode_rejects_oversized_calls():
+    """The allocation-free paged decode validates like the workspace call, and
+    refuses (before any launch) a shape whose scratch exceeds its 96 MiB."""
+    lib = dsa.load()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, 4096, FAKE, 64, 64, 262144, 64, 128, 128, 576, 512, 2048, 0.07,
+            FAKE, FAKE, FAKE, 0]
+    need = lib.dsa_forward_decode_paged_workspace_bytes(64, 262144, 128, 512, 2048)
+    assert need > 96 << 20
+    assert lib.dsa_forward_decode_paged_noalloc(*args) == 2
+    assert "maximum" in lib.dsa_last_error_message().decode()
+    bad = list(args)
+    bad[9] = 32  # page size
+    assert lib.dsa_forward_decode_paged_noalloc(*bad) == 2
+    bad = list(args)
+    bad[2] = 0  # k_pool
+    assert lib.dsa_forward_decode_paged_noalloc(*bad) == 1
+    bad = list(args)
+    bad[10] = 0  # B = 0 is a no-op
+    assert lib.dsa_forward_decode_paged_noalloc(*bad) == 0
