@@ -64,6 +64,29 @@ def decode_indexer_row_job(args):
     return oracle.indexer_row(configs.q_idx_bytes(wl, [b])[0], configs.w_f32(wl, [b])[0], keys)
 
 
+def timed_prefill_row_job(args):
+    """args = (prefill workload name, row t) -> (n_t, seconds spent in the
+    oracle's indexer, top-k and attention for row t).  Input generation (the
+    row's query values and the selected latent rows) is outside the timing."""
+    import time
+
+    import oracle
+    from dsa_inputs import configs
+    name, t = args
+    wl = _workload(name, None)
+    keys = _prefill_keys(wl, t + 1)
+    q_i, w, q = configs.q_idx_bytes(wl, [t])[0], configs.w_f32(wl, [t])[0], configs.q_bf16(wl, [t])[0]
+    t0 = time.perf_counter()
+    scores = oracle.indexer_row(q_i, w, keys[: t + 1])
+    idx = oracle.topk_row(scores, wl.k)
+    t1 = time.perf_counter()
+    kv = oracle.gather_kv(wl, 0, idx)
+    t2 = time.perf_counter()
+    oracle.sparse_mla_row(q, kv, wl.scale, wl.D_v)
+    t3 = time.perf_counter()
+    return min(t + 1, wl.N), (t1 - t0) + (t3 - t2)
+
+
 def decode_job(args):
     """args = (workload name, sequence b, k or None) -> oracle chain dict."""
     import oracle
