@@ -17,7 +17,9 @@
  * Conventions shared by every call
  *  - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
  *    and allocates every buffer; the library never allocates device memory
- *    and keeps no per-call state.  `stream` is a hipStream_t (NULL = default).
+ *    at run time and keeps no per-call state (the one exception is the
+ *    static scratch of dsa_forward_decode_paged_noalloc, below).  `stream` is
+ *    a hipStream_t (NULL = default).
  *  - Calls are asynchronous and ordered on `stream`.  Inputs are read only;
  *    outputs are fully overwritten (including -1 / -inf padding).
  *  - Arguments are validated on the host before any launch.  On failure the
@@ -244,10 +246,18 @@ dsa_status dsa_dense_warmup_loss(const uint8_t* q_idx, const float* w, const uin
                                  size_t ws_bytes, dsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * Fused prefill of one sequence: indexer -> top-k -> sparse attention for the
- * T queries at positions q_pos0 .. q_pos0+T-1 over keys 0 .. N-1 (N >= q_pos0+T
- * is not required; candidates are capped at N).  The L x L score matrix is
- * never formed: scores live in a row-tiled part of the workspace.
+ * Fused prefill of one sequence: the whole DSA chain of [P1] -- index scores
+ * (§2.1.1 index-score equation), fine-grained top-k token selection and
+ * attention over the selected latent entries (§2.1.2), MLA in MQA mode (§2.2)
+ * -- for the T queries at positions q_pos0 .. q_pos0+T-1 over keys 0 .. N-1
+ * (N >= q_pos0+T is not required; candidates are capped at N).  The L x L
+ * score matrix is never formed: scores live in a row-tiled part of the
+ * workspace.  The selection equals dsa_indexer_scores followed by dsa_topk
+ * bit for bit: every causal pair is first scored on the FP8 matrix cores, and
+ * every key whose place relative to its row's threshold that approximate
+ * score leaves open (a bound on its error holds by construction) is rescored
+ * with the exact arithmetic of dsa_indexer_scores.  The outputs are those of
+ * dsa_sparse_mla_fwd over that selection.
  *   idx may be NULL (then kept in the workspace); otherwise [T, k] out.
  */
 size_t dsa_forward_prefill_workspace_bytes(int64_t T, int64_t N, int32_t H, int32_t D_v, int32_t k);
@@ -298,9 +308,14 @@ dsa_status dsa_forward_prefill_paged(const uint8_t* q_idx, const float* w, const
                                      int32_t* idx, float* out, float* lse, void* ws, size_t ws_bytes,
                                      dsa_stream_t stream);
 
-/* Fused decode of B sequences with contiguous caches, one query each:
+/* Fused decode of B sequences with contiguous caches, one query each: the DSA
+ * chain of [P1] §2.1.1 (index scores), §2.1.2 (top-k selection and attention
+ * over the selected entries) and §2.2 (MQA mode) for the newest token of each
+ * sequence, whose key is already in the cache:
  *   k_idx [B, N, d_I], kv [B, N, D_qk]; ctx_len [B] (device) with
- *   1 <= ctx_len[b] <= N.  Other arguments as in the calls above.
+ *   1 <= ctx_len[b] <= N.  Other arguments as in the calls above.  Scores are
+ *   exact (the arithmetic of dsa_indexer_scores_paged); each query's entries
+ *   may be split over several workgroups and merged exactly (same out/lse).
  */
 size_t dsa_forward_decode_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t D_v, int32_t k);
 dsa_status dsa_forward_decode(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, const uint16_t* q,
@@ -309,7 +324,10 @@ dsa_status dsa_forward_decode(const uint8_t* q_idx, const float* w, const uint8_
                               int32_t* idx, float* out, float* lse, void* ws, size_t ws_bytes,
                               dsa_stream_t stream);
 
-/* Fused decode of B sequences over paged caches (64-token pages):
+/* Fused decode of B sequences over paged caches (64-token pages): the chain
+ * of dsa_forward_decode ([P1] §2.1.1, §2.1.2, §2.2) with every key and latent
+ * row read through the page table (a serving layout; the pages do not fix
+ * one):
  *   k_pool [n_pages, page_size, d_I], kv_pool [n_pages, page_size, D_qk],
  *   page_table [B, max_pages], ctx_len [B] with ctx_len[b] <= max_ctx <=
  *   max_pages * page_size.  Returned indices are logical positions.
