@@ -451,7 +451,7 @@ dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, 
 // globals, per row) and the attention's split partials.
 namespace {
 struct PrefillWs {
-  size_t scores, idx, key_s, glob, row_fac, row_eps, row_flag, mla, total;
+  size_t scores, idx, key_s, glob, row_fac, row_eps, row_flag, row_scale, mla, total;
 };
 PrefillWs prefill_ws(int64_t T, int64_t N, int32_t H, int32_t k) {
   PrefillWs w{};
@@ -470,6 +470,8 @@ PrefillWs prefill_ws(int64_t T, int64_t N, int32_t H, int32_t k) {
   o += round_up(sizeof(float) * (size_t)T);
   w.row_flag = o;
   o += round_up(sizeof(int32_t) * (size_t)T);
+  w.row_scale = o;
+  o += round_up(sizeof(float) * (size_t)T);
   w.mla = o;
   o += mla_ws(T, H, k);
   w.total = o;
@@ -523,6 +525,7 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
   float* row_fac = (float*)(base + wl.row_fac);
   float* row_eps = (float*)(base + wl.row_eps);
   int32_t* row_flag = (int32_t*)(base + wl.row_flag);
+  float* row_scale = (float*)(base + wl.row_scale);
   // Per row tile: the FP8 scoring pass, then the band top-k, which rescores
   // the keys near each row's threshold exactly (the selection is that of the
   // exact scores).  The bound inputs are computed once, with the first tile.
@@ -532,12 +535,13 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
                                        [&] {
                                          if (r0 == 0) {
                                            hipError_t e = dsa::launch_fp8_bounds(q_idx, w, k_idx, T, N, H_I, key_s,
-                                                                                 glob, row_fac, row_eps, row_flag, st);
+                                                                                 glob, row_fac, row_eps, row_flag,
+                                                                                 row_scale, st);
                                            if (e != hipSuccess) return e;
                                          }
                                          return dsa::launch_indexer_fp8_prefill(q_idx + r0 * H_I * 128, w + r0 * H_I,
-                                                                                k_idx, tr, N, H_I, q_pos0 + r0, scores,
-                                                                                ld, st);
+                                                                                k_idx, tr, N, H_I, q_pos0 + r0,
+                                                                                row_scale + r0, scores, ld, st);
                                        }),
                                  "indexer launch"))
       return s;
@@ -546,7 +550,7 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
                                          return dsa::launch_topk_band(scores, ld, tr, N, q_pos0 + r0, k, sel + r0 * k,
                                                                       q_idx + r0 * H_I * 128, w + r0 * H_I, k_idx, H_I,
                                                                       key_s, glob, row_fac + r0, row_eps + r0,
-                                                                      row_flag + r0, st);
+                                                                      row_flag + r0, row_scale + r0, st);
                                        }),
                                  "top-k launch"))
       return s;

@@ -238,8 +238,10 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
 // (2^-10 + 2^-11)(1 + 2^-20) of sum_j w_j R_j, which the f16 MFMA's fp32 sums
 // keep below 2^-9 I~; the exact route's own fp32 rounding (at most 2^-18 of
 // sum_j |w_j| sum_i |q k|, and |q k| < 4 MQ MK) is below 2^-3 of the first term.  With W[g] = sum_j |w_j| MQ[j, g] and S[s] = sum_g MK[s, g]:
-//   |I~[s] - I[s]| <= fac * S[s] + 2^-9 I~[s] + eps,
+//   |I~[s] - I[s]| <= fac * S[s] + 1.0625 2^-9 I~[s] + eps,
 //   fac = 1.25 * 2^-10 * max_g W[g],  eps = the f16 underflow terms.
+// The stored score is f16(I~ * 2^-s), s chosen per row so that the row's
+// largest possible |I~| fits f16's range.
 // Rows with a negative or non-finite weight, or whose dot products could pass
 // f16's range, are flagged and take the exact route whole.
 
@@ -298,7 +300,8 @@ __global__ __launch_bounds__(256) void fp8_row_bounds_kernel(const uint8_t* __re
                                                              const float* __restrict__ w, int64_t T, int32_t H_I,
                                                              const uint32_t* __restrict__ glob,
                                                              float* __restrict__ row_fac, float* __restrict__ row_eps,
-                                                             int32_t* __restrict__ row_flag) {
+                                                             int32_t* __restrict__ row_flag,
+                                                             float* __restrict__ row_scale) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -332,6 +335,7 @@ __global__ __launch_bounds__(256) void fp8_row_bounds_kernel(const uint8_t* __re
   // f16 underflow: a weight below 2^-14 may flush to zero (error w |c|), and
   // a rectified dot product below 2^-14 likewise (error 2^-14 w)
   float eps = (aw < 0x1p-14f ? aw * cmax : 0.f) + 0x1p-14f * aw;
+  float imax = aw * cmax;  // bound on the row's |I~|
   float wmax = 0.f;
 #pragma unroll
   for (int g = 0; g < 16; ++g) {
@@ -341,18 +345,30 @@ __global__ __launch_bounds__(256) void fp8_row_bounds_kernel(const uint8_t* __re
     wmax = fmaxf(wmax, x);
   }
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) eps += __shfl_xor(eps, d, 64);
+  for (int d = 32; d >= 1; d >>= 1) {
+    eps += __shfl_xor(eps, d, 64);
+    imax += __shfl_xor(imax, d, 64);
+  }
   const bool any_bad = __any(bad);
   if (lane == 0) {
+    // the stored score is I~ * 2^-s in f16: the smallest s >= 0 that keeps the
+    // row's largest possible |I~| below 60000 after scaling; rounding it to
+    // f16 (to nearest) adds 2^-11 |I~| (in the relative term) and at most
+    // 2^(s - 25) in f16's subnormal range
+    int sc = 0;
+    const float lim = imax * (1.f + 0x1p-8f);
+    while (sc < 120 && ldexpf(lim, -sc) > 60000.f) ++sc;
+    row_scale[t] = ldexpf(1.f, sc);
     row_fac[t] = 1.25f * 0x1p-10f * wmax * (1.f + 0x1p-16f);
-    row_eps[t] = (eps + 0x1p-20f) * (1.f + 0x1p-16f);
+    row_eps[t] = (eps + ldexpf(1.f, sc - 24) + 0x1p-20f) * (1.f + 0x1p-16f);
     row_flag[t] = any_bad ? 1 : 0;
   }
 }
 
 // Approximate scores of the causal pairs of a 4-row query block (one row per
 // wave) over one chunk of `key_chunk` keys; only candidates (s <= pos) are
-// written.  64-key groups of FP8 keys are staged in LDS as stored (128-byte
+// written, as f16 I~ * 2^-s (row_scale = 2^s, rounded to nearest) in the
+// first half of each fp32 row of the tile.  64-key groups of FP8 keys are staged in LDS as stored (128-byte
 // rows whose 16-byte chunks are XOR-swizzled by key, so the operand reads of
 // 16 keys x one chunk are free of bank conflicts) and shared by the 4 rows.
 // Per 16-key block: one 16x16x128 FP8 MFMA per 16-head tile (heads on the
@@ -365,7 +381,8 @@ __global__ __launch_bounds__(256) void fp8_row_bounds_kernel(const uint8_t* __re
 template <int NT>
 __global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx, int64_t T,
-    int64_t N, int32_t H_I, int64_t q_pos0, float* __restrict__ scores, int64_t ld, int32_t key_chunk) {
+    int64_t N, int32_t H_I, int64_t q_pos0, const float* __restrict__ row_scale, float* __restrict__ scores,
+    int64_t ld, int32_t key_chunk) {
   constexpr int NS = (NT + 1) / 2;  // f16 k-steps of the head sum, two head tiles each
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][64 * kIdxD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -380,6 +397,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
   const int64_t r = r0 + wave;
   const bool valid = r < T;
   const int64_t nq = valid ? min(q_pos0 + r + 1, N) : 0;
+  const float inv_scale = valid ? 1.f / row_scale[r] : 1.f;  // a power of two: exact
 
   v8i a[NT];
 #pragma unroll
@@ -459,13 +477,16 @@ __global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
     }
     if (valid && col < 4) {
       const int64_t s = kg + 16 * col + 4 * grp;
-      float* dst = scores + r * ld + s;
+      _Float16* dst = reinterpret_cast<_Float16*>(scores + r * ld) + s;
+      const _Float16 h0 = (_Float16)(d[0] * inv_scale), h1 = (_Float16)(d[1] * inv_scale);
+      const _Float16 h2 = (_Float16)(d[2] * inv_scale), h3 = (_Float16)(d[3] * inv_scale);
       if (s + 3 < nq) {
-        *(v4f*)dst = d;
+        typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+        *(v4h*)dst = (v4h){h0, h1, h2, h3};
       } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (s + i < nq) dst[i] = d[i];
+        if (s < nq) dst[0] = h0;
+        if (s + 1 < nq) dst[1] = h1;
+        if (s + 2 < nq) dst[2] = h2;
       }
     }
     buf ^= 1;
@@ -552,7 +573,7 @@ hipError_t launch_indexer_decode(const uint8_t* q_idx, const float* w, const uin
 
 hipError_t launch_fp8_bounds(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
                              int32_t H_I, float* key_s, uint32_t* glob, float* row_fac, float* row_eps,
-                             int32_t* row_flag, hipStream_t st) {
+                             int32_t* row_flag, float* row_scale, hipStream_t st) {
   hipError_t e = launch_zero_f32(reinterpret_cast<float*>(glob), 2, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fp8_key_bounds_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, k_idx, N, key_s,
@@ -560,31 +581,32 @@ hipError_t launch_fp8_bounds(const uint8_t* q_idx, const float* w, const uint8_t
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(fp8_row_bounds_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, q_idx, w, T, H_I, glob,
-                     row_fac, row_eps, row_flag);
+                     row_fac, row_eps, row_flag, row_scale);
   return hipGetLastError();
 }
 
 namespace {
 template <int NT>
 hipError_t fp8_prefill_nt(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
-                          int32_t H_I, int64_t q_pos0, float* scores, int64_t ld, hipStream_t st) {
+                          int32_t H_I, int64_t q_pos0, const float* row_scale, float* scores, int64_t ld,
+                          hipStream_t st) {
   const int64_t n_all = std::min<int64_t>(q_pos0 + T, N);
   dim3 grid((unsigned)((T + 3) / 4), (unsigned)((n_all + kPrefillChunk - 1) / kPrefillChunk));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   hipLaunchKernelGGL((indexer_fp8_prefill_kernel<NT>), grid, dim3(256), 0, st, q_idx, w, k_idx, T, N, H_I, q_pos0,
-                     scores, ld, kPrefillChunk);
+                     row_scale, scores, ld, kPrefillChunk);
   return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_indexer_fp8_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T,
-                                      int64_t N, int32_t H_I, int64_t q_pos0, float* scores, int64_t ld,
-                                      hipStream_t st) {
+                                      int64_t N, int32_t H_I, int64_t q_pos0, const float* row_scale, float* scores,
+                                      int64_t ld, hipStream_t st) {
   switch ((H_I + 15) / 16) {
-    case 1: return fp8_prefill_nt<1>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, st);
-    case 2: return fp8_prefill_nt<2>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, st);
-    case 3: return fp8_prefill_nt<3>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, st);
-    default: return fp8_prefill_nt<4>(q_idx, w, k_idx, T, N, H_I, q_pos0, scores, ld, st);
+    case 1: return fp8_prefill_nt<1>(q_idx, w, k_idx, T, N, H_I, q_pos0, row_scale, scores, ld, st);
+    case 2: return fp8_prefill_nt<2>(q_idx, w, k_idx, T, N, H_I, q_pos0, row_scale, scores, ld, st);
+    case 3: return fp8_prefill_nt<3>(q_idx, w, k_idx, T, N, H_I, q_pos0, row_scale, scores, ld, st);
+    default: return fp8_prefill_nt<4>(q_idx, w, k_idx, T, N, H_I, q_pos0, row_scale, scores, ld, st);
   }
 }
 

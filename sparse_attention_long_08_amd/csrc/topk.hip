@@ -156,6 +156,37 @@ __device__ __forceinline__ void scan_row(const float* __restrict__ row, int64_t 
   }
 }
 
+// The fused prefill's score tile holds f16 approximate scores, each the row's
+// score times 2^-s (the row's scale is 2^s, so every score fits f16's range);
+// a key is that of the fp32 value f16 * 2^s, which is exact.
+__device__ __forceinline__ uint32_t h_key(_Float16 h, float scale) { return order_key((float)h * scale); }
+
+// scan_row over such a row (16-byte aligned): eight keys per 16-byte load,
+// four loads in flight per thread.
+template <class Fn>
+__device__ __forceinline__ void scan_row_h(const _Float16* __restrict__ row, float scale, int64_t n, Fn&& fn) {
+  const int tid = threadIdx.x;
+  constexpr int kU = 4;
+  constexpr int64_t kStep = 8 * kTopkThreads;  // keys per unrolled sub-step
+  const int64_t nU = n / (kU * kStep) * (kU * kStep);
+  for (int64_t s0 = 8 * (int64_t)tid; s0 < nU; s0 += kU * kStep) {
+    v8h v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = *(const v8h*)(row + s0 + u * kStep);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fn(s0 + u * kStep + j, h_key(v[u][j], scale));
+  }
+  const int64_t n8 = n & ~(int64_t)7;
+  for (int64_t s = nU + 8 * (int64_t)tid; s < n8; s += kStep) {
+    const v8h v = *(const v8h*)(row + s);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fn(s + j, h_key(v[j], scale));
+  }
+  for (int64_t s = n8 + tid; s < n; s += kTopkThreads) fn(s, h_key(row[s], scale));
+}
+
 // Radix levels: 0 -> key bits 31..20, 1 -> bits 19..8, 2 -> bits 7..0.
 __device__ __forceinline__ int level_shift(int level) { return level == 0 ? 20 : (level == 1 ? 8 : 0); }
 __device__ __forceinline__ int level_bits(int level) { return level == 2 ? 8 : 12; }
@@ -317,6 +348,18 @@ __device__ __forceinline__ uint32_t select_in_list(TopkShared& sh, int nl, const
 // LDS) and its exact r-th largest key returned, with r chosen so that about
 // target_eighths / 8 of k keys of the full row are expected at or above it.
 // Needs a 16-byte aligned row with n >= kSampleMinN.
+// The estimate from the m sampled keys of a row of n: the key of sample rank
+// ceil(target * m / n), target = target_eighths / 8 of k (1.375 k unless the
+// caller asks for more), so that about `target` keys of the row lie above it.
+__device__ __forceinline__ uint32_t sample_select(TopkShared& sh, int m, int64_t n, int32_t k, uint32_t* sample,
+                                                  int32_t target_eighths) {
+  const int64_t target = (int64_t)k * target_eighths / 8;
+  int64_t rs = (target * m + n - 1) / n;
+  if (rs < 1) rs = 1;
+  if (rs > m) rs = m;
+  return select_in_list(sh, m, sample, (uint32_t)rs, 2);
+}
+
 __device__ __forceinline__ uint32_t sample_estimate(TopkShared& sh, const float* __restrict__ row, int64_t n,
                                                     int32_t k, uint32_t* sample, int32_t target_eighths = 11) {
   const int tid = threadIdx.x;
@@ -340,13 +383,30 @@ __device__ __forceinline__ uint32_t sample_estimate(TopkShared& sh, const float*
     }
   }
   __syncthreads();
-  // rank of the estimate within the sample: about target_eighths / 8 of k keys
-  // of the row lie above it (1.375 k unless the caller asks for more)
-  const int64_t target = (int64_t)k * target_eighths / 8;
-  int64_t rs = (target * m + n - 1) / n;
-  if (rs < 1) rs = 1;
-  if (rs > m) rs = m;
-  return select_in_list(sh, m, sample, (uint32_t)rs, 2);
+  return sample_select(sh, m, n, k, sample, target_eighths);
+}
+
+// sample_estimate over an f16 tile row (16-byte aligned): the same chunks.
+__device__ __forceinline__ uint32_t sample_estimate_h(TopkShared& sh, const _Float16* __restrict__ row, float scale,
+                                                      int64_t n, int32_t k, uint32_t* sample, int32_t target_eighths) {
+  const int tid = threadIdx.x;
+  const int64_t n_chunks = n / 64;
+  const int m_chunks = (int)((n_chunks + kSampleStride - 1) / kSampleStride);
+  int m = 0;
+  for (int j = 0; j < m_chunks; ++j)
+    if ((int64_t)kSampleStride * j + (5 * j) % kSampleStride < n_chunks) m += 64;
+  for (int f = tid; f < m_chunks * 8; f += kTopkThreads) {
+    const int j = f >> 3;
+    const int64_t chunk = (int64_t)kSampleStride * j + (5 * j) % kSampleStride;
+    if (chunk < n_chunks) {
+      const v8h v = *(const v8h*)(row + 64 * chunk + 8 * (f & 7));
+      uint32_t* dst = sample + 64 * j + 8 * (f & 7);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i] = h_key(v[i], scale);
+    }
+  }
+  __syncthreads();
+  return sample_select(sh, m, n, k, sample, target_eighths);
 }
 
 __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float* __restrict__ row, int64_t n, int32_t k,
@@ -696,10 +756,10 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int64_t T, int64_t 
 // (indexer.hip) and selects on those approximate scores I~ as follows, which
 // gives exactly the selection the exact scores I (those of
 // dsa_indexer_scores, bit for bit) give.  With |I~[s] - I[s]| <= E[s] =
-// fac S[s] + 2^-9 I~[s] + eps (the bound of the scoring pass; I~ >= 0 on
-// rows that are not flagged) and theta~ the k-th largest I~ of the row, the
-// k-th largest exact score theta lies in [L, U] = theta~ -+ H with
-// H = fac max(S) + 2^-9 theta~ + eps.  A key with I~ - E > U is above theta,
+// fac S[s] + r I~[s] + eps (the bound of the scoring pass, r = 1.0625 2^-9;
+// I~ >= 0 on rows that are not flagged) and theta~ the k-th largest I~ of the
+// row, the k-th largest exact score theta lies in [L, U] = theta~ -+ H with
+// H = fac max(S) + r theta~ + eps.  A key with I~ - E > U is above theta,
 // so it is selected whatever the ties; one with I~ + E < L is below theta and
 // is not.  Every other key (the band, a few hundred per row) is rescored with
 // the exact arithmetic, and the band's (k - #sure) largest exact scores, ties
@@ -717,6 +777,7 @@ struct BandArgs {
   const float* row_fac;     // [T]
   const float* row_eps;     // [T]
   const int32_t* row_flag;  // [T] nonzero: exact route
+  const float* row_scale;   // [T] 2^s: the tile holds each row's scores times 2^-s, in f16
 };
 
 // inverse of order_key
@@ -724,10 +785,11 @@ __device__ __forceinline__ float key_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// The k-th largest key of the row (theta) by radix refinement over the row,
-// then over the threshold bin gathered into the LDS list.
-__device__ __forceinline__ uint32_t row_theta_exact(TopkShared& sh, const float* __restrict__ row, int64_t n,
-                                                    bool vec, int32_t k) {
+// The k-th largest key of a row (theta) by radix refinement over the row,
+// then over the threshold bin gathered into the LDS list; scan(fn) calls
+// fn(s, key) for every candidate of the row.
+template <class Scan>
+__device__ __forceinline__ uint32_t row_theta_exact(TopkShared& sh, int64_t n, int32_t k, Scan&& scan) {
   const int tid = threadIdx.x;
   uint32_t lo = 0u, hi = 0xFFFFFFFFu, above = 0u, in_range = (uint32_t)n;
   int level = 0;
@@ -736,7 +798,7 @@ __device__ __forceinline__ uint32_t row_theta_exact(TopkShared& sh, const float*
     const int sh_ = level_shift(level), nb = 1 << level_bits(level);
     for (int i = tid; i < nb; i += kTopkThreads) sh.hist[i] = 0;
     __syncthreads();
-    scan_row(row, n, vec, [&](int64_t, uint32_t key) {
+    scan([&](int64_t, uint32_t key) {
       if (key >= lo && key <= hi) atomicAdd(&sh.hist[(key >> sh_) & (nb - 1)], 1u);
     });
     __syncthreads();
@@ -752,7 +814,7 @@ __device__ __forceinline__ uint32_t row_theta_exact(TopkShared& sh, const float*
   if (lo == hi) return lo;
   if (tid == 0) sh.list_n = 0;
   __syncthreads();
-  scan_row(row, n, vec, [&](int64_t s, uint32_t key) {
+  scan([&](int64_t s, uint32_t key) {
     if (key >= lo && key <= hi) {
       const uint32_t slot = atomicAdd(&sh.list_n, 1u);
       sh.list_key[slot] = key;
@@ -792,26 +854,32 @@ __device__ __forceinline__ void rescore_exact(const uint8_t* __restrict__ q_row,
   }
 }
 
+// Relative part of the bound E (the f16 roundings of the scoring pass and of
+// the stored score).
+constexpr float kRelErr = 0x1.1p-9f;
+
 // The band selection of one row (see above).  Returns false, having written
 // no output, when the row must take the exact route instead.
 template <int NT>
-__device__ __forceinline__ bool band_select(TopkShared& sh, const float* __restrict__ row, int64_t n, bool vec,
-                                            int32_t k, int64_t t, const BandArgs& ba, uint32_t* gt_bits,
-                                            uint32_t* eq_bits, int32_t* __restrict__ out) {
+__device__ __forceinline__ bool band_select(TopkShared& sh, const _Float16* __restrict__ row, int64_t n, int32_t k,
+                                            int64_t t, const BandArgs& ba, uint32_t* gt_bits, uint32_t* eq_bits,
+                                            int32_t* __restrict__ out) {
   constexpr int kPer = (kTopkCap + kTopkThreads - 1) / kTopkThreads;  // list entries per thread
   const int tid = threadIdx.x;
   // theta~: from the sampled candidate list when it brackets rank k, else by
   // radix refinement over the row
+  const float scale = ba.row_scale[t];
+  auto scan = [&](auto&& fn) { scan_row_h(row, scale, n, fn); };
   uint32_t th_key = 0u, t_low = 0xFFFFFFFFu;
   bool have_list = false;
-  if (vec && n >= kSampleMinN) {
+  if (n >= kSampleMinN) {
     // 1.5 k keys expected above the estimate: the band reaches about 1.2 k
     // to 1.3 k below the top on these workloads, so the list gathered here
     // usually holds every band key and no second pass over the row is needed
-    const uint32_t t_est = sample_estimate(sh, row, n, k, gt_bits, 12);
+    const uint32_t t_est = sample_estimate_h(sh, row, scale, n, k, gt_bits, 12);
     if (tid == 0) sh.list_n = 0;
     __syncthreads();
-    scan_row(row, n, true, [&](int64_t s, uint32_t key) {
+    scan([&](int64_t s, uint32_t key) {
       if (key >= t_est) {
         const uint32_t slot = atomicAdd(&sh.list_n, 1u);
         if (slot < (uint32_t)kTopkCap) {
@@ -828,17 +896,17 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const float* __restr
       t_low = t_est;
     }
   }
-  if (!have_list) th_key = row_theta_exact(sh, row, n, vec, k);
+  if (!have_list) th_key = row_theta_exact(sh, n, k, scan);
 
   // the bracket [L, U] of theta and the lowest approximate score a band key
   // can have; the 2^-18 terms cover the fp32 rounding of these sums
   const float theta = key_float(th_key);
   const float fac = ba.row_fac[t], eps = ba.row_eps[t];
   const float base = fmaf(fac, __uint_as_float(ba.glob[0]), eps);
-  float H = fmaf(0x1p-9f, fabsf(theta), base);
+  float H = fmaf(kRelErr, fabsf(theta), base);
   H += 0x1p-18f * (fabsf(theta) + H);
   const float U = theta + H, L = theta - H;
-  const float lcut = L - base - 0x1p-8f * fabsf(L) - 0x1p-18f * (fabsf(L) + base);
+  const float lcut = L - base - 2.f * kRelErr * fabsf(L) - 0x1p-18f * (fabsf(L) + base);
   const uint32_t key_lcut = order_key(lcut);
 
   // candidate list: every key with I~ >= lcut (the sampled list already holds
@@ -847,7 +915,7 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const float* __restr
   if (!(have_list && key_lcut >= t_low)) {
     if (tid == 0) sh.list_n = 0;
     __syncthreads();
-    scan_row(row, n, vec, [&](int64_t s, uint32_t key) {
+    scan([&](int64_t s, uint32_t key) {
       if (key >= key_lcut) {
         const uint32_t slot = atomicAdd(&sh.list_n, 1u);
         if (slot < (uint32_t)kTopkCap) {
@@ -878,7 +946,7 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const float* __restr
     if (i < nl) {
       const float x = key_float(sh.list_key[i]);
       pos[j] = sh.list_idx[i];
-      float E = fmaf(fac, ba.key_s[pos[j]], fmaf(0x1p-9f, fabsf(x), eps));
+      float E = fmaf(fac, ba.key_s[pos[j]], fmaf(kRelErr, fabsf(x), eps));
       E += 0x1p-18f * (fabsf(x) + E);
       cls[j] = (x - E > U) ? 1 : ((x + E >= L) ? 2 : 0);
     }
@@ -925,8 +993,9 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const float* __restr
 }
 
 // One workgroup per row of the fused prefill's score tile (approximate
-// scores of the candidates).  Rows without a band selection are rescored in
-// place with the exact arithmetic and take the plain selection.
+// scores of the candidates, f16 scaled per row).  Rows without a band
+// selection are rescored in place with the exact arithmetic (as fp32, over
+// the row's full fp32 stride) and take the plain selection.
 template <int NT>
 __global__ __launch_bounds__(kTopkThreads) void topk_band_kernel(float* __restrict__ scores, int64_t ld, int64_t T,
                                                                   int64_t N, int64_t q_pos0, int32_t k,
@@ -945,16 +1014,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_band_kernel(float* __restri
     for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
     return;
   }
-  float* row = scores + t * ld;
-  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
-  if (ba.row_flag[t] == 0 && band_select<NT>(sh, row, n, vec, k, t, ba, gt_bits, eq_bits, out)) return;
-  // exact route: the whole row rescored in place, then the plain selection
+  float* row = scores + t * ld;  // 16-byte aligned (ld is a multiple of 64)
+  if (ba.row_flag[t] == 0 && band_select<NT>(sh, reinterpret_cast<const _Float16*>(row), n, k, t, ba, gt_bits,
+                                             eq_bits, out))
+    return;
+  // exact route: the whole row rescored in place as fp32, then the plain selection
   rescore_exact<NT>(ba.q_idx + t * ba.H_I * kIdxD, ba.w + t * ba.H_I, ba.H_I, ba.k_idx, (int)n,
                     [](int e) { return (int64_t)e; }, [&](int e, float v) { row[e] = v; });
   __threadfence();
   __syncthreads();
-  if (vec && n >= kSampleMinN && topk_sampled(sh, row, n, k, gt_bits, eq_bits, n_words, out)) return;
-  topk_exact_row(sh, row, n, vec, k, gt_bits, eq_bits, n_words, out);
+  if (n >= kSampleMinN && topk_sampled(sh, row, n, k, gt_bits, eq_bits, n_words, out)) return;
+  topk_exact_row(sh, row, n, true, k, gt_bits, eq_bits, n_words, out);
 }
 
 namespace {
@@ -979,9 +1049,9 @@ hipError_t topk_band_nt(float* scores, int64_t ld, int64_t T, int64_t N, int64_t
 hipError_t launch_topk_band(float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0, int32_t k,
                             int32_t* idx, const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int32_t H_I,
                             const float* key_s, const uint32_t* glob, const float* row_fac, const float* row_eps,
-                            const int32_t* row_flag, hipStream_t st) {
+                            const int32_t* row_flag, const float* row_scale, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const BandArgs ba{q_idx, w, k_idx, H_I, key_s, glob, row_fac, row_eps, row_flag};
+  const BandArgs ba{q_idx, w, k_idx, H_I, key_s, glob, row_fac, row_eps, row_flag, row_scale};
   switch ((H_I + 15) / 16) {
     case 1: return topk_band_nt<1>(scores, ld, T, N, q_pos0, k, idx, ba, st);
     case 2: return topk_band_nt<2>(scores, ld, T, N, q_pos0, k, idx, ba, st);
