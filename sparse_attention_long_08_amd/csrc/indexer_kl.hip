@@ -385,14 +385,16 @@ __global__ __launch_bounds__(kDThreads, 1) void indexer_dense_kl_kernel(DenseKlP
                                          0, 0);
     }
   };
-  // wait for this wave's DMA of block blk; one later block's DMA (10 ops for
-  // wave 0, 9 for the other gatherers) may stay in flight
+  // wait for this wave's DMA of block blk; one later block's DMA (kDmaPerWave
+  // row DMAs, plus wave 0's score DMA) may stay in flight
+  constexpr int kScoreDma = 1;
+  static_assert(kDmaPerWave + kScoreDma <= 63, "vmcnt field");
   auto wait_block = [&](int blk) {
     if (blk + 1 < nb) {
       if (wave == 0)
-        asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave + kScoreDma) : "memory");
       else
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }

@@ -47,6 +47,14 @@ constexpr int kDv = 512;
 constexpr int kBlk = 32;                    // selected rows per block
 constexpr int kStage = kBlk * kDqk * 2;     // 36864 bytes of gathered rows
 constexpr int kBand = 4096;                 // one 8-chunk band of all 32 rows
+constexpr int kDmaPerWave = kStage / kBand; // one DMA per band, eight rows per wave
+constexpr int kStoreTiles = 2;              // 16-key tiles of a block
+constexpr int kStoreRows = 4;               // accumulator rows per lane and tile
+constexpr int kStoresPerStep = 2 * kStoreTiles * kStoreRows;  // P and dS of every (tile, row)
+static_assert(kStage == kDmaPerWave * kBand, "a stage is whole bands");
+static_assert(kStoreTiles * 16 == kBlk, "a block is two 16-key tiles");
+// vmcnt is a 6-bit field: the deepest wait below must fit it
+static_assert(kDmaPerWave + 2 * kStoresPerStep + kDmaPerWave <= 63, "vmcnt field");
 constexpr int kThreads = 256;               // 4 waves
 constexpr int kMaxK = 4096;
 constexpr int kQSteps = kDqk / 32;          // 18 k-steps of the logit product
@@ -202,13 +210,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
     if constexpr (kBufDma) {
       const uint32_t voff = (uint32_t)row * (kDqk * 2) + 16 * g_chunk;
 #pragma unroll
-      for (int bd = 0; bd < 9; ++bd)
+      for (int bd = 0; bd < kDmaPerWave; ++bd)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (lds_ptr)(base + bd * kBand + wave * 1024), 16,
                                                  voff + 128 * bd, 0, 0, 0);
     } else {
       const uint16_t* src = p.kv + ((uint64_t)(uint32_t)row * kDqk + 8 * g_chunk);
 #pragma unroll
-      for (int bd = 0; bd < 9; ++bd)
+      for (int bd = 0; bd < kDmaPerWave; ++bd)
         __builtin_amdgcn_global_load_lds((const void*)(src + 64 * bd), (lds_ptr)(base + bd * kBand + wave * 1024),
                                          16, 0, 0);
     }
@@ -266,18 +274,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
     for (int r = 0; r < 4; ++r) st_off[kt][r] = (uint32_t)((16 * kt + kperm(4 * qd + r)) * p.Hs + head);
 
   // Wait for this wave's DMA of block blk.  Vector memory operations retire
-  // in issue order; after that DMA each earlier step issued its 16 P / dS
-  // stores and the DMA two blocks ahead of it (9 operations).
+  // in issue order, so what was issued after that DMA may stay in flight:
+  // for block 0 the prologue's DMA of block 1; for block 1 step 0's DMA of
+  // block 2 and its stores; for later blocks the stores of steps blk-2 and
+  // blk-1 and step blk-1's DMA of block blk+1 (each DMA only if that block
+  // exists).
+  constexpr int kW0 = kDmaPerWave;                       // step 0, block 1 in flight
+  constexpr int kW1 = kStoresPerStep + kDmaPerWave;      // step 1, block 2 in flight
+  constexpr int kW2 = 2 * kStoresPerStep + kDmaPerWave;  // later steps, block blk+1 in flight
   auto wait_block = [&](int blk) {
     if (blk == 0) {
-      if (nb > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      if (nb > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW0) : "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else if (blk == 1) {
-      if (nb > 2) asm volatile("s_waitcnt vmcnt(25)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      if (nb > 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW1) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStoresPerStep) : "memory");
     } else {
-      if (blk + 1 < nb) asm volatile("s_waitcnt vmcnt(41)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+      if (blk + 1 < nb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kW2) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kStoresPerStep) : "memory");
     }
     __builtin_amdgcn_s_barrier();
   };
@@ -335,15 +349,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_dq_kernel(BwdParams p) {
       }
     const v8bf bop = (v8bf){to_bf16(dv[0][0]), to_bf16(dv[0][1]), to_bf16(dv[0][2]), to_bf16(dv[0][3]),
                             to_bf16(dv[1][0]), to_bf16(dv[1][1]), to_bf16(dv[1][2]), to_bf16(dv[1][3])};
-    // 16 stores per lane and block, issued by every wave (a wave of padding
+    // kStoresPerStep stores per lane and block, issued by every wave (a wave of padding
     // heads writes the zeros of its own padding slots), so the wait counts
     // above are exact; entries k .. kp-1 are padding rows
     uint16_t* const pb = pdst + (int64_t)blk * kBlk * p.Hs;
     uint16_t* const sb = sdst + (int64_t)blk * kBlk * p.Hs;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < kStoreTiles; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < kStoreRows; ++r) {
         pb[st_off[kt][r]] = __builtin_bit_cast(uint16_t, to_bf16(pv[kt][r]));
         sb[st_off[kt][r]] = __builtin_bit_cast(uint16_t, to_bf16(dv[kt][r]));
       }
