@@ -16,9 +16,11 @@ CPU oracle's rate on a bounded sample of the same workload.
 Other modes (not the headline line):
   --workload decode_b64_ctx32k | paged_decode_b32_ctx4k_128k
       one step = one fused decode call (indexer -> top-k -> split attention ->
-      combine) for the whole batch, timed in the same two phases; the staged
-      check replays it through the paged entry points (the contiguous cache is
-      addressed through an identity page table for it).
+      combine) for the whole batch, timed in the same two phases, then K
+      replays of a HIP graph captured from one fused call (no host launch gaps;
+      each replay's outputs must equal the eager call's; --no-graph skips it);
+      the staged check replays it through the paged entry points (the
+      contiguous cache is addressed through an identity page table for it).
   --workload paged_prefill_b4_ctx32k_q8k
       one step = one chunked prefill call into a paged cache (4 sequences of
       32K tokens, the last 8K of each new).
@@ -154,6 +156,7 @@ def main():
     ap.add_argument("--fused-only", action="store_true",
                     help="run only the fused calls (both timing phases): no staged-replay check and no CPU "
                          "baseline, so that a profiler sees the product path alone")
+    ap.add_argument("--no-graph", action="store_true", help="decode: skip the HIP graph replay timing")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--dense-kl", action="store_true",
                     help="time the dense warm-up indexer KL loss (prefill_L32k unless --workload names another "
@@ -242,6 +245,44 @@ def launch_times(dsa, torch, stream, fused, steps: int):
     rec = dsa.dsa_timing_end()
     print(f"[bench] {steps} fused steps with launch events done", file=sys.stderr, flush=True)
     return rec, e0.elapsed_time(e1) / steps
+
+
+def decode_graph_times(torch, stream, fused, outs, steps: int):
+    """Captures one fused decode call into a HIP graph and times `steps`
+    replays on `stream` (the decode path records no memset nodes).  Every
+    replay's outputs must equal the eager call's: one replay is checked before
+    the timed ones, the last timed one after them, with eager work in
+    between."""
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fused()
+    checks = []
+
+    def scribble():  # so that the next call must rewrite every output
+        for t in outs:
+            t.fill_(-7)
+
+    def check():
+        torch.cuda.synchronize()
+        checks.append(all(bool(torch.equal(a, b)) for a, b in zip(outs, ref)))
+
+    scribble()
+    g.replay()
+    check()
+    scribble()
+    fused()  # eager work between replays
+    check()
+    scribble()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    check()
+    print(f"[bench] {steps} HIP graph replays done", file=sys.stderr, flush=True)
+    return {"ms_per_step": e0.elapsed_time(e1) / steps, "replays_equal_eager": all(checks)}
 
 
 def bench_prefill(args, wl):
@@ -900,6 +941,7 @@ def bench_decode(args, wl):
     rec_t, ev_ms_per_step = launch_times(dsa, torch, stream, fused, args.steps)
     stage_ms = {"indexer": rec_t["indexer"][0] / args.steps, "topk": rec_t["topk"][0] / args.steps,
                 "sparse_mla": rec_t["attention"][0] / args.steps}
+    graph = decode_graph_times(torch, stream, fused, (idx, out, lse), args.steps) if not args.no_graph else None
 
     # the same step through the single-stage paged calls (untimed) must give the same bits
     same = None
@@ -929,6 +971,7 @@ def bench_decode(args, wl):
         "ms_per_step": ms_per_step,
         "host_wall_ms_per_step": wall_ms,
         "ms_per_step_with_launch_events": ev_ms_per_step,
+        "hip_graph": graph,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -60,10 +60,15 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f c) {
 // group_row(b, g): row of token g of a 64-aligned group g .. g+63 whose tokens
 // sit in consecutive rows (true for every layout here, pages being 64 tokens),
 // or -1 when the group has no backing rows.
+// Two-phase form of row(): lookup(b, s) issues the layout's loads with no
+// branch (indexes clamped into range, valid for any s), row_of(b, s, look)
+// finishes; several lookups can then be in flight together.
 struct AddrSingle {  // one contiguous sequence of n rows
   int64_t n;
   __device__ __forceinline__ int64_t row(int64_t /*b*/, int64_t s) const { return (s >= 0 && s < n) ? s : -1; }
   __device__ __forceinline__ int64_t group_row(int64_t b, int64_t g) const { return row(b, g); }
+  __device__ __forceinline__ int32_t lookup(int64_t, int64_t) const { return 0; }
+  __device__ __forceinline__ int64_t row_of(int64_t b, int64_t s, int32_t) const { return row(b, s); }
 };
 struct AddrBatched {  // [B, stride] contiguous sequences
   int64_t stride;
@@ -71,6 +76,8 @@ struct AddrBatched {  // [B, stride] contiguous sequences
     return (s >= 0 && s < stride) ? b * stride + s : -1;
   }
   __device__ __forceinline__ int64_t group_row(int64_t b, int64_t g) const { return row(b, g); }
+  __device__ __forceinline__ int32_t lookup(int64_t, int64_t) const { return 0; }
+  __device__ __forceinline__ int64_t row_of(int64_t b, int64_t s, int32_t) const { return row(b, s); }
 };
 struct AddrPaged {  // pool of pages addressed through a page table
   const int32_t* page_table;
@@ -86,6 +93,14 @@ struct AddrPaged {  // pool of pages addressed through a page table
     return ((int64_t)p << page_shift) + (s & ((1 << page_shift) - 1));
   }
   __device__ __forceinline__ int64_t group_row(int64_t b, int64_t g) const { return row(b, g); }
+  __device__ __forceinline__ int32_t lookup(int64_t b, int64_t s) const {
+    const int64_t lp = s < 0 ? 0 : min(s >> page_shift, (int64_t)max_pages - 1);
+    return page_table[b * max_pages + lp];
+  }
+  __device__ __forceinline__ int64_t row_of(int64_t /*b*/, int64_t s, int32_t p) const {
+    if (s < 0 || (s >> page_shift) >= max_pages || p < 0 || p >= n_pages) return -1;
+    return ((int64_t)p << page_shift) + (s & ((1 << page_shift) - 1));
+  }
 };
 
 // ------------------------------------------------------------------ top-k keys

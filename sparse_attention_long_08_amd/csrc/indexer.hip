@@ -155,16 +155,22 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
   if (c0 >= c_end) return;
   int64_t n = ctx_len[b];
   n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
+  if (c0 >= n) {  // the whole chunk lies past the context: only the -inf fill
+    for (int64_t s = c0 + tid; s < c_end; s += 256) scores[b * ld + s] = -INFINITY;
+    return;
+  }
 
   Frag a[NT];
   float wr[NT][4];
   load_query<NT>(q_idx, w, b, true, H_I, col, grp, a, wr);
 
-  // groups of this wave: kg(i) = c0 + 64*wave + 256*i.  Lane i resolves the
-  // row of group i up front (one page lookup per 64-key group, which always
-  // lies in one page), so no key load waits on a lookup.
+  // groups of this wave: kg(i) = c0 + 64*wave + 256*i, the first nv of them
+  // holding keys of the context.  Lane i resolves the row of group i up
+  // front (one page lookup per 64-key group, which always lies in one page),
+  // so no key load waits on a lookup.
   const int64_t kg0 = c0 + 64 * wave;
   const int ng = kg0 < c_end ? (int)((c_end - kg0 + 255) / 256) : 0;
+  const int nv = kg0 < n ? min(ng, (int)((n - kg0 + 255) / 256)) : 0;
   auto kg_of = [&](int i) { return kg0 + 256 * (int64_t)i; };
   int64_t my_base = -1;
   if (lane < ng && kg_of(lane) < n) my_base = addr.group_row(b, kg_of(lane));
@@ -199,17 +205,21 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(const uint8_t* __re
 
   // keys of the next two groups in flight while one group is on the matrix cores
   v4i ra[4][2], rb[4][2], rc[4][2];
-  if (ng > 0) load(0, ra);
-  if (ng > 1) load(1, rb);
-  for (int i = 0; i < ng; i += 3) {
-    if (i + 2 < ng) load(i + 2, rc);
+  if (nv > 0) load(0, ra);
+  if (nv > 1) load(1, rb);
+  for (int i = 0; i < nv; i += 3) {
+    if (i + 2 < nv) load(i + 2, rc);
     finish(i, ra);
-    if (i + 1 >= ng) break;
-    if (i + 3 < ng) load(i + 3, ra);
+    if (i + 1 >= nv) break;
+    if (i + 3 < nv) load(i + 3, ra);
     finish(i + 1, rb);
-    if (i + 2 >= ng) break;
-    if (i + 4 < ng) load(i + 4, rb);
+    if (i + 2 >= nv) break;
+    if (i + 4 < nv) load(i + 4, rb);
     finish(i + 2, rc);
+  }
+  for (int i = nv; i < ng; ++i) {  // groups past the context
+    const int64_t s = kg_of(i) + lane;
+    if (s < c_end) scores[b * ld + s] = -INFINITY;
   }
 }
 

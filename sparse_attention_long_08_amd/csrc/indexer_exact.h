@@ -60,25 +60,35 @@ __device__ __forceinline__ Frag widen32(v4i lo, v4i hi) {
   return f;
 }
 
+// Query row r (its H_I heads and weights) in the A layout of head_sum; heads
+// past H_I, and every head when !valid, are zero.  All loads are issued
+// unconditionally -- an invalid row reads row 0 (valid memory whenever a
+// kernel runs) and a padding head reads head H_I-1 -- and zeroed by selects,
+// so the NT query tiles and the weights are in flight together: one memory
+// round trip rather than one per tile.
 template <int NT>
 __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx, const float* __restrict__ w,
                                            int64_t r, bool valid, int32_t H_I, int col, int grp, Frag (&a)[NT],
                                            float (&wr)[NT][4]) {
+  const int64_t rr = valid ? r : 0;
+  v4i lo[NT], hi[NT];
+  float wv[NT][4];
 #pragma unroll
   for (int tl = 0; tl < NT; ++tl) {
-    const int head = 16 * tl + col;
-    if (valid && head < H_I) {
-      const v4i* p = (const v4i*)(q_idx + ((r * H_I + head) * kIdxD + 32 * grp));
-      a[tl] = widen32(p[0], p[1]);
-    } else {
+    const int head = min(16 * tl + col, H_I - 1);
+    const v4i* p = (const v4i*)(q_idx + ((rr * H_I + head) * kIdxD + 32 * grp));
+    lo[tl] = p[0];
+    hi[tl] = p[1];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) a[tl].s[st] = (v8bf){};
-    }
+    for (int i = 0; i < 4; ++i) wv[tl][i] = w[rr * H_I + min(16 * tl + 4 * grp + i, H_I - 1)];
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hw = 16 * tl + 4 * grp + i;
-      wr[tl][i] = (valid && hw < H_I) ? 0.5f * w[r * H_I + hw] : 0.f;
-    }
+  for (int tl = 0; tl < NT; ++tl) {
+    const bool hv = valid && 16 * tl + col < H_I;
+    const v4i z = {0, 0, 0, 0};
+    a[tl] = widen32(hv ? lo[tl] : z, hv ? hi[tl] : z);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wr[tl][i] = (valid && 16 * tl + 4 * grp + i < H_I) ? 0.5f * wv[tl][i] : 0.f;
   }
 }
 

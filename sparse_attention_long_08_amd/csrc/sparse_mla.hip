@@ -193,36 +193,51 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   const int n_ent = j1 > j0 ? j1 - j0 : 0;
   const int nb = (n_ent + kBlk - 1) / kBlk;
 
-  // ---- resolve every entry to a latent row once (index and page-table
-  // loads happen here only, so the block loop issues no other memory reads)
-  for (int e = tid; e < nb * kBlk; e += kThreads) {
-    int32_t row = -1;
-    if (e < n_ent) {
-      const int32_t s = idx_row[j0 + e];
-      if (s >= 0 && s < n_b) row = (int32_t)addr.row(b, s);
-    }
-    rows[e] = row;
-  }
-
   // ---- query rows of this wave's heads in the B layout of the logit
   // MFMA: k-step ks of lane (head hn, half hh) is dims 16*ks + 8*hh .. +7.
-  // Lanes past the last head read head H-1 and zero it.
+  // Lanes past the last head read head H-1 and zero it.  Issued first, so
+  // that they are in flight while the entries resolve.
   v8bf qf[kQReg];
+  v8bf qt[kQTail];
+  const bool q_hv = kHeadsPerWave * wave + hn < p.H;
   {
-    const int head = kHeadsPerWave * wave + hn;
-    const bool hv = head < p.H;
-    const uint16_t* qrow = p.q + (t * p.H + (hv ? head : p.H - 1)) * (int64_t)kDqk + 8 * hh;
+    const uint16_t* qrow =
+        p.q + (t * p.H + (q_hv ? kHeadsPerWave * wave + hn : p.H - 1)) * (int64_t)kDqk + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < kQReg; ++ks) {
+    for (int ks = 0; ks < kKSteps; ++ks) {
       const v8bf v = *(const v8bf*)(qrow + 16 * ks);
-      qf[ks] = hv ? v : (v8bf){};
-    }
-#pragma unroll
-    for (int ks = kQReg; ks < kKSteps; ++ks) {
-      const v8bf v = *(const v8bf*)(qrow + 16 * ks);
-      qtail[((ks - kQReg) * kWaves + wave) * 64 + lane] = hv ? v : (v8bf){};
+      if (ks < kQReg)
+        qf[ks < kQReg ? ks : 0] = v;
+      else
+        qt[ks < kQReg ? 0 : ks - kQReg] = v;
     }
   }
+
+  // ---- resolve every entry to a latent row once (index and page-table
+  // loads happen here only, so the block loop issues no other memory
+  // reads).  Four entries per thread at a time: their index loads, then
+  // their page-table loads, each issued together.
+  constexpr int kResolve = 4;
+  for (int e0 = 0; e0 < nb * kBlk; e0 += kResolve * kThreads) {
+    int32_t sv[kResolve], pe[kResolve];
+#pragma unroll
+    for (int u = 0; u < kResolve; ++u) sv[u] = idx_row[j0 + min(e0 + u * kThreads + tid, n_ent - 1)];
+#pragma unroll
+    for (int u = 0; u < kResolve; ++u) {
+      const int e = e0 + u * kThreads + tid;
+      sv[u] = (e < n_ent && sv[u] >= 0 && sv[u] < n_b) ? sv[u] : -1;
+      pe[u] = addr.lookup(b, sv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kResolve; ++u) {
+      const int e = e0 + u * kThreads + tid;
+      if (e < nb * kBlk) rows[e] = sv[u] < 0 ? -1 : (int32_t)addr.row_of(b, sv[u], pe[u]);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < kQReg; ++ks) qf[ks] = q_hv ? qf[ks] : (v8bf){};
+#pragma unroll
+  for (int ks = 0; ks < kQTail; ++ks) qtail[(ks * kWaves + wave) * 64 + lane] = q_hv ? qt[ks] : (v8bf){};
   __syncthreads();
 
   // Gather one block into stage `base`: this wave moves rows 8w .. 8w+7, one
