@@ -62,8 +62,9 @@ typedef void* dsa_stream_t; /* hipStream_t */
 
 /* Version of this ABI (bumped on any signature change). */
 int32_t dsa_abi_version(void);
-/* Static description of a status code. */
-const char* dsa_status_string(dsa_status s);
+/* Static description of a status code: any integer is accepted, codes that
+ * are not a dsa_status give "unknown status". */
+const char* dsa_status_string(int32_t status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char* dsa_last_error_message(void);
 

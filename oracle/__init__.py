@@ -16,7 +16,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dsa_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# DSA_ORACLE_LIB selects another build of the oracle (e.g. a sanitizer build), used as it is
+_LIB_OVERRIDE = os.environ.get("DSA_ORACLE_LIB")
+_LIB = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
@@ -26,19 +28,21 @@ _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 
 
-def build() -> str:
-    """Compile the oracle with gcc (no fast-math, so double arithmetic is IEEE)."""
-    tmp = _LIB + ".tmp"
-    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-fno-fast-math", _SRC, "-o", tmp, "-lm"],
+def build(out: str | None = None, extra=()) -> str:
+    """Compile the oracle with gcc (no fast-math, so double arithmetic is IEEE)
+    into `out` (default: the in-tree library)."""
+    out = out or os.path.join(_HERE, "liboracle.so")
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-fno-fast-math", *extra, _SRC, "-o", tmp, "-lm"],
                    check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _LIB_OVERRIDE and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
         lib = ctypes.CDLL(_LIB)
         lib.oracle_e4m3_to_double.restype = ctypes.c_double

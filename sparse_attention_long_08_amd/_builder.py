@@ -37,7 +37,8 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), out: str | None = None, link_extra=()) -> str:
+    """Compiles every source and links libdsa.so into `out` (default: in-tree)."""
     import concurrent.futures
     import tempfile
     inc = ["-I", os.path.join(ROOT, "include")]
@@ -51,14 +52,15 @@ def build(verbose: bool = False, extra=()) -> str:
                          os.path.join(CSRC, src), "-o", obj])
         with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
             results = list(ex.map(_run, cmds))
-        tmp = LIB + ".tmp"
-        link = ["hipcc", "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp]
+        out = out or LIB
+        tmp = out + ".tmp"
+        link = ["hipcc", "--offload-arch=gfx950", "-fPIC", "-shared", *link_extra, *objs, "-o", tmp]
         results.append(_run(link))
     if verbose:
         for r in results:
             sys.stderr.write(r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

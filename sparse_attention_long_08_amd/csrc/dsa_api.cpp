@@ -137,10 +137,10 @@ int64_t score_ld(int64_t N) { return (N + 63) / 64 * 64; }
 
 extern "C" {
 
-int32_t dsa_abi_version(void) { return 1; }
+int32_t dsa_abi_version(void) { return 2; }
 
-const char* dsa_status_string(dsa_status s) {
-  switch (s) {
+const char* dsa_status_string(int32_t status) {
+  switch (status) {
     case DSA_OK: return "ok";
     case DSA_ERR_INVALID_ARG: return "invalid argument";
     case DSA_ERR_UNSUPPORTED: return "unsupported shape";

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = dsa.load()
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
     for s in range(5):
         assert lib.dsa_status_string(s)
     assert lib.dsa_status_string(99) == b"unknown status"
