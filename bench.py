@@ -54,9 +54,16 @@ PEAK_HBM_GBS = 8000.0
 # on; once one changes, the figure no longer describes the kernel and the roofline reports
 # traffic as null.
 COUNTER_TRAFFIC = {
-    ("prefill_L128k", "indexer"): ("f549e4e43a2a7f63", ('indexer.hip', 'indexer_exact.h', 'common.h'), 785.5e6),
-    ("prefill_L128k", "topk"): ("2fea2f937c93bd32", ('topk.hip', 'indexer_exact.h', 'common.h'), 797.4e6),
-    ("prefill_L128k", "sparse_mla"): ("d70d6bbba063ac08", ('sparse_mla.hip', 'common.h'), 222216.9e6),
+    ("prefill_L128k", "indexer"): ("a2dfea7dbf9d26e9", ('indexer.hip', 'indexer_exact.h', 'common.h'), 492.1e6),
+    ("prefill_L128k", "topk"): ("704189eb74e2fe09", ('topk.hip', 'indexer_exact.h', 'common.h'), 492.7e6),
+    ("prefill_L128k", "sparse_mla"): ("6496f7e28980a049", ('sparse_mla.hip', 'common.h'), 218227.5e6),
+    ("decode_b64_ctx32k", "indexer"): ("a2dfea7dbf9d26e9", ('indexer.hip', 'indexer_exact.h', 'common.h'), 281.4e6),
+    ("decode_b64_ctx32k", "topk"): ("704189eb74e2fe09", ('topk.hip', 'indexer_exact.h', 'common.h'), 9.2e6),
+    ("decode_b64_ctx32k", "sparse_mla"): ("6496f7e28980a049", ('sparse_mla.hip', 'common.h'), 355.9e6),
+    ("paged_decode_b32_ctx4k_128k", "indexer"): ("a2dfea7dbf9d26e9", ('indexer.hip', 'indexer_exact.h', 'common.h'),
+                                                 278.3e6),
+    ("paged_decode_b32_ctx4k_128k", "topk"): ("704189eb74e2fe09", ('topk.hip', 'indexer_exact.h', 'common.h'), 10.7e6),
+    ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("6496f7e28980a049", ('sparse_mla.hip', 'common.h'), 172.9e6),
 }
 
 

@@ -508,7 +508,10 @@ namespace {
 constexpr int kPrefillNW = 4;
 constexpr int kPrefillQW = 1;
 constexpr int kPrefillChunk = 8192;
-constexpr int kDecodeChunk = 4096;  // keys per decode workgroup: 16 groups of 64 per wave
+// keys per decode workgroup (8 groups of 64 per wave): measured on MI355X, 2048 balances
+// ragged contexts (32 sequences of 5.8K..127K keys: 77 us against 90 us with 4096) at
+// about the same time for uniform ones (64 x 32K: 66 us against 64 us)
+constexpr int kDecodeChunk = 2048;
 
 template <int NT, class Addr>
 hipError_t prefill_nt(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, Addr addr, int64_t T, int64_t N,

@@ -536,10 +536,16 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   if (threadIdx.x == 0) lse[th] = lse_tot;
 }
 
+// Each split keeps at least kMinSplitKeys entries: a split's fixed cost (query
+// load, entry resolution, partial write and merge) outweighs further
+// parallelism below that (measured on MI355X, 32 queries x 2048 entries:
+// attention + combine 58 us with 4 splits against 62 us with 8).
+constexpr int kMinSplitKeys = 512;
+
 int32_t sparse_mla_splits(int64_t T, int32_t /*H*/, int32_t k) {
   if (T >= 256) return 1;
   int64_t s = (256 + T - 1) / T;
-  const int64_t max_s = (k + kBlk - 1) / kBlk;
+  const int64_t max_s = k / kMinSplitKeys;
   if (s > max_s) s = max_s;
   if (s > 16) s = 16;
   return (int32_t)(s < 1 ? 1 : s);
