@@ -120,7 +120,8 @@ dsa_status check_paged(const void* pool, int64_t n_pages, const int32_t* page_ta
 size_t mla_ws(int64_t T, int32_t H, int32_t k) {
   const int32_t s = dsa::sparse_mla_splits(T, H, k);
   if (s <= 1) return 0;
-  return round_up(sizeof(float) * (size_t)T * s * H * 512) + round_up(sizeof(float) * (size_t)T * s * H);
+  // f16 partial outputs, fp32 lse and scale per (query, split, head)
+  return round_up(sizeof(uint16_t) * (size_t)T * s * H * 512) + 2 * round_up(sizeof(float) * (size_t)T * s * H);
 }
 
 int64_t prefill_tile_rows(int64_t T, int64_t N) {
@@ -274,8 +275,12 @@ static dsa_status run_mla(const uint16_t* q, const uint16_t* kv, const int32_t* 
   a.paged = paged;
   a.n_split = dsa::sparse_mla_splits(T, H, k);
   if (a.n_split > 1) {
-    a.part_o = (float*)ws;
-    a.part_lse = (float*)((char*)ws + round_up(sizeof(float) * (size_t)T * a.n_split * H * 512));
+    char* w = (char*)ws;
+    a.part_o = (uint16_t*)w;
+    w += round_up(sizeof(uint16_t) * (size_t)T * a.n_split * H * 512);
+    a.part_lse = (float*)w;
+    w += round_up(sizeof(float) * (size_t)T * a.n_split * H);
+    a.part_scale = (float*)w;
   }
   return hip_check(timed(DSA_KERNEL_ATTENTION, st, [&] { return dsa::launch_sparse_mla(a, st); }),
                    "sparse attention launch");

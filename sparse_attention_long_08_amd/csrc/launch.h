@@ -68,7 +68,8 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int64_t T, int64_t 
 // (seq_per_query ? t : 0) through the given addressing: contiguous rows
 // (kv + row*D_qk with row = b*stride + s, s < seq_len) or paged.
 // n_split > 1 splits each query's k entries over n_split workgroups and
-// merges the partials (part_o [T, n_split, H, D_v], part_lse [T, n_split, H]).
+// merges the partials (part_o [T, n_split, H, D_v] f16 scaled by 1/part_scale,
+// part_lse and part_scale [T, n_split, H] fp32).
 struct MlaArgs {
   const uint16_t* q;
   const uint16_t* kv;
@@ -87,8 +88,9 @@ struct MlaArgs {
   const PagedArgs* paged;    // non-null: paged addressing
   // split-key partials
   int32_t n_split;
-  float* part_o;
+  uint16_t* part_o;
   float* part_lse;
+  float* part_scale;
 };
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 

@@ -154,8 +154,9 @@ struct MlaParams {
   int32_t per_split;
   float* out;
   float* lse;
-  float* part_o;
+  uint16_t* part_o;  // f16
   float* part_lse;
+  float* part_scale;
 };
 
 // Drives the pipeline over the three stage buffers.  They arrive as
@@ -488,28 +489,51 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   const float lse_v = empty ? -INFINITY : (m_ref + log2f(l_tot)) * 0.69314718055994530942f;
-  float* orow;
-  float* lrow;
-  if (p.n_split == 1) {
-    orow = p.out + (t * p.H + head) * (int64_t)kDv;
-    lrow = p.lse + t * p.H + head;
-  } else {
-    orow = p.part_o + ((t * p.n_split + sp) * p.H + head) * (int64_t)kDv;
-    lrow = p.part_lse + (t * p.n_split + sp) * p.H + head;
-  }
   // O^T tile ct: lane (head hn, half hh) holds c' = 32*ct + 8*(r/4) + 4*hh + r%4
+  auto o4 = [&](int ct, int r4) {
+    return (v4f){o[ct][4 * r4], o[ct][4 * r4 + 1], o[ct][4 * r4 + 2], o[ct][4 * r4 + 3]};
+  };
+  if (p.n_split == 1) {
+    float* orow = p.out + (t * p.H + head) * (int64_t)kDv;
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) *(v4f*)(orow + 32 * ct + 8 * r4 + 4 * hh) = o4(ct, r4) * inv;
+    if (hh == 0) p.lse[t * p.H + head] = lse_v;
+    return;
+  }
+  // A split's partial: the normalised output in f16, times 2^-e with e >= 0
+  // the smallest that brings the head's largest |value| to at most 2^15
+  // (2^e kept beside its lse; e = 0 unless the latent values are that large).
+  float amax = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) amax = fmaxf(amax, __builtin_fabsf(o[ct][r]));
+  amax *= inv;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+    amax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // both halves of the head
+  }
+  const int e = (amax > 32768.f && amax < INFINITY) ? ilogbf(amax) - 14 : 0;
+  const float sc = inv * ldexpf(1.f, -e);
+  const int64_t prow = (t * p.n_split + sp) * p.H + head;
+  _Float16* orow = reinterpret_cast<_Float16*>(p.part_o) + prow * (int64_t)kDv;
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
-      *(v4f*)(orow + 32 * ct + 8 * r4 + 4 * hh) =
-          (v4f){o[ct][4 * r4], o[ct][4 * r4 + 1], o[ct][4 * r4 + 2], o[ct][4 * r4 + 3]} * inv;
-  if (hh == 0) *lrow = lse_v;
+      *(v4h*)(orow + 32 * ct + 8 * r4 + 4 * hh) = __builtin_convertvector(o4(ct, r4) * sc, v4h);
+  if (hh == 0) {
+    p.part_lse[prow] = lse_v;
+    p.part_scale[prow] = ldexpf(1.f, e);
+  }
 }
 
-// Exact merge of split partials; one workgroup of 128 threads per (t, head).
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_lse, int64_t T, int32_t H,
+// Merge of split partials; one workgroup of 128 threads per (t, head).
+__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ part_o,
+                                                      const float* __restrict__ part_lse,
+                                                      const float* __restrict__ part_scale, int64_t T, int32_t H,
                                                       int32_t n_split, float* __restrict__ out,
                                                       float* __restrict__ lse) {
   const int64_t th = blockIdx.x;  // t * H + h
@@ -528,9 +552,10 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   for (int i = 0; i < n_split; ++i) {
     const float li = part_lse[(t * n_split + i) * H + h];
     if (li == -INFINITY) continue;
-    const float wgt = expf(li - lse_tot);
-    const v4f v = *(const v4f*)(part_o + ((t * n_split + i) * H + h) * (int64_t)kDv + 4 * threadIdx.x);
-    acc += wgt * v;
+    const int64_t prow = (t * n_split + i) * H + h;
+    const float wgt = expf(li - lse_tot) * part_scale[prow];
+    const v4h v = *(const v4h*)(reinterpret_cast<const _Float16*>(part_o) + prow * (int64_t)kDv + 4 * threadIdx.x);
+    acc += wgt * __builtin_convertvector(v, v4f);
   }
   *(v4f*)(out + th * (int64_t)kDv + 4 * threadIdx.x) = acc;
   if (threadIdx.x == 0) lse[th] = lse_tot;
@@ -588,6 +613,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
   p.lse = a.lse;
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
+  p.part_scale = a.part_scale;
   hipError_t e;
   if (a.paged) {
     AddrPaged ad{a.paged->page_table, a.paged->max_pages, __builtin_ctz((unsigned)a.paged->page_size),
@@ -598,8 +624,8 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
     e = launch_mla(p, ad, st);
   }
   if (e != hipSuccess || p.n_split == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.T * a.H)), dim3(128), 0, st, a.part_o, a.part_lse, a.T,
-                     a.H, p.n_split, a.out, a.lse);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.T * a.H)), dim3(128), 0, st, a.part_o, a.part_lse,
+                     a.part_scale, a.T, a.H, p.n_split, a.out, a.lse);
   return hipGetLastError();
 }
 

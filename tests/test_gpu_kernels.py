@@ -337,6 +337,42 @@ def test_sparse_mla_large_logit_jump(dsa):
         check_attention(g_out[t], g_lse[t], o_out, o_lse)
 
 
+def test_sparse_mla_split_partials_of_large_values(dsa):
+    """Split partials are stored in f16, each (split, head) row scaled by a
+    power of two when its largest value passes 2^15.  With the latent rows
+    times 2^20 and the queries times 2^-20 the logits are the same numbers, so
+    the output must be exactly 2^20 times the plain one up to f16 subnormals
+    (here within 2^-11 of the largest value) and the lse equal; the plain call
+    also against the oracle.  8 queries x 2048 entries run 4 splits."""
+    T, H, N, k = 8, 128, 4096, 2048
+    scale = 1.0 / np.sqrt(192.0)
+    _case("sparse_mla split partials of large values")
+    rng = np.random.default_rng(11)
+    qv = rng.standard_normal((T, H, 576)).astype(np.float32)
+    kvv = rng.standard_normal((N, 576)).astype(np.float32)
+    idx = np.stack([rng.permutation(N)[:k] for _ in range(T)]).astype(np.int32)
+    res = {}
+    for name, fq, fkv in (("plain", 1.0, 1.0), ("scaled", 2.0 ** -20, 2.0 ** 20)):
+        q_h, kv_h = _bf16_bits(qv * fq), _bf16_bits(kvv * fkv)
+        q = torch.from_numpy(q_h.view(np.int16)).cuda().view(torch.uint16)
+        kv = torch.from_numpy(kv_h.view(np.int16)).cuda().view(torch.uint16)
+        out = torch.empty((T, H, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        nb = dsa.dsa_sparse_mla_fwd_workspace_bytes(T, H, 512, k)
+        ws = ws_tensor(nb)
+        dsa.dsa_sparse_mla_fwd(q, kv, torch.from_numpy(idx).cuda(), T, N, H, 576, 512, k, scale, out, lse, ws, nb)
+        torch.cuda.synchronize()
+        res[name] = (out.cpu().numpy().astype(np.float64), lse.cpu().numpy(), q_h, kv_h)
+    p_out, p_lse, q_h, kv_h = res["plain"]
+    s_out, s_lse = res["scaled"][0], res["scaled"][1]
+    assert np.array_equal(p_lse, s_lse)
+    assert np.max(np.abs(s_out * 2.0 ** -20 - p_out)) <= 2.0 ** -11 * np.max(np.abs(p_out))
+    assert np.max(np.abs(s_out)) > 2.0 ** 15  # the scaled partials took the scaled store
+    for t in (0, T - 1):
+        o_out, o_lse = oracle.sparse_mla_row(q_h[t], kv_h[idx[t]], scale, 512)
+        check_attention(p_out[t], p_lse[t], o_out, o_lse)
+
+
 def test_sparse_mla_paged(dsa):
     wl = configs.WORKLOADS["paged_decode_b32_ctx4k_128k"]
     ctx = np.array([5, 700, 4096, 2000], dtype=np.int32)
