@@ -292,7 +292,9 @@ __global__ __launch_bounds__(256) void fp8_key_bounds_kernel(const uint8_t* __re
     }
     key_s[s] = S;
   }
-  uint32_t sb = __float_as_uint(S), kb = __float_as_uint(e4m3_abs(kmax));
+  // a NaN code (S.1111.111) anywhere among the keys makes the largest |k_I|
+  // infinite, which sends every row of the call down the exact route
+  uint32_t sb = __float_as_uint(S), kb = __float_as_uint(kmax == 0x7Fu ? INFINITY : e4m3_abs(kmax));
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     sb = max(sb, (uint32_t)__shfl_xor((int)sb, d, 64));
@@ -329,10 +331,10 @@ __global__ __launch_bounds__(256) void fp8_row_bounds_kernel(const uint8_t* __re
       mq[2 * c] = exp_field_pow2(max(max_exp_field(v.x), max_exp_field(v.y)));
       mq[2 * c + 1] = exp_field_pow2(max(max_exp_field(v.z), max_exp_field(v.w)));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t x = (uint32_t)v[i];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sum_abs += e4m3_abs((x >> (8 * b)) & 0xFFu);
+      for (int i = 0; i < 4; ++i) {  // exact conversions, two values each; a NaN code gives NaN
+        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[i], 1.0f, false);
+        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[i], 1.0f, true);
+        sum_abs += (__builtin_fabsf(lo[0]) + __builtin_fabsf(lo[1])) + (__builtin_fabsf(hi[0]) + __builtin_fabsf(hi[1]));
       }
     }
   } else {
@@ -340,20 +342,35 @@ __global__ __launch_bounds__(256) void fp8_row_bounds_kernel(const uint8_t* __re
     for (int g = 0; g < 16; ++g) mq[g] = 0.f;
   }
   const float aw = bad ? 0.f : wj;
-  const float cmax = sum_abs * kmax;  // bound on |c| and |c~| of this head
+  const float cmax = sum_abs * kmax;  // bound on |c| and |c~| of this head (NaN codes: NaN)
   bad = bad || !(cmax <= 60000.f);
   // f16 underflow: a weight below 2^-14 may flush to zero (error w |c|), and
   // a rectified dot product below 2^-14 likewise (error 2^-14 w)
   float eps = (aw < 0x1p-14f ? aw * cmax : 0.f) + 0x1p-14f * aw;
   float imax = aw * cmax;  // bound on the row's |I~|
-  float wmax = 0.f;
+  // W[g] = sum over heads of aw * mq[g] for the 16 groups, then their max:
+  // a transposed reduction -- each exchange halves the groups a lane keeps
+  // (lane bit 5 picks groups 8..15, bit 4 the upper four of those, ...) --
+  // leaves W[8 b5 + 4 b4 + 2 b3 + b2] summed over the other lane bits
+  float x[16];
 #pragma unroll
-  for (int g = 0; g < 16; ++g) {
-    float x = aw * mq[g];
+  for (int g = 0; g < 16; ++g) x[g] = aw * mq[g];
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-    wmax = fmaxf(wmax, x);
+  for (int half = 8, d = 32; half >= 1; half >>= 1, d >>= 1) {
+    const bool up = (lane & d) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float keep = up ? x[i + half] : x[i];
+      const float give = up ? x[i] : x[i + half];
+      x[i] = keep + __shfl_xor(give, d, 64);
+    }
   }
+  float wsum = x[0];
+  wsum += __shfl_xor(wsum, 2, 64);
+  wsum += __shfl_xor(wsum, 1, 64);
+  float wmax = wsum;
+#pragma unroll
+  for (int d = 4; d <= 32; d <<= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, d, 64));
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     eps += __shfl_xor(eps, d, 64);

@@ -108,7 +108,6 @@ static_assert(kAhead >= 2, "a slot consumes up to two units");
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s_t __attribute__((ext_vector_type(8)));
-typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;

@@ -87,3 +87,23 @@ def test_fused_selection_long_rows_and_tiles(dsa):
     h = 300
     g1, _ = _fused_vs_staged(dsa, q_idx[h:], w[h:], k_idx, T - h, N, H_I, k, q_pos0 + h)
     assert np.array_equal(g[h:], g1)
+
+
+@pytest.mark.parametrize("where", ["query", "key"])
+def test_fused_selection_with_nan_codes(dsa, where):
+    """E4M3 NaN codes (S.1111.111): a query row holding one takes the exact
+    route; a key holding one sends every row of the call down the exact
+    route.  The selection still equals the staged exact one, whose scores
+    are NaN wherever such a code meets a candidate."""
+    T, N, k, H_I = 600, 5000, 256, 64
+    q_pos0 = N - T
+    _case(f"fused vs staged with NaN codes in the {where}s")
+    q_idx, w, k_idx = _inputs(5, T, N, H_I)
+    if where == "query":
+        q_idx[7::50, 3, 17] = 0x7F
+        q_idx[11, 0, 0] = 0xFF
+    else:
+        k_idx[1234, 5] = 0x7F
+    g, scores = _fused_vs_staged(dsa, q_idx, w, k_idx, T, N, H_I, k, q_pos0)
+    nan_rows = np.isnan(scores[:, :N]).any(axis=1)
+    assert nan_rows.sum() == (13 if where == "query" else T)
