@@ -541,12 +541,13 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
                                          if (r0 == 0) {
                                            hipError_t e = dsa::launch_fp8_bounds(q_idx, w, k_idx, T, N, H_I, key_s,
                                                                                  glob, row_fac, row_eps, row_flag,
-                                                                                 row_scale, st);
+                                                                                 row_scale, nullptr, st);
                                            if (e != hipSuccess) return e;
                                          }
                                          return dsa::launch_indexer_fp8_prefill(q_idx + r0 * H_I * 128, w + r0 * H_I,
                                                                                 k_idx, tr, N, H_I, q_pos0 + r0,
-                                                                                row_scale + r0, scores, ld, st);
+                                                                                row_scale + r0, scores, ld, nullptr,
+                                                                                st);
                                        }),
                                  "indexer launch"))
       return s;
@@ -555,7 +556,7 @@ dsa_status dsa_forward_prefill(const uint8_t* q_idx, const float* w, const uint8
                                          return dsa::launch_topk_band(scores, ld, tr, N, q_pos0 + r0, k, sel + r0 * k,
                                                                       q_idx + r0 * H_I * 128, w + r0 * H_I, k_idx, H_I,
                                                                       key_s, glob, row_fac + r0, row_eps + r0,
-                                                                      row_flag + r0, row_scale + r0, st);
+                                                                      row_flag + r0, row_scale + r0, nullptr, st);
                                        }),
                                  "top-k launch"))
       return s;
@@ -622,12 +623,19 @@ static size_t chunk_mla_ws(int64_t total_q, int32_t H, int32_t k) {
   return m;
 }
 
+// The fused prefill's layout over all chunks' rows: one score tile, the
+// selection, the FP8 pass's bound inputs (keys of the longest context, the
+// rows of every chunk), then the attention's split partials of one chunk.
+static PrefillWs paged_prefill_ws(int64_t total_q, int64_t max_ctx, int32_t H, int32_t k) {
+  PrefillWs w = prefill_ws(total_q, max_ctx, H, k);
+  w.total = w.mla + chunk_mla_ws(total_q, H, k);
+  return w;
+}
+
 size_t dsa_forward_prefill_paged_workspace_bytes(int64_t total_q, int64_t max_ctx, int32_t H, int32_t /*D_v*/,
                                                  int32_t k) {
   if (total_q <= 0 || max_ctx <= 0 || k <= 0) return 0;
-  const int64_t rows = prefill_tile_rows(total_q, max_ctx);
-  return round_up(sizeof(float) * (size_t)rows * score_ld(max_ctx)) +
-         round_up(sizeof(int32_t) * (size_t)total_q * k) + chunk_mla_ws(total_q, H, k);
+  return paged_prefill_ws(total_q, max_ctx, H, k).total;
 }
 
 dsa_status dsa_forward_prefill_paged(const uint8_t* q_idx, const float* w, const uint8_t* k_pool,
@@ -670,12 +678,20 @@ dsa_status dsa_forward_prefill_paged(const uint8_t* q_idx, const float* w, const
   hipStream_t st = (hipStream_t)stream;
   const int64_t rows = prefill_tile_rows(total_q, max_ctx);
   const int64_t ld = score_ld(max_ctx);
-  char* p = (char*)ws;
-  float* scores = (float*)p;
-  p += round_up(sizeof(float) * (size_t)rows * ld);
-  int32_t* idx_ws = (int32_t*)p;
-  p += round_up(sizeof(int32_t) * (size_t)total_q * k);
-  int32_t* sel = idx ? idx : idx_ws;
+  const PrefillWs wl = paged_prefill_ws(total_q, max_ctx, H, k);
+  char* base = (char*)ws;
+  float* scores = (float*)(base + wl.scores);
+  int32_t* sel = idx ? idx : (int32_t*)(base + wl.idx);
+  float* key_s = (float*)(base + wl.key_s);
+  uint32_t* glob = (uint32_t*)(base + wl.glob);
+  float* row_fac = (float*)(base + wl.row_fac);
+  float* row_eps = (float*)(base + wl.row_eps);
+  int32_t* row_flag = (int32_t*)(base + wl.row_flag);
+  float* row_scale = (float*)(base + wl.row_scale);
+  char* mla = base + wl.mla;
+  // Per sequence: the bound inputs of its keys and chunk rows, then per row
+  // tile the FP8 scoring pass and the band top-k, as in the contiguous fused
+  // prefill, with the keys addressed through the sequence's page-table row.
   for (int64_t b = 0; b < B; ++b) {
     const int64_t q0 = q_start[b], nq = q_start[b + 1] - q0, n = ctx_len[b];
     if (nq == 0) continue;
@@ -685,24 +701,32 @@ dsa_status dsa_forward_prefill_paged(const uint8_t* q_idx, const float* w, const
     for (int64_t r0 = 0; r0 < nq; r0 += rows) {
       const int64_t tr = std::min(rows, nq - r0);
       const int64_t g = q0 + r0;  // first global query row of the tile
-      if (dsa_status s = hip_check(timed(DSA_KERNEL_INDEXER, st,
-                                         [&] {
-                                           return dsa::launch_indexer_prefill(q_idx + g * H_I * 128, w + g * H_I,
-                                                                              k_pool, tr, n, H_I, pos0 + r0, scores,
-                                                                              ld, false, &pa, st);
-                                         }),
-                                   "indexer launch"))
+      if (dsa_status s = hip_check(
+              timed(DSA_KERNEL_INDEXER, st,
+                    [&] {
+                      if (r0 == 0) {
+                        hipError_t e = dsa::launch_fp8_bounds(q_idx + q0 * H_I * 128, w + q0 * H_I, k_pool, nq, n,
+                                                              H_I, key_s, glob, row_fac + q0, row_eps + q0,
+                                                              row_flag + q0, row_scale + q0, &pa, st);
+                        if (e != hipSuccess) return e;
+                      }
+                      return dsa::launch_indexer_fp8_prefill(q_idx + g * H_I * 128, w + g * H_I, k_pool, tr, n, H_I,
+                                                             pos0 + r0, row_scale + g, scores, ld, &pa, st);
+                    }),
+              "indexer launch"))
         return s;
       if (dsa_status s = hip_check(timed(DSA_KERNEL_TOPK, st,
                                          [&] {
-                                           return dsa::launch_topk(scores, ld, tr, n, pos0 + r0, nullptr, k,
-                                                                   sel + g * k, st);
+                                           return dsa::launch_topk_band(scores, ld, tr, n, pos0 + r0, k, sel + g * k,
+                                                                        q_idx + g * H_I * 128, w + g * H_I, k_pool,
+                                                                        H_I, key_s, glob, row_fac + g, row_eps + g,
+                                                                        row_flag + g, row_scale + g, &pa, st);
                                          }),
                                    "top-k launch"))
         return s;
     }
     if (dsa_status s = run_mla(q + q0 * H * 576, kv_pool, sel + q0 * k, nq, H, k, scale, out + q0 * H * 512,
-                               lse + q0 * H, p, ws_bytes - (size_t)(p - (char*)ws), false, 0, n, nullptr, &pa, st))
+                               lse + q0 * H, mla, ws_bytes - wl.mla, false, 0, n, nullptr, &pa, st))
       return s;
   }
   return ok();

@@ -270,17 +270,21 @@ __device__ __forceinline__ float e4m3_abs(uint32_t b) {
 }
 
 // One thread per key: S[s], and over all keys the largest S and the largest
-// |k_I| (as float bits; positive floats order like their bit patterns).
-__global__ __launch_bounds__(256) void fp8_key_bounds_kernel(const uint8_t* __restrict__ k_idx, int64_t N,
+// |k_I| (as float bits; positive floats order like their bit patterns).  Key
+// s is row addr.row(0, s) of k_idx; a key without a backing row is a zero key.
+template <class Addr>
+__global__ __launch_bounds__(256) void fp8_key_bounds_kernel(const uint8_t* __restrict__ k_idx, Addr addr, int64_t N,
                                                              float* __restrict__ key_s, uint32_t* __restrict__ glob) {
   const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
   float S = 0.f;
   uint32_t kmax = 0;
   if (s < N) {
-    const v4i* p = (const v4i*)(k_idx + s * kIdxD);
+    const int64_t row = addr.row(0, s);
+    const v4i* p = (const v4i*)(k_idx + (row < 0 ? 0 : row) * kIdxD);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const v4i v = p[c];
+      const v4i z = {0, 0, 0, 0};
+      const v4i v = row < 0 ? z : p[c];
       S += exp_field_pow2(max(max_exp_field(v.x), max_exp_field(v.y)));
       S += exp_field_pow2(max(max_exp_field(v.z), max_exp_field(v.w)));
 #pragma unroll
@@ -405,11 +409,11 @@ __global__ __launch_bounds__(256) void fp8_row_bounds_kernel(const uint8_t* __re
 // in column b for block b: the four blocks accumulate into one 16x16 result
 // whose column b holds block b's scores, so lane (g, b) ends with the scores of
 // keys 16 b + 4 g .. +3 and stores them as one 16-byte write.
-template <int NT>
+template <int NT, class Addr>
 __global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
-    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx, int64_t T,
-    int64_t N, int32_t H_I, int64_t q_pos0, const float* __restrict__ row_scale, float* __restrict__ scores,
-    int64_t ld, int32_t key_chunk) {
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w, const uint8_t* __restrict__ k_idx, Addr addr,
+    int64_t T, int64_t N, int32_t H_I, int64_t q_pos0, const float* __restrict__ row_scale,
+    float* __restrict__ scores, int64_t ld, int32_t key_chunk) {
   constexpr int NS = (NT + 1) / 2;  // f16 k-steps of the head sum, two head tiles each
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][64 * kIdxD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -450,10 +454,13 @@ __global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
 
   const int st_key = 16 * wave + col;
   auto slot = [](int key, int ch) { return ch ^ ((key >> 1) & 7); };
+  // key s of the sequence is row addr.row(0, s); a 64-key group lies in one
+  // page, so one lookup per group (a group without a backing row stages zeros)
   auto stage_load = [&](int64_t kg, v4i& s0, v4i& s1) {
     const int64_t s = kg + st_key;
-    if (s < c_end) {
-      const v4i* p = (const v4i*)(k_idx + s * kIdxD + 32 * grp);
+    const int64_t grow = addr.group_row(0, kg);
+    if (s < c_end && grow >= 0) {
+      const v4i* p = (const v4i*)(k_idx + (grow + st_key) * kIdxD + 32 * grp);
       s0 = p[0];
       s1 = p[1];
     } else {
@@ -603,11 +610,18 @@ hipError_t launch_indexer_decode(const uint8_t* q_idx, const float* w, const uin
 
 hipError_t launch_fp8_bounds(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
                              int32_t H_I, float* key_s, uint32_t* glob, float* row_fac, float* row_eps,
-                             int32_t* row_flag, float* row_scale, hipStream_t st) {
+                             int32_t* row_flag, float* row_scale, const PagedArgs* paged, hipStream_t st) {
   hipError_t e = launch_zero_f32(reinterpret_cast<float*>(glob), 2, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fp8_key_bounds_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, k_idx, N, key_s,
-                     glob);
+  const dim3 kgrid((unsigned)((N + 255) / 256));
+  if (paged) {
+    const AddrPaged ad{paged->page_table, paged->max_pages, __builtin_ctz((unsigned)paged->page_size),
+                       paged->n_pages};
+    hipLaunchKernelGGL(fp8_key_bounds_kernel<AddrPaged>, kgrid, dim3(256), 0, st, k_idx, ad, N, key_s, glob);
+  } else {
+    hipLaunchKernelGGL(fp8_key_bounds_kernel<AddrSingle>, kgrid, dim3(256), 0, st, k_idx, AddrSingle{N}, N, key_s,
+                       glob);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(fp8_row_bounds_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, q_idx, w, T, H_I, glob,
@@ -616,28 +630,40 @@ hipError_t launch_fp8_bounds(const uint8_t* q_idx, const float* w, const uint8_t
 }
 
 namespace {
-template <int NT>
-hipError_t fp8_prefill_nt(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
+template <int NT, class Addr>
+hipError_t fp8_prefill_nt(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, Addr addr, int64_t T, int64_t N,
                           int32_t H_I, int64_t q_pos0, const float* row_scale, float* scores, int64_t ld,
                           hipStream_t st) {
   const int64_t n_all = std::min<int64_t>(q_pos0 + T, N);
   dim3 grid((unsigned)((T + 3) / 4), (unsigned)((n_all + kPrefillChunk - 1) / kPrefillChunk));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((indexer_fp8_prefill_kernel<NT>), grid, dim3(256), 0, st, q_idx, w, k_idx, T, N, H_I, q_pos0,
-                     row_scale, scores, ld, kPrefillChunk);
+  hipLaunchKernelGGL((indexer_fp8_prefill_kernel<NT, Addr>), grid, dim3(256), 0, st, q_idx, w, k_idx, addr, T, N,
+                     H_I, q_pos0, row_scale, scores, ld, kPrefillChunk);
   return hipGetLastError();
+}
+
+template <class Addr>
+hipError_t fp8_prefill_dispatch(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, Addr addr, int64_t T,
+                                int64_t N, int32_t H_I, int64_t q_pos0, const float* row_scale, float* scores,
+                                int64_t ld, hipStream_t st) {
+  switch ((H_I + 15) / 16) {
+    case 1: return fp8_prefill_nt<1>(q_idx, w, k_idx, addr, T, N, H_I, q_pos0, row_scale, scores, ld, st);
+    case 2: return fp8_prefill_nt<2>(q_idx, w, k_idx, addr, T, N, H_I, q_pos0, row_scale, scores, ld, st);
+    case 3: return fp8_prefill_nt<3>(q_idx, w, k_idx, addr, T, N, H_I, q_pos0, row_scale, scores, ld, st);
+    default: return fp8_prefill_nt<4>(q_idx, w, k_idx, addr, T, N, H_I, q_pos0, row_scale, scores, ld, st);
+  }
 }
 }  // namespace
 
 hipError_t launch_indexer_fp8_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T,
                                       int64_t N, int32_t H_I, int64_t q_pos0, const float* row_scale, float* scores,
-                                      int64_t ld, hipStream_t st) {
-  switch ((H_I + 15) / 16) {
-    case 1: return fp8_prefill_nt<1>(q_idx, w, k_idx, T, N, H_I, q_pos0, row_scale, scores, ld, st);
-    case 2: return fp8_prefill_nt<2>(q_idx, w, k_idx, T, N, H_I, q_pos0, row_scale, scores, ld, st);
-    case 3: return fp8_prefill_nt<3>(q_idx, w, k_idx, T, N, H_I, q_pos0, row_scale, scores, ld, st);
-    default: return fp8_prefill_nt<4>(q_idx, w, k_idx, T, N, H_I, q_pos0, row_scale, scores, ld, st);
+                                      int64_t ld, const PagedArgs* paged, hipStream_t st) {
+  if (paged) {
+    const AddrPaged ad{paged->page_table, paged->max_pages, __builtin_ctz((unsigned)paged->page_size),
+                       paged->n_pages};
+    return fp8_prefill_dispatch(q_idx, w, k_idx, ad, T, N, H_I, q_pos0, row_scale, scores, ld, st);
   }
+  return fp8_prefill_dispatch(q_idx, w, k_idx, AddrSingle{N}, T, N, H_I, q_pos0, row_scale, scores, ld, st);
 }
 
 }  // namespace dsa

@@ -26,13 +26,14 @@ hipError_t launch_indexer_prefill(const uint8_t* q_idx, const float* w, const ui
 // approximate scores of the causal pairs (candidates only, f16 I~ * 2^-s in
 // the first half of each fp32 tile row).  key_s [N], glob [2] (cleared here:
 // largest key_s, largest |k_I|, as float bits), row_fac / row_eps / row_flag /
-// row_scale (2^s) [T].
+// row_scale (2^s) [T].  Keys are rows 0..N-1 of k_idx, or (paged != nullptr)
+// pool rows through page-table row 0 of `paged`.
 hipError_t launch_fp8_bounds(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T, int64_t N,
                              int32_t H_I, float* key_s, uint32_t* glob, float* row_fac, float* row_eps,
-                             int32_t* row_flag, float* row_scale, hipStream_t st);
+                             int32_t* row_flag, float* row_scale, const PagedArgs* paged, hipStream_t st);
 hipError_t launch_indexer_fp8_prefill(const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int64_t T,
                                       int64_t N, int32_t H_I, int64_t q_pos0, const float* row_scale, float* scores,
-                                      int64_t ld, hipStream_t st);
+                                      int64_t ld, const PagedArgs* paged, hipStream_t st);
 
 // Indexer scores for B decode queries; keys of sequence b are either rows
 // b*stride + s of k_idx (paged == nullptr) or pool rows via the page table.
@@ -50,11 +51,12 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, in
 // each row's threshold rescored exactly.  scores (the tile) is also written:
 // rows that take the exact route are rescored in place.  q_idx, w, row_fac,
 // row_eps, row_flag and row_scale are the tile's rows; key_s and glob as
-// filled by launch_fp8_bounds.
+// filled by launch_fp8_bounds; keys addressed as there.
 hipError_t launch_topk_band(float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0, int32_t k,
                             int32_t* idx, const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int32_t H_I,
                             const float* key_s, const uint32_t* glob, const float* row_fac, const float* row_eps,
-                            const int32_t* row_flag, const float* row_scale, hipStream_t st);
+                            const int32_t* row_flag, const float* row_scale, const PagedArgs* paged,
+                            hipStream_t st);
 
 // Top-k for a few long rows (decode): the full-row passes run over
 // 4096-key chunks in parallel; needs topk_rows_scratch_bytes(T, N) of device

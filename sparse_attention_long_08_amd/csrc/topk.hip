@@ -770,7 +770,11 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int64_t T, int64_t 
 struct BandArgs {
   const uint8_t* q_idx;     // the tile's query rows [T, H_I, 128]
   const float* w;           // [T, H_I]
-  const uint8_t* k_idx;     // [N, 128]
+  const uint8_t* k_idx;     // keys: rows 0..N-1, or a page pool through page_table
+  const int32_t* page_table;  // nullptr: contiguous keys; else the sequence's page-table row
+  int32_t max_pages;
+  int32_t page_shift;
+  int64_t n_pages;
   int32_t H_I;
   const float* key_s;       // [N] S of each key
   const uint32_t* glob;     // [0]: largest S (float bits)
@@ -779,6 +783,14 @@ struct BandArgs {
   const int32_t* row_flag;  // [T] nonzero: exact route
   const float* row_scale;   // [T] 2^s: the tile holds each row's scores times 2^-s, in f16
 };
+
+// Row of k_idx holding key s (-1: no backing row, a zero key).  A template
+// parameter, so that the contiguous kernel carries none of the paged lookup.
+template <bool kPaged>
+__device__ __forceinline__ int64_t band_key_row(const BandArgs& ba, int64_t s) {
+  if constexpr (!kPaged) return s;
+  return AddrPaged{ba.page_table, ba.max_pages, ba.page_shift, ba.n_pages}.row(0, s);
+}
 
 // inverse of order_key
 __device__ __forceinline__ float key_float(uint32_t key) {
@@ -828,11 +840,12 @@ __device__ __forceinline__ uint32_t row_theta_exact(TopkShared& sh, int64_t n, i
 
 // Exact scores of nk keys of one query row, each wave taking 64 keys at a
 // time through the score kernels' own arithmetic (indexer_exact.h): entry e
-// is key pos(e); out(e, score) runs on the lane that holds entry e.
-template <int NT, class PosFn, class OutFn>
+// is the key in row key_row(e) of k_idx (with kZeroKeys, -1 is a zero key);
+// out(e, score) runs on the lane that holds entry e.
+template <int NT, bool kZeroKeys, class RowFn, class OutFn>
 __device__ __forceinline__ void rescore_exact(const uint8_t* __restrict__ q_row, const float* __restrict__ w_row,
-                                              int32_t H_I, const uint8_t* __restrict__ k_idx, int nk, PosFn pos,
-                                              OutFn out) {
+                                              int32_t H_I, const uint8_t* __restrict__ k_idx, int nk,
+                                              RowFn key_row, OutFn out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int n_chunks = (nk + 63) / 64;
@@ -845,8 +858,15 @@ __device__ __forceinline__ void rescore_exact(const uint8_t* __restrict__ q_row,
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const int e = min(64 * ch + 16 * blk + col, nk - 1);
-      const v4i* p = (const v4i*)(k_idx + pos(e) * kIdxD + 32 * grp);
-      part[blk] = head_sum<NT>(a, wr, widen32(p[0], p[1]));
+      const int64_t r = key_row(e);
+      if constexpr (kZeroKeys) {  // a zero key scores +0 exactly, whatever row 0 holds
+        const v4i* p = (const v4i*)(k_idx + (r < 0 ? 0 : r) * kIdxD + 32 * grp);
+        const float h = head_sum<NT>(a, wr, widen32(p[0], p[1]));
+        part[blk] = r < 0 ? 0.f : h;
+      } else {
+        const v4i* p = (const v4i*)(k_idx + r * kIdxD + 32 * grp);
+        part[blk] = head_sum<NT>(a, wr, widen32(p[0], p[1]));
+      }
     }
     const float v = group_transpose_reduce(part[0], part[1], part[2], part[3], grp);
     const int e = 64 * ch + lane;
@@ -860,7 +880,7 @@ constexpr float kRelErr = 0x1.1p-9f;
 
 // The band selection of one row (see above).  Returns false, having written
 // no output, when the row must take the exact route instead.
-template <int NT>
+template <int NT, bool kPaged>
 __device__ __forceinline__ bool band_select(TopkShared& sh, const _Float16* __restrict__ row, int64_t n, int32_t k,
                                             int64_t t, const BandArgs& ba, uint32_t* gt_bits, uint32_t* eq_bits,
                                             int32_t* __restrict__ out) {
@@ -974,8 +994,8 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const _Float16* __re
   if (n_sure >= (uint32_t)k || (uint32_t)nb < (uint32_t)k - n_sure) return false;
 
   // exact scores of the band keys, as order keys in the list
-  rescore_exact<NT>(ba.q_idx + t * ba.H_I * kIdxD, ba.w + t * ba.H_I, ba.H_I, ba.k_idx, nb,
-                    [&](int e) { return (int64_t)sh.list_idx[e]; },
+  rescore_exact<NT, kPaged>(ba.q_idx + t * ba.H_I * kIdxD, ba.w + t * ba.H_I, ba.H_I, ba.k_idx, nb,
+                    [&](int e) { return band_key_row<kPaged>(ba, sh.list_idx[e]); },
                     [&](int e, float v) { sh.list_key[e] = order_key(v); });
   __syncthreads();
   const uint32_t hi = select_in_list(sh, nb, sh.list_key, (uint32_t)k - n_sure, 3);  // theta itself
@@ -996,7 +1016,7 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const _Float16* __re
 // scores of the candidates, f16 scaled per row).  Rows without a band
 // selection are rescored in place with the exact arithmetic (as fp32, over
 // the row's full fp32 stride) and take the plain selection.
-template <int NT>
+template <int NT, bool kPaged>
 __global__ __launch_bounds__(kTopkThreads) void topk_band_kernel(float* __restrict__ scores, int64_t ld, int64_t T,
                                                                   int64_t N, int64_t q_pos0, int32_t k,
                                                                   int32_t* __restrict__ idx, int32_t n_words,
@@ -1015,12 +1035,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_band_kernel(float* __restri
     return;
   }
   float* row = scores + t * ld;  // 16-byte aligned (ld is a multiple of 64)
-  if (ba.row_flag[t] == 0 && band_select<NT>(sh, reinterpret_cast<const _Float16*>(row), n, k, t, ba, gt_bits,
+  if (ba.row_flag[t] == 0 && band_select<NT, kPaged>(sh, reinterpret_cast<const _Float16*>(row), n, k, t, ba, gt_bits,
                                              eq_bits, out))
     return;
   // exact route: the whole row rescored in place as fp32, then the plain selection
-  rescore_exact<NT>(ba.q_idx + t * ba.H_I * kIdxD, ba.w + t * ba.H_I, ba.H_I, ba.k_idx, (int)n,
-                    [](int e) { return (int64_t)e; }, [&](int e, float v) { row[e] = v; });
+  rescore_exact<NT, kPaged>(ba.q_idx + t * ba.H_I * kIdxD, ba.w + t * ba.H_I, ba.H_I, ba.k_idx, (int)n,
+                    [&](int e) { return band_key_row<kPaged>(ba, e); }, [&](int e, float v) { row[e] = v; });
   __threadfence();
   __syncthreads();
   if (n >= kSampleMinN && topk_sampled(sh, row, n, k, gt_bits, eq_bits, n_words, out)) return;
@@ -1028,19 +1048,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_band_kernel(float* __restri
 }
 
 namespace {
-template <int NT>
+template <int NT, bool kPaged>
 hipError_t topk_band_nt(float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0, int32_t k, int32_t* idx,
                         const BandArgs& ba, hipStream_t st) {
   const int32_t n_words = (int32_t)((N + 31) / 32);
   const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words + 256;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_band_kernel<NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void*)topk_band_kernel<NT, kPaged>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192 + 256));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(topk_band_kernel<NT>, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, T, N, q_pos0,
+  hipLaunchKernelGGL((topk_band_kernel<NT, kPaged>), dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, T, N, q_pos0,
                      k, idx, n_words, ba);
   return hipGetLastError();
 }
@@ -1049,14 +1069,32 @@ hipError_t topk_band_nt(float* scores, int64_t ld, int64_t T, int64_t N, int64_t
 hipError_t launch_topk_band(float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0, int32_t k,
                             int32_t* idx, const uint8_t* q_idx, const float* w, const uint8_t* k_idx, int32_t H_I,
                             const float* key_s, const uint32_t* glob, const float* row_fac, const float* row_eps,
-                            const int32_t* row_flag, const float* row_scale, hipStream_t st) {
+                            const int32_t* row_flag, const float* row_scale, const PagedArgs* paged,
+                            hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const BandArgs ba{q_idx, w, k_idx, H_I, key_s, glob, row_fac, row_eps, row_flag, row_scale};
+  const BandArgs ba{q_idx,
+                    w,
+                    k_idx,
+                    paged ? paged->page_table : nullptr,
+                    paged ? paged->max_pages : 0,
+                    paged ? __builtin_ctz((unsigned)paged->page_size) : 0,
+                    paged ? paged->n_pages : 0,
+                    H_I,
+                    key_s,
+                    glob,
+                    row_fac,
+                    row_eps,
+                    row_flag,
+                    row_scale};
   switch ((H_I + 15) / 16) {
-    case 1: return topk_band_nt<1>(scores, ld, T, N, q_pos0, k, idx, ba, st);
-    case 2: return topk_band_nt<2>(scores, ld, T, N, q_pos0, k, idx, ba, st);
-    case 3: return topk_band_nt<3>(scores, ld, T, N, q_pos0, k, idx, ba, st);
-    default: return topk_band_nt<4>(scores, ld, T, N, q_pos0, k, idx, ba, st);
+    case 1: return paged ? topk_band_nt<1, true>(scores, ld, T, N, q_pos0, k, idx, ba, st)
+                         : topk_band_nt<1, false>(scores, ld, T, N, q_pos0, k, idx, ba, st);
+    case 2: return paged ? topk_band_nt<2, true>(scores, ld, T, N, q_pos0, k, idx, ba, st)
+                         : topk_band_nt<2, false>(scores, ld, T, N, q_pos0, k, idx, ba, st);
+    case 3: return paged ? topk_band_nt<3, true>(scores, ld, T, N, q_pos0, k, idx, ba, st)
+                         : topk_band_nt<3, false>(scores, ld, T, N, q_pos0, k, idx, ba, st);
+    default: return paged ? topk_band_nt<4, true>(scores, ld, T, N, q_pos0, k, idx, ba, st)
+                          : topk_band_nt<4, false>(scores, ld, T, N, q_pos0, k, idx, ba, st);
   }
 }
 
