@@ -700,10 +700,10 @@ def bench_bwd(args, wl):
     w = algorithmic_work(wl, T)
     # per selected (query, entry) pair and head: the dq kernel forms the logits
     # (576), dP (512) and dq (576); the dkv kernel dS^T q (576) and P^T dO (512).
-    # The row sums read each pair's fp32 addend row once and update dkv.
+    # The row sums read each pair's bf16 addend row once and update dkv.
     flops = {"mla_bwd_dq": w["selected"] * 2 * H * (wl.D_qk + wl.D_v + wl.D_qk),
              "mla_bwd_dkv": w["selected"] * 2 * H * (wl.D_qk + wl.D_v)}
-    red_bytes = w["selected"] * (wl.D_qk * 4 + 2 * 4 + 4)
+    red_bytes = w["selected"] * (wl.D_qk * 2 + 2 * 4 + 4)
     dom = max(stage_ms, key=stage_ms.get)
     launches = rec_t[dom][1] // args.steps
     if dom == "mla_bwd_reduce":

@@ -184,11 +184,12 @@ dsa_status dsa_sparse_mla_fwd_paged(const uint16_t* q, const uint16_t* kv_pool, 
  *   then accumulated; rows no query selects are 0).
  * P and dS enter the gradient products as bf16 (relative error ~2^-9 per
  * term); products are bf16 x bf16 with fp32 accumulation.  Each (query,
- * entry) contribution to dkv is formed as an fp32 row; the rows of one cache
- * row are summed in fp32 in an order that may vary from call to call.
+ * entry) contribution to dkv is formed in fp32 and stored as a bf16 row
+ * (rounded to nearest, 2^-9 relative); the rows of one cache row are summed
+ * in fp32 in an order that may vary from call to call.
  * ws: P, dS and the contribution rows of a tile of up to 2048 queries plus
  * their grouping by cache row; size from
- * dsa_sparse_mla_bwd_workspace_bytes(T, N, H, k) (about 12 GB at k = 2048,
+ * dsa_sparse_mla_bwd_workspace_bytes(T, N, H, k) (about 7 GB at k = 2048,
  * H = 128; DSA_ERR_WORKSPACE_TOO_SMALL below it).  N <= 2^30.  All pointers
  * are device memory owned by the caller.
  */

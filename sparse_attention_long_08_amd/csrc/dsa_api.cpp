@@ -300,7 +300,7 @@ dsa_status dsa_sparse_mla_fwd(const uint16_t* q, const uint16_t* kv, const int32
 }
 
 // Queries per tile of the attention backward.  A tile's workspace holds P
-// and dS (bf16 [tile, k rounded up to 32, H rounded up to 64]), the fp32 addend rows [tile, k, 576] (9.7 GB at
+// and dS (bf16 [tile, k rounded up to 32, H rounded up to 64]), the bf16 addend rows [tile, k, 576] (4.8 GB at
 // k = 2048) and the inverted index of its entries.
 constexpr int64_t kBwdTile = 2048;
 
@@ -320,7 +320,7 @@ BwdWs bwd_ws(int64_t T, int64_t N, int32_t H, int32_t k) {
   w.ds = o;
   o += al256(ent_p * dsa::mla_bwd_slot_heads(H) * 2);
   w.addend = o;
-  o += al256(ent * 576 * 4);
+  o += al256(ent * 576 * 2);
   w.count = o;
   o += al256((size_t)N * 4);
   w.offsets = o;
@@ -376,7 +376,7 @@ dsa_status dsa_sparse_mla_bwd(const uint16_t* q, const uint16_t* kv, const int32
     a.dq = dq + t0 * H * (int64_t)D_qk;
     a.pbuf = (uint16_t*)(base + w.p);
     a.dsbuf = (uint16_t*)(base + w.ds);
-    a.addend = (float*)(base + w.addend);
+    a.addend = (uint16_t*)(base + w.addend);
     a.row_count = (int32_t*)(base + w.count);
     a.row_offsets = (int32_t*)(base + w.offsets);
     a.row_list = (int32_t*)(base + w.list);

@@ -112,7 +112,7 @@ hipError_t launch_indexer_dense_kl(const uint16_t* q, const uint16_t* kv, int64_
 // Sparse MLA-MQA backward over one tile of T queries.  Stage 0 (dq kernel):
 // dq, and P / dS of every entry into pbuf / dsbuf ([T, kp, Hs] bf16, kp = k
 // rounded up to 32, Hs = mla_bwd_slot_heads(H)); stage 1 (dkv kernel): each entry's contribution
-// to its cache row into addend ([T, k, 576] fp32); stage 2: groups the
+// to its cache row into addend ([T, k, 576] bf16); stage 2: groups the
 // entries by cache row (row_count [N], row_offsets [N+1], row_list [T*k]
 // int32) and adds each row's sum to dkv (dkv cleared beforehand).
 struct MlaBwdArgs {
@@ -130,7 +130,7 @@ struct MlaBwdArgs {
   float* dq;
   uint16_t* pbuf;
   uint16_t* dsbuf;
-  float* addend;
+  uint16_t* addend;
   int32_t* row_count;
   int32_t* row_offsets;
   int32_t* row_list;

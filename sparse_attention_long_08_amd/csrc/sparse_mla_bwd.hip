@@ -29,7 +29,8 @@
 // all heads in the B layout of the head contraction (heads on k), streams
 // the P and dS tiles of each 32-entry block through LDS by DMA, forms
 //   addend_block = dS^T q + P^T dO          (32 entries x 576 dims)
-// and stores it, one fp32 row per (query, entry).
+// and stores it, one bf16 row per (query, entry) (rounded to nearest: 2^-9
+// of each addend, against the 2^-7 tolerance of the gradients).
 //
 // dkv sums the addends over every (query, entry) that selected a row, so it
 // is a scatter.  Instead of atomics (whose adds all travel to the memory
@@ -108,7 +109,7 @@ struct BwdParams {
   float* dq;             // [T, H, 576]
   uint16_t* pbuf;        // [T, kp, Hs] bf16 P (entries k .. kp-1 and heads H .. Hs-1 are padding)
   uint16_t* dsbuf;       // [T, kp, Hs] bf16 dS (scale folded in)
-  float* addend;         // [T, k, 576] fp32: each entry's contribution to its cache row
+  uint16_t* addend;      // [T, k, 576] bf16: each entry's contribution to its cache row
 };
 
 // Resolves the entries of query t to cache rows (-1: skipped), padded with
@@ -507,11 +508,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void mla_bwd_dkv_kernel(BwdParams p)
       for (int r = 0; r < 4; ++r) {
         const int e = blk * kBlk + 16 * kt + 4 * qd + r;
         if (e < p.k) {
-          float* dst = p.addend + (t * (int64_t)p.k + e) * kDqk + hn;
+          uint16_t* dst = p.addend + (t * (int64_t)p.k + e) * kDqk + hn;
 #pragma unroll
           for (int ci = 0; ci < kTilesPerWave; ++ci) {
             const int tile = kv_tile(wave, ci);
-            if (tile >= 0) dst[16 * tile] = acc[kt][ci][r];
+            if (tile >= 0) dst[16 * tile] = __builtin_bit_cast(uint16_t, to_bf16(acc[kt][ci][r]));
           }
         }
       }
@@ -537,28 +538,34 @@ __global__ void csr_count_kernel(const int32_t* __restrict__ idx, int64_t n_ent,
   }
 }
 
-// One workgroup of 1024 threads: thread i scans a contiguous chunk.
+// One workgroup of 1024 threads: thread i sums a contiguous chunk, the 1024
+// chunk sums are scanned across the workgroup (within each wave by shuffles,
+// then over the 16 wave totals), and each thread writes its chunk's offsets.
 __global__ __launch_bounds__(1024) void csr_scan_kernel(int32_t* __restrict__ count, int32_t* __restrict__ offsets,
                                                         int64_t N) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
+  __shared__ int32_t wave_sum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t chunk = (N + 1023) / 1024;
-  const int64_t b = tid * chunk, e = b + chunk < N ? b + chunk : N;
+  const int64_t b = tid * chunk < N ? tid * chunk : N, e = b + chunk < N ? b + chunk : N;
   int32_t sum = 0;
   for (int64_t i = b; i < e; ++i) sum += count[i];
-  part[tid] = sum;
-  __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int i = 0; i < 1024; ++i) {
-      const int32_t v = part[i];
-      part[i] = run;
-      run += v;
-    }
-    offsets[N] = run;
+  int32_t incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
   }
+  if (lane == 63) wave_sum[wave] = incl;
   __syncthreads();
-  int32_t run = part[tid];
+  int32_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int32_t v = wave_sum[w];
+    before += w < wave ? v : 0;
+    total += v;
+  }
+  if (tid == 0) offsets[N] = total;
+  int32_t run = before + incl - sum;
   for (int64_t i = b; i < e; ++i) {
     const int32_t c = count[i];
     offsets[i] = run;
@@ -575,44 +582,85 @@ __global__ void csr_fill_kernel(const int32_t* __restrict__ idx, int64_t n_ent, 
   }
 }
 
-// dkv[s] += sum of the addend rows listed for s: one wave per cache row, lane
-// l holding dims l + 64c (c < 9); list entries are fetched 64 at a time.
+// dkv[s] += sum of the (bf16) addend rows listed for s, in fp32: one wave per
+// cache row.  Lane l holds dims 4l..4l+3 of the first and second 256-dim
+// halves of the row and, for l < 16, of the 64 rope dims, so a row is three
+// 8-byte loads per lane; list entries are fetched 64 at a time and kRedRows
+// rows are in flight.
+constexpr int kRedRows = 8;
+
+struct Bf16x4 {
+  float v[4];
+};
+
+__device__ __forceinline__ Bf16x4 bf16x4_to_f32(uint2 w) {
+  Bf16x4 r;
+  r.v[0] = __uint_as_float(w.x << 16);
+  r.v[1] = __uint_as_float(w.x & 0xFFFF0000u);
+  r.v[2] = __uint_as_float(w.y << 16);
+  r.v[3] = __uint_as_float(w.y & 0xFFFF0000u);
+  return r;
+}
+
 __global__ __launch_bounds__(256) void dkv_reduce_kernel(const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ list,
-                                                         const float* __restrict__ addend, float* __restrict__ dkv,
-                                                         int64_t N) {
+                                                         const uint16_t* __restrict__ addend,
+                                                         float* __restrict__ dkv, int64_t N) {
   const int lane = threadIdx.x & 63;
   const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (s >= N) return;
   const int32_t b = offsets[s], e = offsets[s + 1];
   if (b == e) return;
-  float acc[9];
+  const bool rope = lane < 16;
+  float acc[3][4];
 #pragma unroll
-  for (int c = 0; c < 9; ++c) acc[c] = 0.f;
+  for (int c = 0; c < 3; ++c)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc[c][x] = 0.f;
   for (int32_t i0 = b; i0 < e; i0 += 64) {
     const int32_t n = e - i0 < 64 ? e - i0 : 64;
     const int32_t mine = lane < n ? list[i0 + lane] : 0;
     int32_t j = 0;
-    for (; j + 4 <= n; j += 4) {  // four addend rows (36 loads per lane) in flight
-      float v[4][9];
+    for (; j + kRedRows <= n; j += kRedRows) {
+      uint2 w[kRedRows][3];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float* r = addend + (int64_t)__shfl(mine, j + u, 64) * kDqk + lane;
-#pragma unroll
-        for (int c = 0; c < 9; ++c) v[u][c] = r[64 * c];
+      for (int u = 0; u < kRedRows; ++u) {
+        const uint2* r = reinterpret_cast<const uint2*>(addend + (int64_t)__shfl(mine, j + u, 64) * kDqk) + lane;
+        w[u][0] = r[0];
+        w[u][1] = r[64];
+        w[u][2] = rope ? r[128] : make_uint2(0u, 0u);
       }
 #pragma unroll
-      for (int c = 0; c < 9; ++c) acc[c] += (v[0][c] + v[1][c]) + (v[2][c] + v[3][c]);
+      for (int u = 0; u < kRedRows; ++u)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          const Bf16x4 f = bf16x4_to_f32(w[u][c]);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) acc[c][x] += f.v[x];
+        }
     }
     for (; j < n; ++j) {
-      const float* r = addend + (int64_t)__shfl(mine, j, 64) * kDqk + lane;
+      const uint2* r = reinterpret_cast<const uint2*>(addend + (int64_t)__shfl(mine, j, 64) * kDqk) + lane;
+      uint2 w[3] = {r[0], r[64], rope ? r[128] : make_uint2(0u, 0u)};
 #pragma unroll
-      for (int c = 0; c < 9; ++c) acc[c] += r[64 * c];
+      for (int c = 0; c < 3; ++c) {
+        const Bf16x4 f = bf16x4_to_f32(w[c]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[c][x] += f.v[x];
+      }
     }
   }
-  float* d = dkv + s * kDqk + lane;
+  float4* d = reinterpret_cast<float4*>(dkv + s * kDqk) + lane;
 #pragma unroll
-  for (int c = 0; c < 9; ++c) d[64 * c] += acc[c];
+  for (int c = 0; c < 3; ++c) {
+    if (c == 2 && !rope) break;
+    float4 o = d[64 * c];
+    o.x += acc[c][0];
+    o.y += acc[c][1];
+    o.z += acc[c][2];
+    o.w += acc[c][3];
+    d[64 * c] = o;
+  }
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ x, int64_t n) {
