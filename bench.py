@@ -47,23 +47,28 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per stage launch read with rocprofv3 (FETCH_SIZE and WRITE_SIZE, one counter per run,
-# on the fused calls alone: bench.py --fused-only), summed over the kernels of the stage,
-# scaled by what the same counters read for a plain 1 GiB device copy (bytes read =
-# FETCH_SIZE KiB x 1024 x 2.0, bytes written = WRITE_SIZE KiB x 1024 x 1.0).  Each entry holds
-# the hash of the kernel's device sources (its .hip file and common.h) the counters were taken
+# on the timed calls alone: bench.py --fused-only, or --bwd --no-cpu for the backward), summed
+# over the kernels of the stage, scaled by what the same counters read for a plain 1 GiB device
+# copy (bytes read = FETCH_SIZE KiB x 1024 x 2.0, bytes written = WRITE_SIZE KiB x 1024 x 1.0).
+# Each entry holds the hash of the device sources of the stage's kernels the counters were taken
 # on; once one changes, the figure no longer describes the kernel and the roofline reports
 # traffic as null.
 COUNTER_TRAFFIC = {
-    ("prefill_L128k", "indexer"): ("a2dfea7dbf9d26e9", ('indexer.hip', 'indexer_exact.h', 'common.h'), 492.1e6),
-    ("prefill_L128k", "topk"): ("704189eb74e2fe09", ('topk.hip', 'indexer_exact.h', 'common.h'), 492.7e6),
-    ("prefill_L128k", "sparse_mla"): ("6496f7e28980a049", ('sparse_mla.hip', 'common.h'), 218227.5e6),
-    ("decode_b64_ctx32k", "indexer"): ("a2dfea7dbf9d26e9", ('indexer.hip', 'indexer_exact.h', 'common.h'), 281.4e6),
-    ("decode_b64_ctx32k", "topk"): ("704189eb74e2fe09", ('topk.hip', 'indexer_exact.h', 'common.h'), 9.2e6),
-    ("decode_b64_ctx32k", "sparse_mla"): ("6496f7e28980a049", ('sparse_mla.hip', 'common.h'), 355.9e6),
-    ("paged_decode_b32_ctx4k_128k", "indexer"): ("a2dfea7dbf9d26e9", ('indexer.hip', 'indexer_exact.h', 'common.h'),
-                                                 278.3e6),
-    ("paged_decode_b32_ctx4k_128k", "topk"): ("704189eb74e2fe09", ('topk.hip', 'indexer_exact.h', 'common.h'), 10.7e6),
-    ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("6496f7e28980a049", ('sparse_mla.hip', 'common.h'), 172.9e6),
+    ("prefill_L128k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 508.2e6),
+    ("prefill_L128k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 493.1e6),
+    ("prefill_L128k", "sparse_mla"): ("b5c7495e98bbf7e1", ('sparse_mla.hip', 'common.h'), 219990.5e6),
+    ("decode_b64_ctx32k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 281.4e6),
+    ("decode_b64_ctx32k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 9.2e6),
+    ("decode_b64_ctx32k", "sparse_mla"): ("b5c7495e98bbf7e1", ('sparse_mla.hip', 'common.h'), 280.0e6),
+    ("paged_decode_b32_ctx4k_128k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 278.3e6),
+    ("paged_decode_b32_ctx4k_128k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 10.7e6),
+    ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("b5c7495e98bbf7e1", ('sparse_mla.hip', 'common.h'), 140.3e6),
+    ("paged_prefill_b4_ctx32k_q8k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 922.6e6),
+    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 988.3e6),
+    ("paged_prefill_b4_ctx32k_q8k", "sparse_mla"): ("b5c7495e98bbf7e1", ('sparse_mla.hip', 'common.h'), 10783.8e6),
+    ("prefill_L32k", "mla_bwd_dq"): ("d841631102c38279", ('sparse_mla_bwd.hip', 'common.h'), 5635.5e6),
+    ("prefill_L32k", "mla_bwd_dkv"): ("d841631102c38279", ('sparse_mla_bwd.hip', 'common.h'), 7632.8e6),
+    ("prefill_L32k", "mla_bwd_reduce"): ("d841631102c38279", ('sparse_mla_bwd.hip', 'common.h'), 5010.0e6),
 }
 
 
