@@ -352,7 +352,7 @@ dsa_status dsa_forward_decode_paged(const uint8_t* q_idx, const float* w, const 
  * on until the process ends: a call needing more
  * (dsa_forward_decode_paged_workspace_bytes above 100663296 bytes; 32
  * sequences of up to 131072 tokens with H = 128 and k = 2048 need about
- * 85 MB) returns DSA_ERR_UNSUPPORTED before any launch.  The call allocates
+ * 52 MB) returns DSA_ERR_UNSUPPORTED before any launch.  The call allocates
  * nothing (no hipMalloc, no allocating library routine).  Every call on a GPU
  * shares that GPU's array: calls that overlap on one GPU (different streams
  * or threads) race and give undefined results; calls ordered on one stream

@@ -480,11 +480,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
     over = false;
   }
 
+  // every wave is past its last read of the stages and of qtail: the
+  // epilogue stages the output through them
+  __syncthreads();
   if (!active) return;
   const int head = kHeadsPerWave * wave + hn;
+  const bool head_ok = head < p.H;
+  const int n_heads = min(kHeadsPerWave, p.H - kHeadsPerWave * wave);  // heads of this wave (>= 1)
   const auto lr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(lr[0]) + __uint_as_float(lr[1]);
-  if (head >= p.H) return;
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   const float lse_v = empty ? -INFINITY : (m_ref + log2f(l_tot)) * 0.69314718055994530942f;
@@ -492,13 +496,33 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   auto o4 = [&](int ct, int r4) {
     return (v4f){o[ct][4 * r4], o[ct][4 * r4 + 1], o[ct][4 * r4 + 2], o[ct][4 * r4 + 3]};
   };
+  // The wave's output goes through 32 KB of LDS of its own (a stage, or the
+  // query tail for wave 3): 32 head rows of 1 KB whose 16-byte chunks are
+  // XOR-swizzled by head, so that the writes from the MFMA layout spread over
+  // the banks and each row reads back conflict-free; every global store then
+  // writes 1 KB of one head row.
+  uint8_t* stage = wave == 0 ? kb0 : (wave == 1 ? kb1 : (wave == 2 ? kb2 : reinterpret_cast<uint8_t*>(qtail)));
+  auto chunk = [&](int j, int c) -> uint8_t* { return stage + 1024 * j + 16 * (c ^ (j & 31)); };
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
   if (p.n_split == 1) {
-    float* orow = p.out + (t * p.H + head) * (int64_t)kDv;
+    float* obase = p.out + (t * p.H + kHeadsPerWave * wave) * (int64_t)kDv;
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct)
+    for (int half = 0; half < 2; ++half) {  // dims 256 half .. +255, 4 per chunk
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) *(v4f*)(orow + 32 * ct + 8 * r4 + 4 * hh) = o4(ct, r4) * inv;
-    if (hh == 0) p.lse[t * p.H + head] = lse_v;
+      for (int ct = 0; ct < kCt / 2; ++ct)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(v4f*)chunk(hn, 8 * ct + 2 * r4 + hh) = o4(kCt / 2 * half + ct, r4) * inv;
+      wave_sync();
+      for (int j = 0; j < n_heads; ++j)
+        *(v4f*)(obase + j * (int64_t)kDv + 256 * half + 4 * lane) = *(const v4f*)chunk(j, lane);
+      wave_sync();
+    }
+    if (hh == 0 && head_ok) p.lse[t * p.H + head] = lse_v;
     return;
   }
   // A split's partial: the normalised output in f16, times 2^-e with e >= 0
@@ -516,20 +540,28 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   }
   const int e = (amax > 32768.f && amax < INFINITY) ? ilogbf(amax) - 14 : 0;
   const float sc = inv * ldexpf(1.f, -e);
-  const int64_t prow = (t * p.n_split + sp) * p.H + head;
-  _Float16* orow = reinterpret_cast<_Float16*>(p.part_o) + prow * (int64_t)kDv;
+  const int64_t prow0 = (t * p.n_split + sp) * p.H + kHeadsPerWave * wave;
+  // dims 8 c .. 8 c + 7 of a head row form chunk c; lane (hn, hh) fills half hh
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
-      *(v4h*)(orow + 32 * ct + 8 * r4 + 4 * hh) = __builtin_convertvector(o4(ct, r4) * sc, v4h);
-  if (hh == 0) {
-    p.part_lse[prow] = lse_v;
-    p.part_scale[prow] = ldexpf(1.f, e);
+      *(v4h*)(chunk(hn, 4 * ct + r4) + 8 * hh) = __builtin_convertvector(o4(ct, r4) * sc, v4h);
+  wave_sync();
+  _Float16* pbase = reinterpret_cast<_Float16*>(p.part_o) + prow0 * (int64_t)kDv;
+  for (int j = 0; j < n_heads; ++j)
+    *(v8h*)(pbase + j * (int64_t)kDv + 8 * lane) = *(const v8h*)chunk(j, lane);
+  if (hh == 0 && head_ok) {
+    p.part_lse[prow0 + hn] = lse_v;
+    p.part_scale[prow0 + hn] = ldexpf(1.f, e);
   }
 }
 
-// Merge of split partials; one workgroup of 128 threads per (t, head).
+// Merge of split partials; one workgroup of 128 threads per (t, head).  Every
+// split's lse, scale and partial slice are loaded before any is used (one
+// memory round trip per workgroup), then merged in split order.
+constexpr int kMaxSplits = 16;
+
 __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       const float* __restrict__ part_scale, int64_t T, int32_t H,
@@ -538,23 +570,34 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
   const int64_t th = blockIdx.x;  // t * H + h
   const int64_t t = th / H;
   const int h = (int)(th % H);
-  float mx = -INFINITY;
-  for (int i = 0; i < n_split; ++i) mx = fmaxf(mx, part_lse[(t * n_split + i) * H + h]);
-  float wsum = 0.f;
-  for (int i = 0; i < n_split; ++i) {
-    const float li = part_lse[(t * n_split + i) * H + h];
-    wsum += (li == -INFINITY) ? 0.f : expf(li - mx);
+  float li[kMaxSplits], scl[kMaxSplits];
+  v4h v[kMaxSplits];
+#pragma unroll
+  for (int i = 0; i < kMaxSplits; ++i) {
+    if (i < n_split) {
+      const int64_t prow = (t * n_split + i) * H + h;
+      li[i] = part_lse[prow];
+      scl[i] = part_scale[prow];
+      v[i] = *(const v4h*)(reinterpret_cast<const _Float16*>(part_o) + prow * (int64_t)kDv + 4 * threadIdx.x);
+    }
   }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMaxSplits; ++i)
+    if (i < n_split) mx = fmaxf(mx, li[i]);
+  float wsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxSplits; ++i)
+    if (i < n_split) wsum += (li[i] == -INFINITY) ? 0.f : expf(li[i] - mx);
   const bool empty = !(wsum > 0.f);
   const float lse_tot = empty ? -INFINITY : mx + logf(wsum);
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < n_split; ++i) {
-    const float li = part_lse[(t * n_split + i) * H + h];
-    if (li == -INFINITY) continue;
-    const int64_t prow = (t * n_split + i) * H + h;
-    const float wgt = expf(li - lse_tot) * part_scale[prow];
-    const v4h v = *(const v4h*)(reinterpret_cast<const _Float16*>(part_o) + prow * (int64_t)kDv + 4 * threadIdx.x);
-    acc += wgt * __builtin_convertvector(v, v4f);
+#pragma unroll
+  for (int i = 0; i < kMaxSplits; ++i) {
+    if (i < n_split && li[i] != -INFINITY) {
+      const float wgt = expf(li[i] - lse_tot) * scl[i];
+      acc += wgt * __builtin_convertvector(v[i], v4f);
+    }
   }
   *(v4f*)(out + th * (int64_t)kDv + 4 * threadIdx.x) = acc;
   if (threadIdx.x == 0) lse[th] = lse_tot;
@@ -562,16 +605,17 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
 
 // Each split keeps at least kMinSplitKeys entries: a split's fixed cost (query
 // load, entry resolution, partial write and merge) outweighs further
-// parallelism below that (measured on MI355X, 32 queries x 2048 entries:
-// attention + combine 58 us with 4 splits against 62 us with 8).
-constexpr int kMinSplitKeys = 512;
+// parallelism below that.  Measured on MI355X, 32 queries x 2048 entries:
+// attention + combine 50.3 us with 8 splits against 51.6 us with 4 (with the
+// output staged through LDS and f16 partials; 62 against 58 us before them).
+constexpr int kMinSplitKeys = 256;
 
 int32_t sparse_mla_splits(int64_t T, int32_t /*H*/, int32_t k) {
   if (T >= 256) return 1;
   int64_t s = (256 + T - 1) / T;
   const int64_t max_s = k / kMinSplitKeys;
   if (s > max_s) s = max_s;
-  if (s > 16) s = 16;
+  if (s > kMaxSplits) s = kMaxSplits;
   return (int32_t)(s < 1 ? 1 : s);
 }
 
