@@ -166,6 +166,41 @@ def test_prefill_128k_sampled(dsa):
     _prefill_sampled(dsa, wl.name, rows)
 
 
+# Irregular shapes of the fused prefill against the oracle: a chunk of a
+# sequence at a query offset with head counts that fill no MFMA tile (rows
+# shorter and longer than k), long rows with few heads, k above every row's
+# length (every candidate, in order), and rows over two 8192-key chunks of
+# the scoring pass with 96 heads.
+_SHAPES = [  # N, H_I, H, k, q_pos0, T, rows checked
+    (700, 20, 40, 100, 400, 300, 300),
+    (5000, 4, 8, 2048, 4870, 130, 130),
+    (64, 64, 128, 4096, 0, 64, 64),
+    (9000, 64, 96, 300, 8100, 900, 40),
+]
+
+
+@pytest.mark.parametrize("shape", _SHAPES, ids=[f"N{s[0]}_HI{s[1]}_H{s[2]}_k{s[3]}" for s in _SHAPES])
+def test_fused_prefill_shapes(dsa, shape):
+    N, H_I, H, k, q_pos0, T, n_check = shape
+    wl = configs.Workload(f"prefill_N{N}_H{H}", "prefill", 20 + _SHAPES.index(shape), B=1, N=N, H_I=H_I, H=H, k=k)
+    _case(f"forward_prefill N={N} H_I={H_I} H={H} k={k} rows {q_pos0}..{q_pos0 + T - 1}")
+    inp = device.make_prefill_inputs(wl)  # rows of every position; the call takes rows q_pos0 ..
+    part = dict(inp, q_idx=inp["q_idx"][q_pos0:q_pos0 + T].contiguous(), w=inp["w"][q_pos0:q_pos0 + T].contiguous(),
+                q=inp["q"][q_pos0:q_pos0 + T].contiguous())
+    idx, out, lse = prefill(wl, part, k=k, T=T, q_pos0=q_pos0)
+    rows = np.arange(T)
+    if n_check < T:
+        rng = np.random.default_rng(N)
+        rows = np.unique(np.concatenate([rng.choice(T, n_check - 4, replace=False), [0, 1, T - 2, T - 1]]))
+    g_idx, g_out, g_lse = idx.cpu().numpy()[rows], out.cpu().numpy()[rows], lse.cpu().numpy()[rows]
+    del inp, part, idx, out, lse
+    _free()
+    keys = configs.k_idx_bytes(wl, 0, np.arange(N))
+    results = [oracle.prefill_row(wl, q_pos0 + int(i), keys, k) for i in rows]
+    _check_rows(wl.name, rows, results, g_idx, g_out, g_lse, k,
+                _attn_on(wl, q_pos0 + rows, np.zeros(len(rows), int)))
+
+
 def test_decode_heavy_ties_and_mixed_lengths(dsa):
     """Long decode rows go through the multi-workgroup top-k.  Keys 0..4095 of
     every sequence are equal (one shared score) and the rest are zero (score 0),
