@@ -54,9 +54,9 @@ PEAK_HBM_GBS = 8000.0
 # on; once one changes, the figure no longer describes the kernel and the roofline reports
 # traffic as null.
 COUNTER_TRAFFIC = {
-    ("prefill_L128k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 508.4e6),
-    ("prefill_L128k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 493.1e6),
-    ("prefill_L128k", "sparse_mla"): ("177408750010f1e6", ('sparse_mla.hip', 'common.h'), 216278.8e6),
+    ("prefill_L128k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 1012.0e6),
+    ("prefill_L128k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 992.6e6),
+    ("prefill_L128k", "sparse_mla"): ("177408750010f1e6", ('sparse_mla.hip', 'common.h'), 219735.1e6),
     ("decode_b64_ctx32k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 281.4e6),
     ("decode_b64_ctx32k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 9.2e6),
     ("decode_b64_ctx32k", "sparse_mla"): ("177408750010f1e6", ('sparse_mla.hip', 'common.h'), 278.8e6),

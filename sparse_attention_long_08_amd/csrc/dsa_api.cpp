@@ -125,8 +125,9 @@ size_t mla_ws(int64_t T, int32_t H, int32_t k) {
 }
 
 int64_t prefill_tile_rows(int64_t T, int64_t N) {
-  // score scratch of about 1 GiB (enough rows to fill the GPU, bounded memory)
-  int64_t rows = (int64_t)(((int64_t)1 << 28) / std::max<int64_t>(N, 1));
+  // score scratch of about 2 GiB (fp32 stride): enough rows that the top-k's
+  // last round of workgroups is a small part of a launch, bounded memory
+  int64_t rows = (int64_t)(((int64_t)1 << 29) / std::max<int64_t>(N, 1));
   rows = std::max<int64_t>(rows, 256);
   rows = (rows + 7) / 8 * 8;
   return std::min<int64_t>(rows, std::max<int64_t>(T, 1));
