@@ -51,11 +51,11 @@ PEAK_HBM_GBS = 8000.0
 # over the kernels of the stage, scaled by what the same counters read for a plain 1 GiB device
 # copy (bytes read = FETCH_SIZE KiB x 1024 x 2.0, bytes written = WRITE_SIZE KiB x 1024 x 1.0).
 # Each entry holds the hash of the device sources of the stage's kernels the counters were taken
-# on; once one changes, the figure no longer describes the kernel and the roofline reports
-# traffic as null.
+# on (and of the host code that sizes the prefill's row tiles, where a launch covers one); once
+# one changes, the figure no longer describes the launch and the roofline reports traffic as null.
 COUNTER_TRAFFIC = {
-    ("prefill_L128k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 1012.0e6),
-    ("prefill_L128k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 992.6e6),
+    ("prefill_L128k", "indexer"): ("3b42e8d8b97e80f3", ('indexer.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 1012.0e6),
+    ("prefill_L128k", "topk"): ("61d565f30ad55140", ('topk.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 992.6e6),
     ("prefill_L128k", "sparse_mla"): ("177408750010f1e6", ('sparse_mla.hip', 'common.h'), 219735.1e6),
     ("decode_b64_ctx32k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 281.4e6),
     ("decode_b64_ctx32k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 9.2e6),
@@ -63,8 +63,8 @@ COUNTER_TRAFFIC = {
     ("paged_decode_b32_ctx4k_128k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 278.4e6),
     ("paged_decode_b32_ctx4k_128k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 10.7e6),
     ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("177408750010f1e6", ('sparse_mla.hip', 'common.h'), 194.7e6),
-    ("paged_prefill_b4_ctx32k_q8k", "indexer"): ("66a64f9e9ba0f2fc", ('indexer.hip', 'indexer_exact.h', 'common.h'), 925.2e6),
-    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("76beaf6c9bae61f1", ('topk.hip', 'indexer_exact.h', 'common.h'), 988.0e6),
+    ("paged_prefill_b4_ctx32k_q8k", "indexer"): ("3b42e8d8b97e80f3", ('indexer.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 925.2e6),
+    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("61d565f30ad55140", ('topk.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 988.0e6),
     ("paged_prefill_b4_ctx32k_q8k", "sparse_mla"): ("177408750010f1e6", ('sparse_mla.hip', 'common.h'), 10396.6e6),
     ("prefill_L32k", "mla_bwd_dq"): ("d841631102c38279", ('sparse_mla_bwd.hip', 'common.h'), 5635.5e6),
     ("prefill_L32k", "mla_bwd_dkv"): ("d841631102c38279", ('sparse_mla_bwd.hip', 'common.h'), 7632.8e6),
