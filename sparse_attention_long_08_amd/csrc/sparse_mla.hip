@@ -179,6 +179,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   __shared__ __attribute__((aligned(16))) uint8_t kb2[kBufBytes];
   __shared__ v8bf qtail[kQTail * kWaves * 64];  // query k-steps kQReg..35 of every wave
   __shared__ int32_t rows[kMaxK];                 // latent row of every entry (-1: skipped)
+  __shared__ int32_t wave_last[kWaves];           // last entry with a latent row, per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hn = lane & 31, hh = lane >> 5;  // MFMA column (head) and k-half of this lane
   const int64_t t = blockIdx.x / p.n_split;
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   const bool active = kHeadsPerWave * wave < p.H;
   const int32_t* idx_row = p.idx + t * (int64_t)p.k;
   const int n_ent = j1 > j0 ? j1 - j0 : 0;
-  const int nb = (n_ent + kBlk - 1) / kBlk;
+  const int nb_all = (n_ent + kBlk - 1) / kBlk;
 
   // ---- query rows of this wave's heads in the B layout of the logit
   // MFMA: k-step ks of lane (head hn, half hh) is dims 16*ks + 8*hh .. +7.
@@ -218,7 +219,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   // reads).  Four entries per thread at a time: their index loads, then
   // their page-table loads, each issued together.
   constexpr int kResolve = 4;
-  for (int e0 = 0; e0 < nb * kBlk; e0 += kResolve * kThreads) {
+  int32_t last = -1;
+  for (int e0 = 0; e0 < nb_all * kBlk; e0 += kResolve * kThreads) {
     int32_t sv[kResolve], pe[kResolve];
 #pragma unroll
     for (int u = 0; u < kResolve; ++u) sv[u] = idx_row[j0 + min(e0 + u * kThreads + tid, n_ent - 1)];
@@ -231,14 +233,25 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
 #pragma unroll
     for (int u = 0; u < kResolve; ++u) {
       const int e = e0 + u * kThreads + tid;
-      if (e < nb * kBlk) rows[e] = sv[u] < 0 ? -1 : (int32_t)addr.row_of(b, sv[u], pe[u]);
+      if (e < nb_all * kBlk) {
+        const int32_t rv = sv[u] < 0 ? -1 : (int32_t)addr.row_of(b, sv[u], pe[u]);
+        rows[e] = rv;
+        if (rv >= 0) last = e;  // e grows with u and e0
+      }
     }
   }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) last = max(last, __shfl_xor(last, d, 64));
+  if (lane == 0) wave_last[wave] = last;
 #pragma unroll
   for (int ks = 0; ks < kQReg; ++ks) qf[ks] = q_hv ? qf[ks] : (v8bf){};
 #pragma unroll
   for (int ks = 0; ks < kQTail; ++ks) qtail[(ks * kWaves + wave) * 64 + lane] = q_hv ? qt[ks] : (v8bf){};
   __syncthreads();
+  // Blocks up to the last entry with a latent row: the blocks after it hold
+  // only skipped entries, which add exact zeros (a selection padded with -1
+  // at its end, as for rows with fewer than k candidates, stops early).
+  const int nb = (max(max(wave_last[0], wave_last[1]), max(wave_last[2], wave_last[3])) + kBlk) / kBlk;
 
   // Gather one block into stage `base`: this wave moves rows 8w .. 8w+7, one
   // DMA per band; lane L carries row 8w + L/8, chunk slot L%8 of the band.
