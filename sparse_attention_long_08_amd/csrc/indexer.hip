@@ -21,6 +21,8 @@
 // L x L matrix): the prefill kernel stages 64-key groups in LDS (widened to
 // bf16 once per workgroup) and shares them across the workgroup's query
 // rows; the decode kernel streams each key once from HBM.
+#include <type_traits>
+
 #include "common.h"
 #include "indexer_exact.h"
 #include "launch.h"
@@ -397,9 +399,10 @@ __global__ __launch_bounds__(256) void fp8_row_bounds_kernel(const uint8_t* __re
 }
 
 // Approximate scores of the causal pairs of a 4-row query block (one row per
-// wave) over one chunk of `key_chunk` keys; only candidates (s <= pos) are
+// wave) over one chunk of `key_chunk` keys; the candidates (s <= pos) are
 // written, as f16 I~ * 2^-s (row_scale = 2^s, rounded to nearest) in the
-// first half of each fp32 row of the tile.  64-key groups of FP8 keys are staged in LDS as stored (128-byte
+// first half of each fp32 row of the tile (with up to three slots past the
+// last candidate, inside the row, that nothing reads).  64-key groups of FP8 keys are staged in LDS as stored (128-byte
 // rows whose 16-byte chunks are XOR-swizzled by key, so the operand reads of
 // 16 keys x one chunk are free of bank conflicts) and shared by the 4 rows.
 // Per 16-key block: one 16x16x128 FP8 MFMA per 16-head tile (heads on the
@@ -455,9 +458,17 @@ __global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
   const int st_key = 16 * wave + col;
   auto slot = [](int key, int ch) { return ch ^ ((key >> 1) & 7); };
   // key s of the sequence is row addr.row(0, s); a 64-key group lies in one
-  // page, so one lookup per group (a group without a backing row stages zeros)
+  // page, so one lookup per group (a group without a backing row stages zeros).
+  // Contiguous keys load unpredicated: a key past c_end (only in the chunk's
+  // last group) re-reads key c_end - 1, and its score is never read.
   auto stage_load = [&](int64_t kg, v4i& s0, v4i& s1) {
     const int64_t s = kg + st_key;
+    if constexpr (std::is_same_v<Addr, AddrSingle>) {
+      const v4i* p = (const v4i*)(k_idx + (s < c_end ? s : c_end - 1) * kIdxD + 32 * grp);
+      s0 = p[0];
+      s1 = p[1];
+      return;
+    }
     const int64_t grow = addr.group_row(0, kg);
     if (s < c_end && grow >= 0) {
       const v4i* p = (const v4i*)(k_idx + (grow + st_key) * kIdxD + 32 * grp);
@@ -514,14 +525,9 @@ __global__ __launch_bounds__(256) void indexer_fp8_prefill_kernel(
       _Float16* dst = reinterpret_cast<_Float16*>(scores + r * ld) + s;
       const _Float16 h0 = (_Float16)(d[0] * inv_scale), h1 = (_Float16)(d[1] * inv_scale);
       const _Float16 h2 = (_Float16)(d[2] * inv_scale), h3 = (_Float16)(d[3] * inv_scale);
-      if (s + 3 < nq) {
-        typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-        *(v4h*)dst = (v4h){h0, h1, h2, h3};
-      } else {
-        if (s < nq) dst[0] = h0;
-        if (s + 1 < nq) dst[1] = h1;
-        if (s + 2 < nq) dst[2] = h2;
-      }
+      // a group of four that crosses the row's last candidate is stored
+      // whole: the slots past it lie inside the row's stride and are never read
+      if (s < nq) *(v4h*)dst = (v4h){h0, h1, h2, h3};
     }
     buf ^= 1;
   }
