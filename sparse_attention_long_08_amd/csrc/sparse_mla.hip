@@ -570,28 +570,31 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   }
 }
 
-// Merge of split partials; one workgroup of 128 threads per (t, head).  Every
-// split's lse, scale and partial slice are loaded before any is used (one
-// memory round trip per workgroup), then merged in split order.
+// Merge of split partials; one wave per (t, head), four per workgroup, each
+// lane merging 8 consecutive dims.  Every split's lse, scale and partial
+// slice are loaded before any is used (one memory round trip per wave), then
+// merged in split order.
 constexpr int kMaxSplits = 16;
 
-__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ part_o,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       const float* __restrict__ part_scale, int64_t T, int32_t H,
                                                       int32_t n_split, float* __restrict__ out,
                                                       float* __restrict__ lse) {
-  const int64_t th = blockIdx.x;  // t * H + h
+  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
+  if (th >= T * H) return;
+  const int ln = threadIdx.x & 63;
   const int64_t t = th / H;
   const int h = (int)(th % H);
   float li[kMaxSplits], scl[kMaxSplits];
-  v4h v[kMaxSplits];
+  v8h v[kMaxSplits];
 #pragma unroll
   for (int i = 0; i < kMaxSplits; ++i) {
     if (i < n_split) {
       const int64_t prow = (t * n_split + i) * H + h;
       li[i] = part_lse[prow];
       scl[i] = part_scale[prow];
-      v[i] = *(const v4h*)(reinterpret_cast<const _Float16*>(part_o) + prow * (int64_t)kDv + 4 * threadIdx.x);
+      v[i] = *(const v8h*)(reinterpret_cast<const _Float16*>(part_o) + prow * (int64_t)kDv + 8 * ln);
     }
   }
   float mx = -INFINITY;
@@ -604,16 +607,18 @@ __global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict
     if (i < n_split) wsum += (li[i] == -INFINITY) ? 0.f : expf(li[i] - mx);
   const bool empty = !(wsum > 0.f);
   const float lse_tot = empty ? -INFINITY : mx + logf(wsum);
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
   for (int i = 0; i < kMaxSplits; ++i) {
     if (i < n_split && li[i] != -INFINITY) {
       const float wgt = expf(li[i] - lse_tot) * scl[i];
-      acc += wgt * __builtin_convertvector(v[i], v4f);
+      acc0 += wgt * __builtin_convertvector(v[i].lo, v4f);
+      acc1 += wgt * __builtin_convertvector(v[i].hi, v4f);
     }
   }
-  *(v4f*)(out + th * (int64_t)kDv + 4 * threadIdx.x) = acc;
-  if (threadIdx.x == 0) lse[th] = lse_tot;
+  *(v4f*)(out + th * (int64_t)kDv + 8 * ln) = acc0;
+  *(v4f*)(out + th * (int64_t)kDv + 8 * ln + 4) = acc1;
+  if (ln == 0) lse[th] = lse_tot;
 }
 
 // Each split keeps at least kMinSplitKeys entries: a split's fixed cost (query
@@ -680,7 +685,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
     e = launch_mla(p, ad, st);
   }
   if (e != hipSuccess || p.n_split == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.T * a.H)), dim3(128), 0, st, a.part_o, a.part_lse,
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((a.T * a.H + 3) / 4)), dim3(256), 0, st, a.part_o, a.part_lse,
                      a.part_scale, a.T, a.H, p.n_split, a.out, a.lse);
   return hipGetLastError();
 }
