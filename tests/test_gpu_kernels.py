@@ -274,11 +274,12 @@ def _rand_idx(rng, T, k, n):
     return idx
 
 
-# (3, 2048, 128): 8 splits per query merged by the combine kernel; (3, 1024,
-# 40), (5, 2000, 96) and (2, 777, 8): 4, 7 and 3 splits (the last two with a
-# shorter last split) with head counts that leave waves partly or wholly idle
-@pytest.mark.parametrize("T,k,H", [(3, 2048, 128), (40, 300, 128), (300, 64, 128), (17, 100, 8), (9, 70, 40),
-                                   (3, 1024, 40), (5, 2000, 96), (2, 777, 8)])
+# (3, 2048, 128): 8 splits per query merged by the combine kernel, (2, 4096,
+# 128): the most, 16; (3, 1024, 40), (5, 2000, 96) and (2, 777, 8): 4, 7 and 3
+# splits (the last two with a shorter last split) with head counts that leave
+# waves partly or wholly idle
+@pytest.mark.parametrize("T,k,H", [(3, 2048, 128), (2, 4096, 128), (40, 300, 128), (300, 64, 128), (17, 100, 8),
+                                   (9, 70, 40), (3, 1024, 40), (5, 2000, 96), (2, 777, 8)])
 def test_sparse_mla_against_oracle(dsa, T, k, H):
     name = "tiny_prefill_L256" if H == 8 else "prefill_L32k"
     wl0 = configs.WORKLOADS[name]
