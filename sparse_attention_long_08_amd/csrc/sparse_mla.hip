@@ -33,10 +33,13 @@
 // loop; if a later block max exceeds the reference by more than 2^64 the
 // query is recomputed with the true max, which the first pass tracked.  The
 // gather uses the buffer-addressed form of the DMA when the latent cache
-// spans less than 4 GiB.
+// spans less than 4 GiB.  A query's blocks end at its last entry with a
+// latent row.  The output goes through LDS on its way out, so that every
+// store instruction writes 1 KB of one head row.
 //
 // Small batches (decode) split each query's k entries over several
-// workgroups; partial (out, lse) pairs are merged exactly by combine_kernel:
+// workgroups; the partial (out, lse) pairs, out stored in f16 with a
+// power-of-two scale per row, are merged by combine_kernel:
 // lse = ln sum_i e^{lse_i}, out = sum_i e^{lse_i - lse} out_i.
 #include <type_traits>
 
