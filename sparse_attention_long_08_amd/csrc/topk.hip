@@ -33,7 +33,14 @@ namespace dsa {
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kTopkCap = 3584;  // LDS candidate list capacity (two workgroups fit a CU)
-constexpr int kSampleStride = 16;   // the sample reads one 64-key chunk in 16
+// The sampled estimate reads one 64-key chunk in kSampleStride of the fp32
+// rows (the plain and the multi-workgroup top-k) and one in kSampleStrideH of
+// the fused prefill's f16 rows.  Measured on MI355X: a 1-in-32 sample took the
+// decode top-k from 29.6 to 28.2 us (64 rows of 32K) and from 44.2 to 38.3 us
+// (32 rows of 4K..128K), while the band top-k of the 128K prefill took 19.5
+// against 18.6 ms with it, so the f16 rows keep 1 in 16.
+constexpr int kSampleStride = 32;
+constexpr int kSampleStrideH = 16;
 constexpr int kSampleMinN = 8192;   // shorter rows take the exact path
 
 struct TopkShared {
@@ -343,9 +350,10 @@ __device__ __forceinline__ uint32_t select_in_list(TopkShared& sh, int nl, const
 // nothing, when the gathered list misses [k, capacity]; the caller then takes
 // the exact path.  Needs a 16-byte aligned row with n >= kSampleMinN; the
 // bitmap area (n_words * 8 bytes >= n / 4 bytes) doubles as the sample buffer.
-// The sampled threshold estimate: 1/16 of the row (64-key chunks spread
-// over the whole row) is read into `sample` (at least n/4 + 240 bytes of
-// LDS) and its exact r-th largest key returned, with r chosen so that about
+// The sampled threshold estimate: one 64-key chunk in kSampleStride of the
+// row (chunks spread over the whole row) is read into `sample` (at most n/4
+// + 240 bytes of LDS, for the f16 rows' 1 in 16) and its exact r-th largest
+// key returned, with r chosen so that about
 // target_eighths / 8 of k keys of the full row are expected at or above it.
 // Needs a 16-byte aligned row with n >= kSampleMinN.
 // The estimate from the m sampled keys of a row of n: the key of sample rank
@@ -363,7 +371,7 @@ __device__ __forceinline__ uint32_t sample_select(TopkShared& sh, int m, int64_t
 __device__ __forceinline__ uint32_t sample_estimate(TopkShared& sh, const float* __restrict__ row, int64_t n,
                                                     int32_t k, uint32_t* sample, int32_t target_eighths = 11) {
   const int tid = threadIdx.x;
-  // sampled chunk j: keys 64*(16*j + (5*j % 16)) .. +63, whole chunks inside the row
+  // sampled chunk j: keys 64*(S*j + (5*j % S)) .. +63 with S = kSampleStride, whole chunks inside the row
   const int64_t n_chunks = n / 64;
   const int m_chunks = (int)((n_chunks + kSampleStride - 1) / kSampleStride);
   int m = 0;  // sampled keys (a multiple of 64, counted by every thread alike)
@@ -386,18 +394,18 @@ __device__ __forceinline__ uint32_t sample_estimate(TopkShared& sh, const float*
   return sample_select(sh, m, n, k, sample, target_eighths);
 }
 
-// sample_estimate over an f16 tile row (16-byte aligned): the same chunks.
+// sample_estimate over an f16 tile row (16-byte aligned), one chunk in kSampleStrideH.
 __device__ __forceinline__ uint32_t sample_estimate_h(TopkShared& sh, const _Float16* __restrict__ row, float scale,
                                                       int64_t n, int32_t k, uint32_t* sample, int32_t target_eighths) {
   const int tid = threadIdx.x;
   const int64_t n_chunks = n / 64;
-  const int m_chunks = (int)((n_chunks + kSampleStride - 1) / kSampleStride);
+  const int m_chunks = (int)((n_chunks + kSampleStrideH - 1) / kSampleStrideH);
   int m = 0;
   for (int j = 0; j < m_chunks; ++j)
-    if ((int64_t)kSampleStride * j + (5 * j) % kSampleStride < n_chunks) m += 64;
+    if ((int64_t)kSampleStrideH * j + (5 * j) % kSampleStrideH < n_chunks) m += 64;
   for (int f = tid; f < m_chunks * 8; f += kTopkThreads) {
     const int j = f >> 3;
-    const int64_t chunk = (int64_t)kSampleStride * j + (5 * j) % kSampleStride;
+    const int64_t chunk = (int64_t)kSampleStrideH * j + (5 * j) % kSampleStrideH;
     if (chunk < n_chunks) {
       const v8h v = *(const v8h*)(row + 64 * chunk + 8 * (f & 7));
       uint32_t* dst = sample + 64 * j + 8 * (f & 7);

@@ -207,17 +207,19 @@ def _topk_rows():
     rows.append(("short", rng.standard_normal(100)))
     rows.append(("one", np.array([2.0])))
     rows.append(("quantised_ties", np.round(rng.standard_normal(65536) * 4) / 4))
-    # rows built to mislead a 1-in-16 chunk sample of the row (64-key chunks
-    # 16*j + (5*j % 16)): large values only inside, or only outside, those
+    # rows built to mislead a 1-in-S chunk sample of the row (64-key chunks
+    # S*j + (5*j % S), S = 32 for these fp32 rows and 16 for the fused
+    # prefill's f16 rows): large values only inside, or only outside, those
     # chunks, so an estimated threshold is far too high or far too low
     n = 65536
-    inside = np.zeros(n, dtype=bool)
-    for j in range(n // 64 // 16):
-        c = 16 * j + (5 * j) % 16
-        inside[64 * c:64 * c + 64] = True
-    x = rng.standard_normal(n)
-    rows.append(("sample_biased_high", np.where(inside, x + 100.0, x)))
-    rows.append(("sample_biased_low", np.where(inside, x, x + 100.0)))
+    for S in (32, 16):
+        inside = np.zeros(n, dtype=bool)
+        for j in range(n // 64 // S):
+            c = S * j + (5 * j) % S
+            inside[64 * c:64 * c + 64] = True
+        x = rng.standard_normal(n)
+        rows.append((f"sample{S}_biased_high", np.where(inside, x + 100.0, x)))
+        rows.append((f"sample{S}_biased_low", np.where(inside, x, x + 100.0)))
     return rows
 
 
