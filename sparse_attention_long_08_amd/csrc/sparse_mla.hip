@@ -161,6 +161,17 @@ struct MlaParams {
   float* part_scale;
 };
 
+// Workgroups are handed to the eight XCDs in turn (workgroup b to XCD b % 8),
+// and each XCD has an L2 of its own.  This numbering gives XCD x one
+// contiguous run of the G logical workgroups, so that the splits of one query
+// (every one of which loads the query's rows) and the merge of their partials
+// run on one XCD.  It is a bijection of [0, G): XCD x receives the
+// q + (x < r) workgroups b = x, x + 8, ... (G = 8q + r).
+__device__ __forceinline__ int64_t xcd_major(int64_t b, int64_t G) {
+  const int64_t x = b & 7, i = b >> 3, q = G >> 3, r = G & 7;
+  return x * q + (x < r ? x : r) + i;
+}
+
 // Drives the pipeline over the three stage buffers.  They arrive as
 // restrict-qualified parameters: after inlining, every access through them
 // carries alias-scope metadata, which lets the compiler see that the stages
@@ -185,8 +196,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams p, Ad
   __shared__ int32_t wave_last[kWaves];           // last entry with a latent row, per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hn = lane & 31, hh = lane >> 5;  // MFMA column (head) and k-half of this lane
-  const int64_t t = blockIdx.x / p.n_split;
-  const int sp = blockIdx.x % p.n_split;
+  // split queries: XCD-major numbering (one query's splits on one XCD)
+  const int64_t wg = p.n_split > 1 ? xcd_major(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
+  const int64_t t = wg / p.n_split;
+  const int sp = (int)(wg % p.n_split);
   const int j0 = sp * p.per_split;
   const int j1 = min(j0 + p.per_split, p.k);
   const int64_t b = p.seq_per_query ? t : 0;
@@ -584,7 +597,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ part_scale, int64_t T, int32_t H,
                                                       int32_t n_split, float* __restrict__ out,
                                                       float* __restrict__ lse) {
-  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * H + h
+  // XCD-major like the split attention: a query's merge runs on the XCD that wrote its partials
+  const int64_t th = xcd_major(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);  // t * H + h
   if (th >= T * H) return;
   const int ln = threadIdx.x & 63;
   const int64_t t = th / H;
