@@ -994,6 +994,14 @@ def bench_decode(args, wl):
         "roofline": {"kernel": dom, "bound": bound, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": ach / PEAK_HBM_GBS, "traffic": counter_traffic(wl.name, dom), "launches_per_step": 1,
                      "avg_launch_ms": stage_ms[dom]},
+        # every stage against the HBM peak: `achieved` from its algorithmic bytes, `counter_gbs` from the
+        # bytes the HBM counters read for it (the key stream of the indexer, the gather of the attention)
+        "stage_rooflines": {kk: {"bound": b, "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": a / PEAK_HBM_GBS, "traffic": counter_traffic(wl.name, kk),
+                                 "counter_gbs": (None if counter_traffic(wl.name, kk) is None
+                                                 else counter_traffic(wl.name, kk) / (stage_ms[kk] * 1e-3) / 1e9),
+                                 "launches_per_step": 1}
+                            for kk, (b, a) in kernels.items()},
         "stages_ms": stage_ms,
         "path_roofline": {"t_roof_ms": t_roof * 1e3, "algorithmic_bytes": total_bytes,
                           "frac": t_roof * 1e3 / ms_per_step},
