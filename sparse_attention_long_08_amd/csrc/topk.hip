@@ -24,6 +24,8 @@
 // "key > theta" and "key == theta"; one block scan over the bitmaps gives each
 // selected position its output slot (the lowest-position ties are the first r
 // "== theta" bits), so the output is ascending with no sort.
+#include <atomic>
+
 #include "common.h"
 #include "indexer_exact.h"
 #include "launch.h"
@@ -567,6 +569,28 @@ __global__ __launch_bounds__(NTH) void topk_kernel(const float* __restrict__ sco
   Ops::topk_exact_row(sh, row, n, vec, k, gt_bits, eq_bits, n_words, out);
 }
 
+// Every kernel here takes up to kTopkLdsCap bytes of dynamic LDS: the fixed
+// state and the two bitmaps of a 262144-key row.
+constexpr int kTopkLdsCap = (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192 + 256);
+
+// Raises the dynamic-LDS limit of the given kernels to kTopkLdsCap on the
+// current device, once per device (the limit is a per-device attribute): the
+// device's bit in `done` records it, so concurrent callers at worst set it
+// twice.  Devices past the 64th set it on every call.
+inline hipError_t lds_limit_once(std::atomic<uint64_t>& done, std::initializer_list<const void*> kernels) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  for (const void* fn : kernels) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kTopkLdsCap);
+    if (e != hipSuccess) return e;
+  }
+  if (bit) done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
+
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, int64_t q_pos0,
                        const int32_t* n_valid, int32_t k, int32_t* idx, hipStream_t st) {
   if (T <= 0) return hipSuccess;
@@ -574,18 +598,10 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t T, int64_t N, in
   // bitmaps (2 x n_words words) + 256 bytes: the sampled path's key sample
   // (at most n/4 + 240 bytes) reuses the bitmap area
   const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words + 256;
-  static bool attr_set = false;
-  if (!attr_set) {
-    // rows up to 262144 keys: fixed state + 64 KiB of bitmaps
-    const int cap = (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192 + 256);
-    hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<kTopkThreads>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)topk_kernel<kTopkWideThreads>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              cap);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = lds_limit_once(lds_set, {(const void*)topk_kernel<kTopkThreads>,
+                                              (const void*)topk_kernel<kTopkWideThreads>}))
+    return e;
   // Few rows (decode) leave most compute units idle: each row's workgroup is
   // alone on its compute unit, so it takes twice the threads (measured on
   // MI355X: 64 rows of 32K keys 28.7 -> 26.8 us).
@@ -765,17 +781,10 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int64_t T, int64_t 
   // the estimate's sample (at most n/4 + 240 bytes) and the finish's bitmaps
   // (2 x n_words words) both fit the same dynamic LDS as topk_kernel
   const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words + 256;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const int cap = (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192 + 256);
-    hipError_t e = hipFuncSetAttribute((const void*)topk_rows_finish_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)topk_rows_estimate_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              cap);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = lds_limit_once(lds_set, {(const void*)topk_rows_finish_kernel,
+                                              (const void*)topk_rows_estimate_kernel}))
+    return e;
   hipLaunchKernelGGL(topk_rows_estimate_kernel, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, N,
                      n_valid, k, meta);
   hipLaunchKernelGGL(topk_rows_collect_kernel, dim3((unsigned)n_chunks, (unsigned)T), dim3(256), 0, st, scores, ld,
@@ -1089,13 +1098,8 @@ hipError_t topk_band_nt(float* scores, int64_t ld, int64_t T, int64_t N, int64_t
                         const BandArgs& ba, hipStream_t st) {
   const int32_t n_words = (int32_t)((N + 31) / 32);
   const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words + 256;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_band_kernel<NT, kPaged>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(sizeof(TopkShared) + sizeof(uint32_t) * 2 * 8192 + 256));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = lds_limit_once(lds_set, {(const void*)topk_band_kernel<NT, kPaged>})) return e;
   hipLaunchKernelGGL((topk_band_kernel<NT, kPaged>), dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, T, N, q_pos0,
                      k, idx, n_words, ba);
   return hipGetLastError();
