@@ -222,6 +222,76 @@ static __device__ __forceinline__ void scan_row_h(const _Float16* __restrict__ r
   for (int64_t s = n8 + tid; s < n; s += NTH) fn(s, h_key(row[s], scale));
 }
 
+// Appends to the LDS list every key >= cut of such a row, with its position
+// (slots from kTopkCap on are counted in list_n but not written), as the
+// candidate passes do.  In the unrolled part each thread keeps the keys of
+// its 32-key batch in registers and marks those to append; one wave prefix
+// count of the marks (six ballots) and one LDS atomic per wave and batch then
+// give every thread its slots, where an append per key position would wait
+// for an LDS atomic at nearly every position (some lane of 64 usually holds
+// a key above the cut).  Measured on MI355X: band top-k 17.4 -> 16.8 ms per
+// 128K prefill step, 5.23 -> 5.14 ms per chunked paged prefill call.
+// Expects list_n set and a barrier before the call.
+static __device__ __forceinline__ void gather_ge_h(TopkShared& sh, const _Float16* __restrict__ row, float scale,
+                                                   int64_t n, uint32_t cut) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  constexpr int kU = 4;
+  constexpr int64_t kStep = 8 * NTH;
+  const int64_t nU = n / (kU * kStep) * (kU * kStep);
+  // every thread runs the same number of these iterations (whole waves active)
+  for (int64_t s0 = 8 * (int64_t)tid; s0 < nU; s0 += kU * kStep) {
+    v8h v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = *(const v8h*)(row + s0 + u * kStep);
+    uint32_t key[kU * 8], m = 0u;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        key[u * 8 + j] = h_key(v[u][j], scale);
+        m |= (key[u * 8 + j] >= cut ? 1u : 0u) << (u * 8 + j);
+      }
+    const uint32_t cnt = __popc(m);
+    uint32_t pre = 0u, tot = 0u;  // marks of the lower lanes, and of the wave
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+      const uint64_t bal = __ballot((cnt >> b) & 1u);
+      pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) << b;
+      tot += (uint32_t)__popcll(bal) << b;
+    }
+    if (tot == 0u) continue;  // uniform across the wave
+    uint32_t base = 0u;
+    if (lane == 0) base = atomicAdd(&sh.list_n, tot);
+    uint32_t slot = __builtin_amdgcn_readfirstlane(base) + pre;
+#pragma unroll
+    for (int j = 0; j < kU * 8; ++j) {
+      if (m & (1u << j)) {
+        if (slot < (uint32_t)kTopkCap) {
+          sh.list_key[slot] = key[j];
+          sh.list_idx[slot] = (int32_t)(s0 + (j >> 3) * kStep + (j & 7));
+        }
+        ++slot;
+      }
+    }
+  }
+  auto one = [&](int64_t s, uint32_t k1) {
+    if (k1 >= cut) {
+      const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+      if (slot < (uint32_t)kTopkCap) {
+        sh.list_key[slot] = k1;
+        sh.list_idx[slot] = (int32_t)s;
+      }
+    }
+  };
+  const int64_t n8 = n & ~(int64_t)7;
+  for (int64_t s = nU + 8 * (int64_t)tid; s < n8; s += kStep) {
+    const v8h v = *(const v8h*)(row + s);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) one(s + j, h_key(v[j], scale));
+  }
+  for (int64_t s = n8 + tid; s < n; s += NTH) one(s, h_key(row[s], scale));
+}
+
 
 // Ordered emit: positions whose gt bit is set, plus the lowest-position
 // (k - #gt) positions whose eq bit is set, in ascending order.
@@ -994,15 +1064,7 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const _Float16* __re
     const uint32_t t_est = TopkOps<kTopkThreads>::sample_estimate_h(sh, row, scale, n, k, gt_bits, 12);
     if (tid == 0) sh.list_n = 0;
     __syncthreads();
-    scan([&](int64_t s, uint32_t key) {
-      if (key >= t_est) {
-        const uint32_t slot = atomicAdd(&sh.list_n, 1u);
-        if (slot < (uint32_t)kTopkCap) {
-          sh.list_key[slot] = key;
-          sh.list_idx[slot] = (int32_t)s;
-        }
-      }
-    });
+    TopkOps<kTopkThreads>::gather_ge_h(sh, row, scale, n, t_est);
     __syncthreads();
     const uint32_t c = sh.list_n;
     if (c >= (uint32_t)k && c <= (uint32_t)kTopkCap) {
@@ -1030,15 +1092,7 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const _Float16* __re
   if (!(have_list && key_lcut >= t_low)) {
     if (tid == 0) sh.list_n = 0;
     __syncthreads();
-    scan([&](int64_t s, uint32_t key) {
-      if (key >= key_lcut) {
-        const uint32_t slot = atomicAdd(&sh.list_n, 1u);
-        if (slot < (uint32_t)kTopkCap) {
-          sh.list_key[slot] = key;
-          sh.list_idx[slot] = (int32_t)s;
-        }
-      }
-    });
+    TopkOps<kTopkThreads>::gather_ge_h(sh, row, scale, n, key_lcut);
     __syncthreads();
     if (sh.list_n > (uint32_t)kTopkCap) return false;  // uniform across the workgroup
   }
