@@ -76,6 +76,20 @@ struct TopkShared {
 // a key is that of the fp32 value f16 * 2^s, which is exact.
 __device__ __forceinline__ uint32_t h_key(_Float16 h, float scale) { return order_key((float)h * scale); }
 
+// Keys sampled from a row of n_chunks whole 64-key chunks when chunk
+// S * j + (5 j mod S) is read for every j < ceil(n_chunks / S) that lies in
+// the row: all but the last such j give chunks below S * (ceil(n_chunks / S) - 1),
+// which is at most n_chunks - 1, so only the last needs the test.  (Counted
+// chunk by chunk, ceil(n_chunks / S) serial steps ran ahead of the sample's
+// loads: measured on MI355X, band top-k 16.6 -> 15.5 ms per 128K prefill
+// step, decode top-k 24.3 -> 23.0 us on 64 x 32K and 36.7 -> 33.9 us paged.)
+__device__ __forceinline__ int sampled_keys(int64_t n_chunks, int S) {
+  const int64_t mc = (n_chunks + S - 1) / S;
+  if (mc == 0) return 0;
+  const int64_t j = mc - 1;
+  return 64 * (int)(j + (S * j + (5 * j) % S < n_chunks ? 1 : 0));
+}
+
 // Radix levels: 0 -> key bits 31..20, 1 -> bits 19..8, 2 -> bits 7..0.
 __device__ __forceinline__ int level_shift(int level) { return level == 0 ? 20 : (level == 1 ? 8 : 0); }
 __device__ __forceinline__ int level_bits(int level) { return level == 2 ? 8 : 12; }
@@ -222,6 +236,80 @@ static __device__ __forceinline__ void scan_row_h(const _Float16* __restrict__ r
   for (int64_t s = n8 + tid; s < n; s += NTH) fn(s, h_key(row[s], scale));
 }
 
+// Appends the B keys of this thread's batch whose bits are set in m to the
+// LDS list, at slots from one LDS atomic per wave: the wave's exclusive
+// prefix of the per-thread counts comes from six ballots (counts < 64).  Every
+// lane of the wave must call it; pos(j) is the row position of key j.
+template <int B, class Pos>
+static __device__ __forceinline__ void append_marked(TopkShared& sh, const uint32_t (&key)[B], uint32_t m, Pos&& pos) {
+  static_assert(B <= 32, "one 32-bit mark word per batch");
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t cnt = __popc(m);
+  uint32_t pre = 0u, tot = 0u;  // marks of the lower lanes, and of the wave
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const uint64_t bal = __ballot((cnt >> b) & 1u);
+    pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) << b;
+    tot += (uint32_t)__popcll(bal) << b;
+  }
+  if (tot == 0u) return;  // uniform across the wave
+  uint32_t base = 0u;
+  if (lane == 0) base = atomicAdd(&sh.list_n, tot);
+  uint32_t slot = __builtin_amdgcn_readfirstlane(base) + pre;
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    if (m & (1u << j)) {
+      if (slot < (uint32_t)kTopkCap) {
+        sh.list_key[slot] = key[j];
+        sh.list_idx[slot] = (int32_t)pos(j);
+      }
+      ++slot;
+    }
+  }
+}
+
+// The same append for a 16-byte aligned fp32 row: batches of 16 keys per
+// thread (four 16-byte loads in flight), the tail key by key.  Measured on
+// MI355X: decode top-k 23.0 -> 22.7 us on 64 x 32K.
+static __device__ __forceinline__ void gather_ge_f(TopkShared& sh, const float* __restrict__ row, int64_t n,
+                                                   uint32_t cut) {
+  const int tid = threadIdx.x;
+  constexpr int kU = 4;
+  constexpr int64_t kStep = 4 * NTH;
+  const int64_t nU = n / (kU * kStep) * (kU * kStep);
+  // every thread runs the same number of these iterations (whole waves active)
+  for (int64_t s0 = 4 * (int64_t)tid; s0 < nU; s0 += kU * kStep) {
+    v4f v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = *(const v4f*)(row + s0 + u * kStep);
+    uint32_t key[kU * 4], m = 0u;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        key[u * 4 + j] = order_key(v[u][j]);
+        m |= (key[u * 4 + j] >= cut ? 1u : 0u) << (u * 4 + j);
+      }
+    append_marked<kU * 4>(sh, key, m, [&](int j) { return s0 + (j >> 2) * kStep + (j & 3); });
+  }
+  auto one = [&](int64_t s, uint32_t k1) {
+    if (k1 >= cut) {
+      const uint32_t slot = atomicAdd(&sh.list_n, 1u);
+      if (slot < (uint32_t)kTopkCap) {
+        sh.list_key[slot] = k1;
+        sh.list_idx[slot] = (int32_t)s;
+      }
+    }
+  };
+  const int64_t n4 = n & ~(int64_t)3;
+  for (int64_t s = nU + 4 * (int64_t)tid; s < n4; s += kStep) {
+    const v4f v = *(const v4f*)(row + s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) one(s + j, order_key(v[j]));
+  }
+  for (int64_t s = n4 + tid; s < n; s += NTH) one(s, order_key(row[s]));
+}
+
 // Appends to the LDS list every key >= cut of such a row, with its position
 // (slots from kTopkCap on are counted in list_n but not written), as the
 // candidate passes do.  In the unrolled part each thread keeps the keys of
@@ -234,7 +322,7 @@ static __device__ __forceinline__ void scan_row_h(const _Float16* __restrict__ r
 // Expects list_n set and a barrier before the call.
 static __device__ __forceinline__ void gather_ge_h(TopkShared& sh, const _Float16* __restrict__ row, float scale,
                                                    int64_t n, uint32_t cut) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int tid = threadIdx.x;
   constexpr int kU = 4;
   constexpr int64_t kStep = 8 * NTH;
   const int64_t nU = n / (kU * kStep) * (kU * kStep);
@@ -251,28 +339,7 @@ static __device__ __forceinline__ void gather_ge_h(TopkShared& sh, const _Float1
         key[u * 8 + j] = h_key(v[u][j], scale);
         m |= (key[u * 8 + j] >= cut ? 1u : 0u) << (u * 8 + j);
       }
-    const uint32_t cnt = __popc(m);
-    uint32_t pre = 0u, tot = 0u;  // marks of the lower lanes, and of the wave
-#pragma unroll
-    for (int b = 0; b < 6; ++b) {
-      const uint64_t bal = __ballot((cnt >> b) & 1u);
-      pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) << b;
-      tot += (uint32_t)__popcll(bal) << b;
-    }
-    if (tot == 0u) continue;  // uniform across the wave
-    uint32_t base = 0u;
-    if (lane == 0) base = atomicAdd(&sh.list_n, tot);
-    uint32_t slot = __builtin_amdgcn_readfirstlane(base) + pre;
-#pragma unroll
-    for (int j = 0; j < kU * 8; ++j) {
-      if (m & (1u << j)) {
-        if (slot < (uint32_t)kTopkCap) {
-          sh.list_key[slot] = key[j];
-          sh.list_idx[slot] = (int32_t)(s0 + (j >> 3) * kStep + (j & 7));
-        }
-        ++slot;
-      }
-    }
+    append_marked<kU * 8>(sh, key, m, [&](int j) { return s0 + (j >> 3) * kStep + (j & 7); });
   }
   auto one = [&](int64_t s, uint32_t k1) {
     if (k1 >= cut) {
@@ -509,9 +576,7 @@ static __device__ __forceinline__ uint32_t sample_estimate(TopkShared& sh, const
   // sampled chunk j: keys 64*(S*j + (5*j % S)) .. +63 with S = kSampleStride, whole chunks inside the row
   const int64_t n_chunks = n / 64;
   const int m_chunks = (int)((n_chunks + kSampleStride - 1) / kSampleStride);
-  int m = 0;  // sampled keys (a multiple of 64, counted by every thread alike)
-  for (int j = 0; j < m_chunks; ++j)
-    if ((int64_t)kSampleStride * j + (5 * j) % kSampleStride < n_chunks) m += 64;
+  const int m = sampled_keys(n_chunks, kSampleStride);  // a multiple of 64
   for (int f = tid; f < m_chunks * 16; f += NTH) {
     const int j = f >> 4;
     const int64_t chunk = (int64_t)kSampleStride * j + (5 * j) % kSampleStride;
@@ -535,9 +600,7 @@ static __device__ __forceinline__ uint32_t sample_estimate_h(TopkShared& sh, con
   const int tid = threadIdx.x;
   const int64_t n_chunks = n / 64;
   const int m_chunks = (int)((n_chunks + kSampleStrideH - 1) / kSampleStrideH);
-  int m = 0;
-  for (int j = 0; j < m_chunks; ++j)
-    if ((int64_t)kSampleStrideH * j + (5 * j) % kSampleStrideH < n_chunks) m += 64;
+  const int m = sampled_keys(n_chunks, kSampleStrideH);
   for (int f = tid; f < m_chunks * 8; f += NTH) {
     const int j = f >> 3;
     const int64_t chunk = (int64_t)kSampleStrideH * j + (5 * j) % kSampleStrideH;
@@ -560,15 +623,7 @@ static __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float*
 
   if (tid == 0) sh.list_n = 0;
   __syncthreads();
-  scan_row(row, n, true, [&](int64_t s, uint32_t key) {
-    if (key >= t_est) {
-      const uint32_t slot = atomicAdd(&sh.list_n, 1u);
-      if (slot < (uint32_t)kTopkCap) {
-        sh.list_key[slot] = key;
-        sh.list_idx[slot] = (int32_t)s;
-      }
-    }
-  });
+  gather_ge_f(sh, row, n, t_est);
   __syncthreads();
   const uint32_t c = sh.list_n;
   if (c < (uint32_t)k || c > (uint32_t)kTopkCap) return false;  // uniform across the workgroup
