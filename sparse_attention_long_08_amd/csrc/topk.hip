@@ -94,6 +94,40 @@ __device__ __forceinline__ int sampled_keys(int64_t n_chunks, int S) {
 __device__ __forceinline__ int level_shift(int level) { return level == 0 ? 20 : (level == 1 ? 8 : 0); }
 __device__ __forceinline__ int level_bits(int level) { return level == 2 ? 8 : 12; }
 
+// Appends the B keys of this thread's batch whose bits are set in m, with
+// their positions pos(j), to a list in LDS (keys[], idxs[], its length in
+// *count; slots from cap on are counted but not written), at slots from one
+// LDS atomic per wave: the wave's exclusive prefix of the per-thread counts
+// comes from six ballots (counts < 64).  Every lane of the wave must call it.
+template <int B, class Pos>
+__device__ __forceinline__ void append_marked(uint32_t* count, uint32_t* keys, int32_t* idxs, uint32_t cap,
+                                              const uint32_t (&key)[B], uint32_t m, Pos&& pos) {
+  static_assert(B <= 32, "one 32-bit mark word per batch");
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t cnt = __popc(m);
+  uint32_t pre = 0u, tot = 0u;  // marks of the lower lanes, and of the wave
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const uint64_t bal = __ballot((cnt >> b) & 1u);
+    pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) << b;
+    tot += (uint32_t)__popcll(bal) << b;
+  }
+  if (tot == 0u) return;  // uniform across the wave
+  uint32_t base = 0u;
+  if (lane == 0) base = atomicAdd(count, tot);
+  uint32_t slot = __builtin_amdgcn_readfirstlane(base) + pre;
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    if (m & (1u << j)) {
+      if (slot < cap) {
+        keys[slot] = key[j];
+        idxs[slot] = (int32_t)pos(j);
+      }
+      ++slot;
+    }
+  }
+}
+
 // The per-row selection steps, for a workgroup of NTH threads (every thread
 // of the workgroup calls them together).
 template <int NTH>
@@ -236,38 +270,6 @@ static __device__ __forceinline__ void scan_row_h(const _Float16* __restrict__ r
   for (int64_t s = n8 + tid; s < n; s += NTH) fn(s, h_key(row[s], scale));
 }
 
-// Appends the B keys of this thread's batch whose bits are set in m to the
-// LDS list, at slots from one LDS atomic per wave: the wave's exclusive
-// prefix of the per-thread counts comes from six ballots (counts < 64).  Every
-// lane of the wave must call it; pos(j) is the row position of key j.
-template <int B, class Pos>
-static __device__ __forceinline__ void append_marked(TopkShared& sh, const uint32_t (&key)[B], uint32_t m, Pos&& pos) {
-  static_assert(B <= 32, "one 32-bit mark word per batch");
-  const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t cnt = __popc(m);
-  uint32_t pre = 0u, tot = 0u;  // marks of the lower lanes, and of the wave
-#pragma unroll
-  for (int b = 0; b < 6; ++b) {
-    const uint64_t bal = __ballot((cnt >> b) & 1u);
-    pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) << b;
-    tot += (uint32_t)__popcll(bal) << b;
-  }
-  if (tot == 0u) return;  // uniform across the wave
-  uint32_t base = 0u;
-  if (lane == 0) base = atomicAdd(&sh.list_n, tot);
-  uint32_t slot = __builtin_amdgcn_readfirstlane(base) + pre;
-#pragma unroll
-  for (int j = 0; j < B; ++j) {
-    if (m & (1u << j)) {
-      if (slot < (uint32_t)kTopkCap) {
-        sh.list_key[slot] = key[j];
-        sh.list_idx[slot] = (int32_t)pos(j);
-      }
-      ++slot;
-    }
-  }
-}
-
 // The same append for a 16-byte aligned fp32 row: batches of 16 keys per
 // thread (four 16-byte loads in flight), the tail key by key.  Measured on
 // MI355X: decode top-k 23.0 -> 22.7 us on 64 x 32K.
@@ -290,7 +292,8 @@ static __device__ __forceinline__ void gather_ge_f(TopkShared& sh, const float* 
         key[u * 4 + j] = order_key(v[u][j]);
         m |= (key[u * 4 + j] >= cut ? 1u : 0u) << (u * 4 + j);
       }
-    append_marked<kU * 4>(sh, key, m, [&](int j) { return s0 + (j >> 2) * kStep + (j & 3); });
+    append_marked<kU * 4>(&sh.list_n, sh.list_key, sh.list_idx, (uint32_t)kTopkCap, key, m,
+                          [&](int j) { return s0 + (j >> 2) * kStep + (j & 3); });
   }
   auto one = [&](int64_t s, uint32_t k1) {
     if (k1 >= cut) {
@@ -339,7 +342,8 @@ static __device__ __forceinline__ void gather_ge_h(TopkShared& sh, const _Float1
         key[u * 8 + j] = h_key(v[u][j], scale);
         m |= (key[u * 8 + j] >= cut ? 1u : 0u) << (u * 8 + j);
       }
-    append_marked<kU * 8>(sh, key, m, [&](int j) { return s0 + (j >> 3) * kStep + (j & 7); });
+    append_marked<kU * 8>(&sh.list_n, sh.list_key, sh.list_idx, (uint32_t)kTopkCap, key, m,
+                          [&](int j) { return s0 + (j >> 3) * kStep + (j & 7); });
   }
   auto one = [&](int64_t s, uint32_t k1) {
     if (k1 >= cut) {
@@ -821,10 +825,14 @@ __device__ __forceinline__ bool row_sampled(const float* row, int64_t n, int32_t
   return n > k && n >= kSampleMinN && (reinterpret_cast<uintptr_t>(row) & 15) == 0;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_rows_estimate_kernel(const float* __restrict__ scores,
-                                                                          int64_t ld, int64_t N,
-                                                                          const int32_t* __restrict__ n_valid,
-                                                                          int32_t k, RowsMeta* __restrict__ meta) {
+// The estimate and finish kernels run one workgroup of NTH threads per row
+// (kTopkWideThreads for launches of few rows, as topk_kernel).  Measured on
+// MI355X, 32 rows of 4K..128K: the collect kernel's batched append took the
+// three kernels from 33.7 to 32.4 us, the wide workgroups to 32.0 us.
+template <int NTH>
+__global__ __launch_bounds__(NTH) void topk_rows_estimate_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                 int64_t N, const int32_t* __restrict__ n_valid,
+                                                                 int32_t k, RowsMeta* __restrict__ meta) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   TopkShared& sh = *reinterpret_cast<TopkShared*>(smem);
   uint32_t* sample = reinterpret_cast<uint32_t*>(smem + sizeof(TopkShared));
@@ -832,7 +840,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_estimate_kernel(const 
   const int64_t n = row_len(n_valid, t, N);
   const float* row = scores + t * ld;
   uint32_t t_est = 0u;
-  if (row_sampled(row, n, k)) t_est = TopkOps<kTopkThreads>::sample_estimate(sh, row, n, k, sample);
+  if (row_sampled(row, n, k)) t_est = TopkOps<NTH>::sample_estimate(sh, row, n, k, sample);
   if (threadIdx.x == 0) meta[t] = RowsMeta{t_est, 0u};
 }
 
@@ -853,26 +861,26 @@ __global__ __launch_bounds__(256) void topk_rows_collect_kernel(const float* __r
   if (threadIdx.x == 0) ln = 0;
   __syncthreads();
   const int64_t s1 = min(s0 + kRowChunk, n);
-  auto visit = [&](int64_t s, float f) {
-    const uint32_t key = order_key(f);
-    if (key >= t_est) {
-      const uint32_t slot = atomicAdd(&ln, 1u);
-      lkey[slot] = key;
-      lidx[slot] = (int32_t)s;
-    }
-  };
+  // the chunk's 16 keys of this thread, marked when inside the row and >= t_est
+  uint32_t key[16], m = 0u;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int64_t s = s0 + 4 * (threadIdx.x + 256 * u);
+    v4f v = {0.f, 0.f, 0.f, 0.f};
     if (s + 3 < s1) {
-      const v4f v = *(const v4f*)(row + s);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) visit(s + j, v[j]);
+      v = *(const v4f*)(row + s);
     } else {
       for (int j = 0; j < 4; ++j)
-        if (s + j < s1) visit(s + j, row[s + j]);
+        if (s + j < s1) v[j] = row[s + j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      key[4 * u + j] = order_key(v[j]);
+      m |= (s + j < s1 && key[4 * u + j] >= t_est ? 1u : 0u) << (4 * u + j);
     }
   }
+  append_marked<16>(&ln, lkey, lidx, (uint32_t)kRowChunk, key, m,
+                    [&](int j) { return s0 + 4 * (threadIdx.x + 256 * (j >> 2)) + (j & 3); });
   __syncthreads();
   if (ln == 0) return;
   if (threadIdx.x == 0) base = atomicAdd(&meta[t].n_cand, ln);
@@ -886,7 +894,8 @@ __global__ __launch_bounds__(256) void topk_rows_collect_kernel(const float* __r
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_rows_finish_kernel(
+template <int NTH>
+__global__ __launch_bounds__(NTH) void topk_rows_finish_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t N, const int32_t* __restrict__ n_valid, int32_t k,
     const RowsMeta* __restrict__ meta, const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_idx,
     int32_t* __restrict__ idx, int32_t n_words_max) {
@@ -899,29 +908,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_finish_kernel(
   const int64_t n = row_len(n_valid, t, N);
   int32_t* out = idx + t * (int64_t)k;
   if (n <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+    for (int i = tid; i < k; i += NTH) out[i] = i < n ? i : -1;
     return;
   }
   const float* row = scores + t * ld;
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
   const uint32_t c = row_sampled(row, n, k) ? meta[t].n_cand : 0u;
   if (c < (uint32_t)k || c > (uint32_t)kTopkCap) {  // uniform: the exact path over the row
-    TopkOps<kTopkThreads>::topk_exact_row(sh, row, n, vec, k, gt_bits, eq_bits, n_words_max, out);
+    TopkOps<NTH>::topk_exact_row(sh, row, n, vec, k, gt_bits, eq_bits, n_words_max, out);
     return;
   }
   const int n_words = (int)((n + 31) / 32);  // bitmap words of this row
-  for (int i = tid; i < n_words; i += kTopkThreads) {
+  for (int i = tid; i < n_words; i += NTH) {
     gt_bits[i] = 0u;
     eq_bits[i] = 0u;
   }
-  for (int i = tid; i < (int)c; i += kTopkThreads) {
+  for (int i = tid; i < (int)c; i += NTH) {
     sh.list_key[i] = cand_key[t * kTopkCap + i];
     sh.list_idx[i] = cand_idx[t * kTopkCap + i];
   }
   __syncthreads();
   // theta, the k-th largest
-  const uint32_t hi = TopkOps<kTopkThreads>::select_in_list(sh, (int)c, sh.list_key, (uint32_t)k, 3);
-  for (int i = tid; i < (int)c; i += kTopkThreads) {
+  const uint32_t hi = TopkOps<NTH>::select_in_list(sh, (int)c, sh.list_key, (uint32_t)k, 3);
+  for (int i = tid; i < (int)c; i += NTH) {
     const uint32_t key = sh.list_key[i];
     const int32_t s = sh.list_idx[i];
     if (key > hi)
@@ -930,7 +939,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_finish_kernel(
       atomicOr(&eq_bits[s >> 5], 1u << (s & 31));
   }
   __syncthreads();
-  TopkOps<kTopkThreads>::emit_selection(sh, gt_bits, eq_bits, n_words, (uint32_t)k, out);
+  TopkOps<NTH>::emit_selection(sh, gt_bits, eq_bits, n_words, (uint32_t)k, out);
 }
 
 size_t topk_rows_scratch_bytes(int64_t T, int64_t /*N*/) {
@@ -959,15 +968,27 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int64_t T, int64_t 
   // (2 x n_words words) both fit the same dynamic LDS as topk_kernel
   const size_t lds = sizeof(TopkShared) + sizeof(uint32_t) * 2 * (size_t)n_words + 256;
   static std::atomic<uint64_t> lds_set{0};
-  if (hipError_t e = lds_limit_once(lds_set, {(const void*)topk_rows_finish_kernel,
-                                              (const void*)topk_rows_estimate_kernel}))
+  if (hipError_t e = lds_limit_once(lds_set, {(const void*)topk_rows_finish_kernel<kTopkThreads>,
+                                              (const void*)topk_rows_estimate_kernel<kTopkThreads>,
+                                              (const void*)topk_rows_finish_kernel<kTopkWideThreads>,
+                                              (const void*)topk_rows_estimate_kernel<kTopkWideThreads>}))
     return e;
-  hipLaunchKernelGGL(topk_rows_estimate_kernel, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, N,
-                     n_valid, k, meta);
+  const bool wide = T <= kTopkWideMaxRows;
+  const dim3 block(wide ? kTopkWideThreads : kTopkThreads);
+  if (wide)
+    hipLaunchKernelGGL(topk_rows_estimate_kernel<kTopkWideThreads>, dim3((unsigned)T), block, lds, st, scores, ld, N,
+                       n_valid, k, meta);
+  else
+    hipLaunchKernelGGL(topk_rows_estimate_kernel<kTopkThreads>, dim3((unsigned)T), block, lds, st, scores, ld, N,
+                       n_valid, k, meta);
   hipLaunchKernelGGL(topk_rows_collect_kernel, dim3((unsigned)n_chunks, (unsigned)T), dim3(256), 0, st, scores, ld,
                      N, n_valid, k, meta, cand_key, cand_idx);
-  hipLaunchKernelGGL(topk_rows_finish_kernel, dim3((unsigned)T), dim3(kTopkThreads), lds, st, scores, ld, N,
-                     n_valid, k, meta, cand_key, cand_idx, idx, n_words);
+  if (wide)
+    hipLaunchKernelGGL(topk_rows_finish_kernel<kTopkWideThreads>, dim3((unsigned)T), block, lds, st, scores, ld, N,
+                       n_valid, k, meta, cand_key, cand_idx, idx, n_words);
+  else
+    hipLaunchKernelGGL(topk_rows_finish_kernel<kTopkThreads>, dim3((unsigned)T), block, lds, st, scores, ld, N,
+                       n_valid, k, meta, cand_key, cand_idx, idx, n_words);
   return hipGetLastError();
 }
 
