@@ -273,8 +273,16 @@ static __device__ __forceinline__ void scan_row_h(const _Float16* __restrict__ r
 // The same append for a 16-byte aligned fp32 row: batches of 16 keys per
 // thread (four 16-byte loads in flight), the tail key by key.  Measured on
 // MI355X: decode top-k 23.0 -> 22.7 us on 64 x 32K.
+// With use_first, first holds the thread's first batch (first_batch_f,
+// taken when the row has at least 16 NTH keys).
+static __device__ __forceinline__ void first_batch_f(const float* __restrict__ row, v4f (&v)[4]) {
+  const int64_t s0 = 4 * (int64_t)threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = *(const v4f*)(row + s0 + u * (4 * NTH));
+}
+
 static __device__ __forceinline__ void gather_ge_f(TopkShared& sh, const float* __restrict__ row, int64_t n,
-                                                   uint32_t cut) {
+                                                   uint32_t cut, bool use_first, const v4f (&first)[4]) {
   const int tid = threadIdx.x;
   constexpr int kU = 4;
   constexpr int64_t kStep = 4 * NTH;
@@ -282,8 +290,13 @@ static __device__ __forceinline__ void gather_ge_f(TopkShared& sh, const float* 
   // every thread runs the same number of these iterations (whole waves active)
   for (int64_t s0 = 4 * (int64_t)tid; s0 < nU; s0 += kU * kStep) {
     v4f v[kU];
+    if (use_first && s0 == 4 * (int64_t)tid) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) v[u] = *(const v4f*)(row + s0 + u * kStep);
+      for (int u = 0; u < kU; ++u) v[u] = first[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = *(const v4f*)(row + s0 + u * kStep);
+    }
     uint32_t key[kU * 4], m = 0u;
 #pragma unroll
     for (int u = 0; u < kU; ++u)
@@ -313,6 +326,31 @@ static __device__ __forceinline__ void gather_ge_f(TopkShared& sh, const float* 
   for (int64_t s = n4 + tid; s < n; s += NTH) one(s, order_key(row[s]));
 }
 
+// Keys of one 32-key batch (four 16-byte loads at s0 + u * 8 NTH) appended
+// when >= cut, through append_marked.
+static __device__ __forceinline__ void gather_batch_h(TopkShared& sh, int64_t s0, const v8h (&v)[4], float scale,
+                                                      uint32_t cut) {
+  constexpr int64_t kStep = 8 * NTH;
+  uint32_t key[32], m = 0u;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      key[u * 8 + j] = h_key(v[u][j], scale);
+      m |= (key[u * 8 + j] >= cut ? 1u : 0u) << (u * 8 + j);
+    }
+  append_marked<32>(&sh.list_n, sh.list_key, sh.list_idx, (uint32_t)kTopkCap, key, m,
+                    [&](int j) { return s0 + (j >> 3) * kStep + (j & 7); });
+}
+
+// The loads of a thread's first batch of gather_ge_h (rows of at least
+// 32 NTH keys), issued ahead of the work that finds the cut.
+static __device__ __forceinline__ void first_batch_h(const _Float16* __restrict__ row, v8h (&v)[4]) {
+  const int64_t s0 = 8 * (int64_t)threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = *(const v8h*)(row + s0 + u * (8 * NTH));
+}
+
 // Appends to the LDS list every key >= cut of such a row, with its position
 // (slots from kTopkCap on are counted in list_n but not written), as the
 // candidate passes do.  In the unrolled part each thread keeps the keys of
@@ -322,28 +360,26 @@ static __device__ __forceinline__ void gather_ge_f(TopkShared& sh, const float* 
 // for an LDS atomic at nearly every position (some lane of 64 usually holds
 // a key above the cut).  Measured on MI355X: band top-k 17.4 -> 16.8 ms per
 // 128K prefill step, 5.23 -> 5.14 ms per chunked paged prefill call.
+// With use_first (first holding the first_batch_h loads, taken when the
+// row has at least 32 NTH keys) the first batch comes from those registers.
 // Expects list_n set and a barrier before the call.
 static __device__ __forceinline__ void gather_ge_h(TopkShared& sh, const _Float16* __restrict__ row, float scale,
-                                                   int64_t n, uint32_t cut) {
+                                                   int64_t n, uint32_t cut, bool use_first, const v8h (&first)[4]) {
   const int tid = threadIdx.x;
   constexpr int kU = 4;
   constexpr int64_t kStep = 8 * NTH;
   const int64_t nU = n / (kU * kStep) * (kU * kStep);
   // every thread runs the same number of these iterations (whole waves active)
-  for (int64_t s0 = 8 * (int64_t)tid; s0 < nU; s0 += kU * kStep) {
+  int64_t s0 = 8 * (int64_t)tid;
+  if (use_first && s0 < nU) {
+    gather_batch_h(sh, s0, first, scale, cut);
+    s0 += kU * kStep;
+  }
+  for (; s0 < nU; s0 += kU * kStep) {
     v8h v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) v[u] = *(const v8h*)(row + s0 + u * kStep);
-    uint32_t key[kU * 8], m = 0u;
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        key[u * 8 + j] = h_key(v[u][j], scale);
-        m |= (key[u * 8 + j] >= cut ? 1u : 0u) << (u * 8 + j);
-      }
-    append_marked<kU * 8>(&sh.list_n, sh.list_key, sh.list_idx, (uint32_t)kTopkCap, key, m,
-                          [&](int j) { return s0 + (j >> 3) * kStep + (j & 7); });
+    gather_batch_h(sh, s0, v, scale, cut);
   }
   auto one = [&](int64_t s, uint32_t k1) {
     if (k1 >= cut) {
@@ -623,11 +659,16 @@ static __device__ __forceinline__ bool topk_sampled(TopkShared& sh, const float*
                                              uint32_t* gt_bits, uint32_t* eq_bits, int n_words,
                                              int32_t* __restrict__ out) {
   const int tid = threadIdx.x;
+  // the candidate pass's first loads go out with the sample's (measured on
+  // MI355X: decode top-k 23.1 -> 22.5 us on 64 x 32K)
+  v4f first[4];
+  const bool pre = n >= 16 * NTH;  // uniform
+  if (pre) first_batch_f(row, first);
   const uint32_t t_est = sample_estimate(sh, row, n, k, gt_bits);
 
   if (tid == 0) sh.list_n = 0;
   __syncthreads();
-  gather_ge_f(sh, row, n, t_est);
+  gather_ge_f(sh, row, n, t_est, pre, first);
   __syncthreads();
   const uint32_t c = sh.list_n;
   if (c < (uint32_t)k || c > (uint32_t)kTopkCap) return false;  // uniform across the workgroup
@@ -1137,10 +1178,16 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const _Float16* __re
     // 1.5 k keys expected above the estimate: the band reaches about 1.2 k
     // to 1.3 k below the top on these workloads, so the list gathered here
     // usually holds every band key and no second pass over the row is needed
+    // the candidate pass's first loads go out with the sample's, one memory
+    // round trip for both (measured on MI355X: 5.00 -> 4.95 ms of top-k per
+    // chunked paged prefill call; the 128K prefill's 15.7 ms unchanged)
+    v8h first[4];
+    const bool pre = n >= 32 * kTopkThreads;  // uniform
+    if (pre) TopkOps<kTopkThreads>::first_batch_h(row, first);
     const uint32_t t_est = TopkOps<kTopkThreads>::sample_estimate_h(sh, row, scale, n, k, gt_bits, 12);
     if (tid == 0) sh.list_n = 0;
     __syncthreads();
-    TopkOps<kTopkThreads>::gather_ge_h(sh, row, scale, n, t_est);
+    TopkOps<kTopkThreads>::gather_ge_h(sh, row, scale, n, t_est, pre, first);
     __syncthreads();
     const uint32_t c = sh.list_n;
     if (c >= (uint32_t)k && c <= (uint32_t)kTopkCap) {
@@ -1168,7 +1215,8 @@ __device__ __forceinline__ bool band_select(TopkShared& sh, const _Float16* __re
   if (!(have_list && key_lcut >= t_low)) {
     if (tid == 0) sh.list_n = 0;
     __syncthreads();
-    TopkOps<kTopkThreads>::gather_ge_h(sh, row, scale, n, key_lcut);
+    v8h none[4];  // not read
+    TopkOps<kTopkThreads>::gather_ge_h(sh, row, scale, n, key_lcut, false, none);
     __syncthreads();
     if (sh.list_n > (uint32_t)kTopkCap) return false;  // uniform across the workgroup
   }
