@@ -55,17 +55,17 @@ PEAK_HBM_GBS = 8000.0
 # one changes, the figure no longer describes the launch and the roofline reports traffic as null.
 COUNTER_TRAFFIC = {
     ("prefill_L128k", "indexer"): ("e80d6cb420658ad0", ('indexer.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 1009.2e6),
-    ("prefill_L128k", "topk"): ("720e897d76044175", ('topk.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 991.4e6),
-    ("prefill_L128k", "sparse_mla"): ("e286d380d79d225d", ('sparse_mla.hip', 'common.h'), 270029.0e6),
+    ("prefill_L128k", "topk"): ("d879294fca012ffb", ('topk.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 991.0e6),
+    ("prefill_L128k", "sparse_mla"): ("e286d380d79d225d", ('sparse_mla.hip', 'common.h'), 278029.8e6),
     ("decode_b64_ctx32k", "indexer"): ("aa70767aa971e6ed", ('indexer.hip', 'indexer_exact.h', 'common.h'), 281.4e6),
-    ("decode_b64_ctx32k", "topk"): ("984021d9b2a4c5b8", ('topk.hip', 'indexer_exact.h', 'common.h'), 9.3e6),
+    ("decode_b64_ctx32k", "topk"): ("d1d997af9d4303a1", ('topk.hip', 'indexer_exact.h', 'common.h'), 9.3e6),
     ("decode_b64_ctx32k", "sparse_mla"): ("e286d380d79d225d", ('sparse_mla.hip', 'common.h'), 246.3e6),
     ("paged_decode_b32_ctx4k_128k", "indexer"): ("aa70767aa971e6ed", ('indexer.hip', 'indexer_exact.h', 'common.h'), 278.3e6),
-    ("paged_decode_b32_ctx4k_128k", "topk"): ("984021d9b2a4c5b8", ('topk.hip', 'indexer_exact.h', 'common.h'), 10.4e6),
+    ("paged_decode_b32_ctx4k_128k", "topk"): ("d1d997af9d4303a1", ('topk.hip', 'indexer_exact.h', 'common.h'), 10.4e6),
     ("paged_decode_b32_ctx4k_128k", "sparse_mla"): ("e286d380d79d225d", ('sparse_mla.hip', 'common.h'), 157.6e6),
-    ("paged_prefill_b4_ctx32k_q8k", "indexer"): ("e80d6cb420658ad0", ('indexer.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 923.1e6),
-    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("720e897d76044175", ('topk.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 988.0e6),
-    ("paged_prefill_b4_ctx32k_q8k", "sparse_mla"): ("e286d380d79d225d", ('sparse_mla.hip', 'common.h'), 10379.9e6),
+    ("paged_prefill_b4_ctx32k_q8k", "indexer"): ("e80d6cb420658ad0", ('indexer.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 924.6e6),
+    ("paged_prefill_b4_ctx32k_q8k", "topk"): ("d879294fca012ffb", ('topk.hip', 'indexer_exact.h', 'common.h', 'dsa_api.cpp'), 989.3e6),
+    ("paged_prefill_b4_ctx32k_q8k", "sparse_mla"): ("e286d380d79d225d", ('sparse_mla.hip', 'common.h'), 10447.6e6),
     ("prefill_L32k", "mla_bwd_dq"): ("d841631102c38279", ('sparse_mla_bwd.hip', 'common.h'), 5635.5e6),
     ("prefill_L32k", "mla_bwd_dkv"): ("d841631102c38279", ('sparse_mla_bwd.hip', 'common.h'), 7632.8e6),
     ("prefill_L32k", "mla_bwd_reduce"): ("d841631102c38279", ('sparse_mla_bwd.hip', 'common.h'), 5010.0e6),
